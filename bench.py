@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of the chained FwPKM read+update chunk on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|INDEX]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+score -> per-half top-k -> Cartesian top-k -> softmax -> gather -> backward
+-> sort -> segmented SGD update, chained through the memory state (each step
+reads the tables the previous one wrote).  For a single-chunk workload a step
+is one chunk call; for a streamed workload it is every chunk of the pass.
+Inputs and tables sit in HBM before the timed region starts.
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed
+with HIP events recorded around each kernel on its own stream) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
+DEFAULT_WORKLOAD = 2            # 65,536 slots, d_v 512, top-8, batch 2 x 256 tokens
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=str(DEFAULT_WORKLOAD))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time spent timing the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile-pass", action="store_true",
+                    help="skip the per-kernel event pass (for external profilers)")
+    return ap.parse_args()
+
+
+def algorithmic_cost(cfg, kernel, tokens, uniq_v, uniq_k):
+    """Compulsory bytes (and flops) one launch of `kernel` must move.
+
+    tokens  = units * tokens per chunk in the launch
+    uniq_v  = distinct value rows the launch updates
+    uniq_k  = distinct K1 plus K2 rows the launch updates
+    """
+    f = 4  # fp32
+    U = cfg.units
+    if kernel == "score":
+        byts = f * (tokens * cfg.dim_qk + U * 2 * cfg.sqrt_slots * cfg.half)
+        flops = 2.0 * tokens * cfg.sqrt_slots * cfg.dim_qk
+        return byts, flops
+    if kernel == "read":
+        # k gathered value rows + the target row read + the retrieved row written
+        return f * tokens * (cfg.topk * cfg.dim_v + 2 * cfg.dim_v), 0.0
+    if kernel == "update":
+        # read-modify-write of every touched V, K1 and K2 row
+        return f * 2 * (uniq_v * cfg.dim_v + uniq_k * cfg.half), 0.0
+    if kernel == "sort":
+        # three key lists read, three index lists written
+        return f * 2 * 3 * tokens * cfg.topk, 0.0
+    return 0.0, 0.0
+
+
+def cpu_baseline(cfg, tables, Q, Y, seconds):
+    """The oracle as it stands, single-threaded, on whole chunks of unit 0."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import numpy as np
+
+    from oracle import fwpkm_oracle as O
+
+    st = {"k1": tables.k1[:1].copy(), "k2": tables.k2[:1].copy(), "v": tables.v[:1].copy()}
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    tokens = 0
+    chunks = 0
+    t0 = time.perf_counter()
+    try:
+        while True:
+            c = chunks % cfg.chunks
+            q = np.ascontiguousarray(Q[:1, c * cfg.chunk:(c + 1) * cfg.chunk, :1])
+            y = np.ascontiguousarray(Y[:1, c * cfg.chunk:(c + 1) * cfg.chunk, :1])
+            O.forward_chunk(st, q, y, cfg.lr, cfg.topk, cfg.eps, inplace=True)
+            tokens += cfg.chunk
+            chunks += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{chunks} chained chunk(s) of {cfg.chunk} tokens on one memory unit "
+                      f"(1 of {cfg.units}; units are independent), float64 numpy, 1 thread, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "memory units are independent, so N GPUs would each run this step on "
+              "their own share of the batch.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_weight_memory_amd import Config, Memory, State, _lib
+    from workloads import draw_queries, draw_targets, get_config, initial_tables
+
+    key = int(args.workload) if args.workload.isdigit() else args.workload
+    cfg = get_config(key)
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_weight_memory_amd import build as _build
+        _build.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    print(f"[bench] workload {cfg.name}: drawing inputs", file=sys.stderr, flush=True)
+    tables = initial_tables(cfg)
+    Q = draw_queries(cfg)
+    Y = draw_targets(cfg)
+    B, H, C = cfg.batch, cfg.heads, cfg.chunk
+
+    mem = Memory(Config(sqrt_slots=cfg.sqrt_slots, dim_qk=cfg.dim_qk, dim_v=cfg.dim_v,
+                        topk=cfg.topk, chunk_size=C, num_heads=H, max_batch=B, eps=cfg.eps))
+    # per-sequence tables expanded from the shared initial ones (untimed)
+    st = State(*(torch.from_numpy(a).to(dev).unsqueeze(0).repeat(B, *([1] * a.ndim)).contiguous()
+                 for a in (tables.k1, tables.k2, tables.v)))
+    # each chunk's inputs contiguous in HBM: [chunks, B, C, H, d]
+    qd = torch.from_numpy(np.ascontiguousarray(
+        Q.reshape(B, cfg.chunks, C, H, cfg.dim_qk).transpose(1, 0, 2, 3, 4))).to(dev)
+    yd = torch.from_numpy(np.ascontiguousarray(
+        Y.reshape(B, cfg.chunks, C, H, cfg.dim_v).transpose(1, 0, 2, 3, 4))).to(dev)
+    ret = torch.empty((B, C, H, cfg.dim_v), device=dev)
+    tokens_per_step = B * C * cfg.chunks
+
+    def step(select=False):
+        out = []
+        for c in range(cfg.chunks):
+            r = mem.forward_chunk(qd[c], yd[c], cfg.lr, st, next=st, retrieved=ret,
+                                  return_selection=select)
+            if select:
+                out.append(r[2])
+        return out
+
+    print(f"[bench] warmup {args.warmup} step(s)", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} step(s)", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    value = tokens_per_step / (ms_step * 1e-3)
+
+    result = {
+        "metric": "tokens/s for chained FwPKM read+update chunk",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "wall_s_timed": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": cfg.name, "batch": B, "heads": H, "chunk": C,
+                   "chunks_per_step": cfg.chunks, "tokens_per_step": tokens_per_step,
+                   "slots": cfg.num_slots, "dim_qk": cfg.dim_qk, "dim_v": cfg.dim_v,
+                   "topk": cfg.topk, "lr": cfg.lr, "eps": cfg.eps,
+                   "parallelism": "single GPU"},
+    }
+
+    if not args.no_profile_pass:
+        print("[bench] per-kernel event pass", file=sys.stderr, flush=True)
+        mem.profile(True)
+        sels = []
+        for _ in range(args.steps):
+            sels = step(select=True)      # keep the last step's selections
+        prof = mem.profile_read()
+        mem.profile(False)
+        # distinct rows each launch updates, from the selections of the same pass
+        uv = uk = 0
+        for s in sels:
+            flat = s.permute(0, 2, 1, 3).reshape(B * H, -1).long()
+            for u in range(B * H):
+                row = flat[u]
+                uv += int(torch.unique(row).numel())
+                uk += int(torch.unique(row // cfg.sqrt_slots).numel())
+                uk += int(torch.unique(row % cfg.sqrt_slots).numel())
+        launches = len(sels)
+        uv /= launches
+        uk /= launches
+        kernels = {}
+        tokens_launch = B * H * C
+        for name, (ms, n) in prof.items():
+            if n == 0:
+                continue
+            avg_us = 1e3 * ms / n
+            byts, flops = algorithmic_cost(cfg, name, tokens_launch, uv, uk)
+            kernels[name] = {"avg_us": avg_us, "launches": n,
+                             "alg_bytes": byts, "alg_gbps": byts / (avg_us * 1e3) if byts else None,
+                             "alg_tflops": flops / (avg_us * 1e6) if flops else None}
+        result["kernels"] = kernels
+        result["unique_rows_per_launch"] = {"v": uv, "k1_plus_k2": uk,
+                                            "pairs": B * H * C * cfg.topk}
+        dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+        kd = kernels[dom]
+        if dom == "score":
+            roof = {"bound": "mfma", "achieved": kd["alg_tflops"], "peak": FP32_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s"}
+        else:
+            roof = {"bound": "hbm", "achieved": kd["alg_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = None
+        roof["kernel"] = dom
+        result["roofline"] = roof
+
+    if not args.no_cpu_baseline:
+        print(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, tables, Q, Y, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

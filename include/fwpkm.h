@@ -1,0 +1,188 @@
+/*
+ * fwpkm.h -- C ABI of the FwPKM chunked read-then-write step on MI355X (gfx950).
+ *
+ * Fast-weight Product Key Memory keeps, per memory unit (one sequence x one
+ * head), fast weights theta = (K1, K2, V): two sub-key tables of n rows and a
+ * value table of N = n*n rows.  One call processes one chunk of tokens:
+ *
+ *   read   each query is split into two halves scored against K1 and K2,
+ *          the per-half best k sub-keys are combined into k*k candidate slots
+ *          (slot = a*n + b), the best k slots are kept, and the retrieved
+ *          vector is the softmax-weighted sum of their value rows.
+ *          [gist.science "Fast-weight Product Key Memory", section 2,
+ *          Core Architecture (two codebooks, top-k slots with O(sqrt N)
+ *          scoring) and Key Technical Choices (IDW score
+ *          -log(eps + ||q - K||^2)); agifrontier tutorial "Fast-weight
+ *          Product Key Memory", Product Key addressing]
+ *   write  one local gradient step theta' = theta - lr * grad L on the
+ *          summed MSE loss L = sum_t 1/2 ||retrieved_t - target_t||^2, held
+ *          at the chunk's starting weights, applied to every touched V, K1
+ *          and K2 row; a row touched by several tokens gets the mean of their
+ *          gradients; no clipping.
+ *          [agifrontier tutorial, update equation; sciencestack.ai
+ *          "Fast-weight Product Key Memory", contents: MSE loss, reducing MSE
+ *          losses to a scalar by summation, weighting gradient by row
+ *          contribution, no gradient clipping; gist.science section 2,
+ *          gradient aggregation by averaging]
+ *   chain  predictions inside the chunk use only the weights from before the
+ *          chunk; the next call reads the updated weights.
+ *          [gist.science section 2, Causality Preservation; PyPI
+ *          "fast-weight-product-key-memory 0.2.2", Usage: chained
+ *          past_memories -> next_memories]
+ *
+ * All tensors are fp32, row-major and contiguous, in device memory owned by
+ * the caller.  All work is enqueued on the caller's stream; no call
+ * synchronises the host with the device except where stated.
+ *
+ * Errors: every entry point returns FWPKM_OK (0) or a negative code, never
+ * throws, and leaves a message for fwpkm_last_error() in thread-local storage.
+ * Argument validation runs before anything is enqueued: on a validation error
+ * no device memory is written.  Device faults are asynchronous and surface at
+ * a later HIP call or stream synchronisation.
+ */
+#ifndef FWPKM_H
+#define FWPKM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define FWPKM_OK               0
+#define FWPKM_ERR_INVALID_ARG (-1) /* null pointer, bad size, k out of range, non-finite lr */
+#define FWPKM_ERR_ALIAS       (-2) /* partial overlap of past/next state, or an output aliasing an input */
+#define FWPKM_ERR_OOM         (-3) /* device workspace allocation failed */
+#define FWPKM_ERR_HIP         (-4) /* HIP runtime error; fwpkm_last_error() holds its text */
+#define FWPKM_ERR_UNSUPPORTED (-5) /* valid shape outside the kernels' limits (listed below) */
+
+/* Scoring modes.
+ * IDW: score = -log(eps + ||q - K||^2) over the full key [K1[a]; K2[b]]
+ *      [gist.science section 2, Key Technical Choices].
+ * DOT: score = q . K, the standard product-key memory score that the same
+ *      passage contrasts IDW with. */
+#define FWPKM_SCORE_IDW 0
+#define FWPKM_SCORE_DOT 1
+
+/* Kernel limits (FWPKM_ERR_UNSUPPORTED beyond them). */
+#define FWPKM_MAX_TOPK      32      /* k */
+#define FWPKM_MAX_SQRT_SLOTS 4096   /* n, so N <= 2^24 */
+#define FWPKM_MAX_HALF      1024    /* d_qk / 2 */
+#define FWPKM_MAX_DIM_V     2048    /* d_v */
+#define FWPKM_MAX_CHUNK     1024    /* chunk_size */
+
+/* Opaque handle: owns the device workspace of one configuration, nothing else. */
+typedef struct fwpkm_handle fwpkm_handle;
+
+/* Configuration, mirroring the constructor arguments on the PyPI page's Usage
+ * section (num_memories = sqrt_slots^2, dim_queries_keys, dim_values, topk,
+ * learning_rate per call, chunk_size) plus the multi-head count. */
+typedef struct {
+    int32_t sqrt_slots;  /* n >= 1; N = n*n slots; n <= FWPKM_MAX_SQRT_SLOTS           */
+    int32_t dim_qk;      /* d_qk, even; each half d_h = d_qk/2, d_h % 4 == 0            */
+    int32_t dim_v;       /* d_v, d_v % 4 == 0                                          */
+    int32_t topk;        /* 1 <= k <= min(n*n, FWPKM_MAX_TOPK), and k <= n              */
+    int32_t chunk_size;  /* C, the most tokens one call may carry                      */
+    int32_t num_heads;   /* H >= 1, an independent memory per head                     */
+    int32_t max_batch;   /* most sequences one call may carry; sizes the workspace     */
+    float   eps;         /* IDW epsilon, finite and > 0 (the pages give no value)      */
+    int32_t score_mode;  /* FWPKM_SCORE_IDW or FWPKM_SCORE_DOT                          */
+} fwpkm_config;
+
+/* Fast-weight state in caller-owned device memory (fp32, contiguous):
+ *   k1, k2 : per sequence [H, n, d_h]
+ *   v      : per sequence [H, N, d_v]
+ * Sequence b's tables start at k1 + b*batch_stride_k (likewise k2) and
+ * v + b*batch_stride_v.  A stride of 0 means one set of tables shared by the
+ * whole batch (allowed for a past state only). */
+typedef struct {
+    float*  k1;
+    float*  k2;
+    float*  v;
+    int64_t batch_stride_k;  /* elements; 0 or >= H*n*d_h */
+    int64_t batch_stride_v;  /* elements; 0 or >= H*N*d_v */
+} fwpkm_state;
+
+/* Validate *cfg and create a handle.  The device workspace is allocated on
+ * the current device at the first fwpkm_forward_chunk call, so creation
+ * itself makes no HIP call.  Returns FWPKM_ERR_INVALID_ARG or
+ * FWPKM_ERR_UNSUPPORTED for a bad configuration, FWPKM_ERR_OOM if the handle
+ * cannot be allocated.  *out is set only on success. */
+int fwpkm_create(const fwpkm_config* cfg, fwpkm_handle** out);
+
+/* Device workspace bytes a handle of this configuration allocates
+ * (0 for an invalid configuration). */
+size_t fwpkm_workspace_bytes(const fwpkm_config* cfg);
+
+/* One chunk: read with past_state, write the updated state into next_state.
+ *
+ *   queries   [batch, tokens, H, d_qk]   read
+ *   targets   [batch, tokens, H, d_v]    read; already paired with the
+ *                                        queries (a lookahead shift, if any,
+ *                                        is the caller's)
+ *   batch     1..max_batch;  tokens 1..chunk_size
+ *   lr        learning rate eta, finite; 0 skips the write entirely and
+ *             next_state then equals past_state bit for bit
+ *   past_state  weights before the chunk (read)
+ *   next_state  weights after the chunk (written).  Either the very same
+ *             pointers and strides as past_state (in-place update, the fast
+ *             path), or tables disjoint from past_state: then past_state is
+ *             first copied into next_state on the stream (this is also how a
+ *             shared, stride-0 past state is expanded into per-sequence
+ *             tables; next_state strides must then be non-zero when
+ *             batch > 1).  Any partial overlap is FWPKM_ERR_ALIAS.
+ *   retrieved [batch, tokens, H, d_v]    written; must not overlap any input
+ *   out_slots   nullable [batch, tokens, H, k] int32: selected slots, best
+ *               first (ties by lower slot)
+ *   out_weights nullable [batch, tokens, H, k] fp32: their softmax weights
+ *   stream    HIP stream to enqueue on (0 = null stream)
+ *
+ * The handle's workspace is reused by every call: calls on one handle must
+ * be ordered (one stream at a time); the handle is not thread-safe. */
+int fwpkm_forward_chunk(fwpkm_handle* h,
+                        const float* queries, const float* targets,
+                        int32_t batch, int32_t tokens, float lr,
+                        const fwpkm_state* past_state, const fwpkm_state* next_state,
+                        float* retrieved, int32_t* out_slots, float* out_weights,
+                        hipStream_t stream);
+
+/* Release the handle and its workspace (synchronises the device before the
+ * workspace is freed).  NULL-safe. */
+void fwpkm_destroy(fwpkm_handle* h);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* fwpkm_last_error(void);
+
+/* ---- per-kernel timing (measurement support, off by default) ------------
+ * With profiling enabled, every fwpkm_forward_chunk call on the handle also
+ * records a pair of HIP events around each kernel (and the state copy) on the
+ * call's stream.  The events are timing-only markers: they add no
+ * synchronisation.  Kernel ids are stable:
+ *   0 score  (sub-key scoring + per-half top-k)
+ *   1 read   (Cartesian top-k, weights, gather, backward)
+ *   2 sort   (pair-list radix sort)
+ *   3 update (segmented mean gradient + SGD)
+ *   4 copy   (past -> next state copy, copy mode only)                      */
+#define FWPKM_NUM_TIMED 5
+
+/* enable != 0: clear the totals and start recording; 0: stop recording. */
+int fwpkm_profile_enable(fwpkm_handle* h, int32_t enable);
+
+/* Wait for the recorded events, add their elapsed times to the totals and
+ * report them: ms[i] = total milliseconds of kernel i, launches[i] = how many
+ * launches were timed.  Arrays hold FWPKM_NUM_TIMED entries; either may be
+ * NULL.  Synchronises with the recorded events (not with the whole device). */
+int fwpkm_profile_read(fwpkm_handle* h, double* ms, int64_t* launches);
+
+/* Short name of timed kernel i ("" outside 0..FWPKM_NUM_TIMED-1). */
+const char* fwpkm_kernel_name(int32_t i);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FWPKM_H */

@@ -1,0 +1,379 @@
+// Host runtime behind the C ABI in include/fwpkm.h: configuration and
+// argument validation, aliasing rules, the device workspace and the launch
+// sequence of one chunk on the caller's stream.
+
+#include "fwpkm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "fwpkm_device.h"
+#include "fwpkm_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int bit_length(int64_t x) {
+  int b = 0;
+  while (x > 0) { ++b; x >>= 1; }
+  return b;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Byte sizes of the workspace regions for `units` units of `tokens` tokens.
+struct WsLayout {
+  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, sorted, seg, nseg, total;
+};
+
+WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
+  const int64_t nblk = (c.sqrt_slots + fwpkm::kKeyBlock - 1) / fwpkm::kKeyBlock;
+  const int64_t P = tokens * c.topk;
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
+  L.half_o = take(sizeof(float) * units * tokens * 2 * nblk * c.topk);
+  L.half_i = take(sizeof(int) * units * tokens * 2 * nblk * c.topk);
+  L.qnorm = take(sizeof(float) * units * tokens * 2);
+  L.sel_w = take(sizeof(float) * units * P);
+  L.g = take(sizeof(float) * units * tokens * c.dim_v);
+  L.keys = take(sizeof(int) * 3 * units * P);
+  L.coef = take(sizeof(float) * 2 * units * P);
+  L.sorted = take(sizeof(int) * 3 * units * P);
+  L.seg = take(sizeof(int) * 3 * units * (P + 1));
+  L.nseg = take(sizeof(int) * 3 * units);
+  L.total = off;
+  return L;
+}
+
+int check_config(const fwpkm_config* c) {
+  if (!c) return fail(FWPKM_ERR_INVALID_ARG, "config is NULL");
+  if (c->sqrt_slots < 1) return fail(FWPKM_ERR_INVALID_ARG, "sqrt_slots must be >= 1 (got %d)", c->sqrt_slots);
+  if (c->dim_qk < 2 || (c->dim_qk & 1)) return fail(FWPKM_ERR_INVALID_ARG, "dim_qk must be even and >= 2 (got %d)", c->dim_qk);
+  if (c->dim_v < 1) return fail(FWPKM_ERR_INVALID_ARG, "dim_v must be >= 1 (got %d)", c->dim_v);
+  const int64_t N = (int64_t)c->sqrt_slots * c->sqrt_slots;
+  if (c->topk < 1 || c->topk > c->sqrt_slots || c->topk > N)
+    return fail(FWPKM_ERR_INVALID_ARG, "topk must lie in [1, sqrt_slots] (got %d)", c->topk);
+  if (c->chunk_size < 1) return fail(FWPKM_ERR_INVALID_ARG, "chunk_size must be >= 1 (got %d)", c->chunk_size);
+  if (c->num_heads < 1) return fail(FWPKM_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", c->num_heads);
+  if (c->max_batch < 1) return fail(FWPKM_ERR_INVALID_ARG, "max_batch must be >= 1 (got %d)", c->max_batch);
+  if (!std::isfinite(c->eps) || !(c->eps > 0.f)) return fail(FWPKM_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if (c->score_mode != FWPKM_SCORE_IDW && c->score_mode != FWPKM_SCORE_DOT)
+    return fail(FWPKM_ERR_INVALID_ARG, "unknown score_mode %d", c->score_mode);
+  // kernel limits
+  const int half = c->dim_qk / 2;
+  if (c->sqrt_slots > FWPKM_MAX_SQRT_SLOTS) return fail(FWPKM_ERR_UNSUPPORTED, "sqrt_slots > %d", FWPKM_MAX_SQRT_SLOTS);
+  if (half % 4 != 0 || half > FWPKM_MAX_HALF) return fail(FWPKM_ERR_UNSUPPORTED, "dim_qk/2 must be a multiple of 4 and <= %d", FWPKM_MAX_HALF);
+  if (c->dim_v % 4 != 0 || c->dim_v > FWPKM_MAX_DIM_V) return fail(FWPKM_ERR_UNSUPPORTED, "dim_v must be a multiple of 4 and <= %d", FWPKM_MAX_DIM_V);
+  if (c->topk > FWPKM_MAX_TOPK) return fail(FWPKM_ERR_UNSUPPORTED, "topk > %d", FWPKM_MAX_TOPK);
+  if (c->chunk_size > FWPKM_MAX_CHUNK) return fail(FWPKM_ERR_UNSUPPORTED, "chunk_size > %d", FWPKM_MAX_CHUNK);
+  if ((int64_t)c->chunk_size * c->topk > fwpkm::kSortMaxPairs)
+    return fail(FWPKM_ERR_UNSUPPORTED, "chunk_size * topk > %d", fwpkm::kSortMaxPairs);
+  const int64_t units = (int64_t)c->max_batch * c->num_heads;
+  if (units > (1 << 20)) return fail(FWPKM_ERR_UNSUPPORTED, "max_batch * num_heads too large");
+  return FWPKM_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range table_range(const float* p, int64_t stride, int64_t size, int batch) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  const int64_t extent = (int64_t)(batch - 1) * stride + size;
+  return {lo, lo + (uintptr_t)extent * sizeof(float)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+}  // namespace
+
+struct fwpkm_handle {
+  fwpkm_config cfg;
+  int device = -1;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  // per-kernel timing
+  struct Mark { hipEvent_t beg, end; int kernel; };
+  bool prof = false;
+  std::vector<Mark> marks;             // recorded, not yet read
+  std::vector<hipEvent_t> spare;       // reusable events
+  double ms[FWPKM_NUM_TIMED] = {};
+  int64_t launches[FWPKM_NUM_TIMED] = {};
+};
+
+namespace {
+
+hipEvent_t take_event(fwpkm_handle* h) {
+  if (!h->spare.empty()) {
+    hipEvent_t e = h->spare.back();
+    h->spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch `fn` on `s`, bracketed by timing events when profiling is on.
+template <typename F>
+hipError_t timed(fwpkm_handle* h, int kernel, hipStream_t s, F&& fn) {
+  if (!h->prof) return fn();
+  hipEvent_t b = take_event(h), e = take_event(h);
+  if (!b || !e) return hipErrorOutOfMemory;
+  hipError_t r = hipEventRecord(b, s);
+  if (r != hipSuccess) return r;
+  r = fn();
+  if (r != hipSuccess) return r;
+  r = hipEventRecord(e, s);
+  if (r != hipSuccess) return r;
+  h->marks.push_back({b, e, kernel});
+  return hipSuccess;
+}
+
+const char* const kKernelNames[FWPKM_NUM_TIMED] = {"score", "read", "sort", "update", "copy"};
+
+}  // namespace
+
+extern "C" {
+
+const char* fwpkm_last_error(void) { return g_err; }
+
+size_t fwpkm_workspace_bytes(const fwpkm_config* cfg) {
+  if (check_config(cfg) != FWPKM_OK) return 0;
+  return ws_layout(*cfg, (int64_t)cfg->max_batch * cfg->num_heads, cfg->chunk_size).total;
+}
+
+int fwpkm_create(const fwpkm_config* cfg, fwpkm_handle** out) {
+  if (!out) return fail(FWPKM_ERR_INVALID_ARG, "out is NULL");
+  const int rc = check_config(cfg);
+  if (rc != FWPKM_OK) return rc;
+  fwpkm_handle* h = new (std::nothrow) fwpkm_handle();
+  if (!h) return fail(FWPKM_ERR_OOM, "cannot allocate the handle");
+  h->cfg = *cfg;
+  h->ws_bytes = ws_layout(*cfg, (int64_t)cfg->max_batch * cfg->num_heads, cfg->chunk_size).total;
+  *out = h;
+  g_err[0] = '\0';
+  return FWPKM_OK;
+}
+
+void fwpkm_destroy(fwpkm_handle* h) {
+  if (!h) return;
+  if (h->ws) {
+    int prev = -1;
+    if (hipGetDevice(&prev) == hipSuccess && prev != h->device) (void)hipSetDevice(h->device);
+    (void)hipDeviceSynchronize();
+    for (auto& m : h->marks) { (void)hipEventDestroy(m.beg); (void)hipEventDestroy(m.end); }
+    for (auto e : h->spare) (void)hipEventDestroy(e);
+    (void)hipFree(h->ws);
+    if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
+  }
+  delete h;
+}
+
+const char* fwpkm_kernel_name(int32_t i) {
+  return (i >= 0 && i < FWPKM_NUM_TIMED) ? kKernelNames[i] : "";
+}
+
+int fwpkm_profile_enable(fwpkm_handle* h, int32_t enable) {
+  if (!h) return fail(FWPKM_ERR_INVALID_ARG, "handle is NULL");
+  if (enable) {
+    for (auto& m : h->marks) { h->spare.push_back(m.beg); h->spare.push_back(m.end); }
+    h->marks.clear();
+    for (int i = 0; i < FWPKM_NUM_TIMED; ++i) { h->ms[i] = 0.0; h->launches[i] = 0; }
+  }
+  h->prof = enable != 0;
+  return FWPKM_OK;
+}
+
+int fwpkm_profile_read(fwpkm_handle* h, double* ms, int64_t* launches) {
+  if (!h) return fail(FWPKM_ERR_INVALID_ARG, "handle is NULL");
+  for (auto& m : h->marks) {
+    hipError_t e = hipEventSynchronize(m.end);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, m.beg, m.end);
+    if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "timing events: %s", hipGetErrorString(e));
+    h->ms[m.kernel] += t;
+    h->launches[m.kernel] += 1;
+    h->spare.push_back(m.beg);
+    h->spare.push_back(m.end);
+  }
+  h->marks.clear();
+  for (int i = 0; i < FWPKM_NUM_TIMED; ++i) {
+    if (ms) ms[i] = h->ms[i];
+    if (launches) launches[i] = h->launches[i];
+  }
+  return FWPKM_OK;
+}
+
+int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targets,
+                        int32_t batch, int32_t tokens, float lr,
+                        const fwpkm_state* past, const fwpkm_state* next,
+                        float* retrieved, int32_t* out_slots, float* out_weights,
+                        hipStream_t stream) {
+  // ---------------------------------------------------------- validation
+  if (!h) return fail(FWPKM_ERR_INVALID_ARG, "handle is NULL");
+  const fwpkm_config& c = h->cfg;
+  if (!queries || !targets || !retrieved) return fail(FWPKM_ERR_INVALID_ARG, "queries, targets and retrieved must be non-NULL");
+  if (!past || !next) return fail(FWPKM_ERR_INVALID_ARG, "past_state and next_state must be non-NULL");
+  if (!past->k1 || !past->k2 || !past->v || !next->k1 || !next->k2 || !next->v)
+    return fail(FWPKM_ERR_INVALID_ARG, "state table pointers must be non-NULL");
+  if (batch < 1 || batch > c.max_batch) return fail(FWPKM_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, c.max_batch);
+  if (tokens < 1 || tokens > c.chunk_size) return fail(FWPKM_ERR_INVALID_ARG, "tokens %d outside [1, %d]", tokens, c.chunk_size);
+  if (!std::isfinite(lr)) return fail(FWPKM_ERR_INVALID_ARG, "lr must be finite");
+
+  const int n = c.sqrt_slots, half = c.dim_qk / 2, H = c.num_heads, k = c.topk;
+  const int64_t N = (int64_t)n * n;
+  const int64_t sk = (int64_t)H * n * half;        // elements of one sequence's K1 (or K2)
+  const int64_t sv = (int64_t)H * N * c.dim_v;     // elements of one sequence's V
+  auto stride_ok = [&](int64_t st, int64_t size, bool allow_zero) {
+    return (st == 0 && allow_zero) || st >= size;
+  };
+  if (!stride_ok(past->batch_stride_k, sk, true) || !stride_ok(past->batch_stride_v, sv, true))
+    return fail(FWPKM_ERR_INVALID_ARG, "past_state strides must be 0 or at least one sequence's tables");
+  if (!stride_ok(next->batch_stride_k, sk, batch == 1) || !stride_ok(next->batch_stride_v, sv, batch == 1))
+    return fail(FWPKM_ERR_INVALID_ARG, "next_state strides must cover one sequence's tables (0 only when batch == 1)");
+
+  const Range pk1 = table_range(past->k1, past->batch_stride_k, sk, batch);
+  const Range pk2 = table_range(past->k2, past->batch_stride_k, sk, batch);
+  const Range pv = table_range(past->v, past->batch_stride_v, sv, batch);
+  const Range nk1 = table_range(next->k1, next->batch_stride_k, sk, batch);
+  const Range nk2 = table_range(next->k2, next->batch_stride_k, sk, batch);
+  const Range nv = table_range(next->v, next->batch_stride_v, sv, batch);
+  const bool inplace = past->k1 == next->k1 && past->k2 == next->k2 && past->v == next->v &&
+                       past->batch_stride_k == next->batch_stride_k &&
+                       past->batch_stride_v == next->batch_stride_v;
+  if (overlap(nk1, nk2) || overlap(nk1, nv) || overlap(nk2, nv))
+    return fail(FWPKM_ERR_ALIAS, "next_state tables overlap each other");
+  if (!inplace) {
+    const Range ps[3] = {pk1, pk2, pv};
+    const Range ns[3] = {nk1, nk2, nv};
+    for (const Range& a : ps)
+      for (const Range& b : ns)
+        if (overlap(a, b)) return fail(FWPKM_ERR_ALIAS, "next_state partially overlaps past_state");
+  }
+  const int64_t rows = (int64_t)batch * tokens * H;
+  const Range rq = {reinterpret_cast<uintptr_t>(queries), reinterpret_cast<uintptr_t>(queries + rows * c.dim_qk)};
+  const Range ry = {reinterpret_cast<uintptr_t>(targets), reinterpret_cast<uintptr_t>(targets + rows * c.dim_v)};
+  const Range rr = {reinterpret_cast<uintptr_t>(retrieved), reinterpret_cast<uintptr_t>(retrieved + rows * c.dim_v)};
+  const Range outs[3] = {rr,
+                         {reinterpret_cast<uintptr_t>(out_slots), reinterpret_cast<uintptr_t>(out_slots + (out_slots ? rows * k : 0))},
+                         {reinterpret_cast<uintptr_t>(out_weights), reinterpret_cast<uintptr_t>(out_weights + (out_weights ? rows * k : 0))}};
+  const Range ins[8] = {rq, ry, pk1, pk2, pv, nk1, nk2, nv};
+  for (int i = 0; i < 3; ++i) {
+    if (outs[i].lo == outs[i].hi) continue;
+    for (const Range& b : ins)
+      if (overlap(outs[i], b)) return fail(FWPKM_ERR_ALIAS, "an output overlaps an input or the state");
+    for (int j = i + 1; j < 3; ++j)
+      if (outs[j].lo != outs[j].hi && overlap(outs[i], outs[j])) return fail(FWPKM_ERR_ALIAS, "outputs overlap each other");
+  }
+  for (const Range& b : {nk1, nk2, nv})
+    if (overlap(b, rq) || overlap(b, ry)) return fail(FWPKM_ERR_ALIAS, "next_state overlaps queries or targets");
+
+  // ---------------------------------------------------------- workspace
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (!h->ws) {
+    e = hipMalloc(&h->ws, h->ws_bytes);
+    if (e != hipSuccess) {
+      h->ws = nullptr;
+      (void)hipGetLastError();
+      if (e == hipErrorOutOfMemory) return fail(FWPKM_ERR_OOM, "workspace of %zu bytes: %s", h->ws_bytes, hipGetErrorString(e));
+      return fail(FWPKM_ERR_HIP, "hipMalloc: %s", hipGetErrorString(e));
+    }
+    h->device = dev;
+  } else if (dev != h->device) {
+    return fail(FWPKM_ERR_INVALID_ARG, "handle's workspace lives on device %d, current device is %d", h->device, dev);
+  }
+
+  // ---------------------------------------------------------- enqueue
+  if (!inplace) {
+    const struct { float* d; const float* s; int64_t ds, ss, n; } cps[3] = {
+        {next->k1, past->k1, next->batch_stride_k, past->batch_stride_k, sk},
+        {next->k2, past->k2, next->batch_stride_k, past->batch_stride_k, sk},
+        {next->v, past->v, next->batch_stride_v, past->batch_stride_v, sv}};
+    e = timed(h, 4, stream, [&]() {
+      for (const auto& cp : cps) {
+        for (int b = 0; b < batch; ++b) {
+          hipError_t r = hipMemcpyAsync(cp.d + (int64_t)b * cp.ds, cp.s + (int64_t)b * cp.ss,
+                                        sizeof(float) * cp.n, hipMemcpyDeviceToDevice, stream);
+          if (r != hipSuccess) return r;
+        }
+      }
+      return hipSuccess;
+    });
+    if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "state copy: %s", hipGetErrorString(e));
+  }
+
+  const int64_t U = (int64_t)batch * H;
+  const WsLayout L = ws_layout(c, U, tokens);
+  char* ws = static_cast<char*>(h->ws);
+  fwpkm::ChunkArgs a{};
+  a.n = n;
+  a.half = half;
+  a.dqk = c.dim_qk;
+  a.dv = c.dim_v;
+  a.k = k;
+  a.T = tokens;
+  a.H = H;
+  a.U = (int)U;
+  a.nblk = (n + fwpkm::kKeyBlock - 1) / fwpkm::kKeyBlock;
+  a.P = tokens * k;
+  a.key_bits_v = bit_length(N);
+  a.key_bits_k = bit_length(n);
+  a.mode = c.score_mode;
+  a.eps = c.eps;
+  a.lr = lr;
+  a.q = queries;
+  a.y = targets;
+  a.k1 = next->k1;
+  a.k2 = next->k2;
+  a.v = next->v;
+  a.stride_k = next->batch_stride_k;
+  a.stride_v = next->batch_stride_v;
+  a.retrieved = retrieved;
+  a.out_slots = out_slots;
+  a.out_weights = out_weights;
+  a.half_o = reinterpret_cast<float*>(ws + L.half_o);
+  a.half_i = reinterpret_cast<int*>(ws + L.half_i);
+  a.qnorm = reinterpret_cast<float*>(ws + L.qnorm);
+  a.sel_w = reinterpret_cast<float*>(ws + L.sel_w);
+  a.g = reinterpret_cast<float*>(ws + L.g);
+  a.keys = reinterpret_cast<int*>(ws + L.keys);
+  a.coef = reinterpret_cast<float*>(ws + L.coef);
+  a.sorted = reinterpret_cast<int*>(ws + L.sorted);
+  a.seg_start = reinterpret_cast<int*>(ws + L.seg);
+  a.nseg = reinterpret_cast<int*>(ws + L.nseg);
+
+  const bool write = lr != 0.0f;
+  if ((e = timed(h, 0, stream, [&] { return fwpkm::launch_ka(a, stream); })) != hipSuccess)
+    return fail(FWPKM_ERR_HIP, "score kernel: %s", hipGetErrorString(e));
+  if ((e = timed(h, 1, stream, [&] { return fwpkm::launch_kb(a, write, stream); })) != hipSuccess)
+    return fail(FWPKM_ERR_HIP, "read kernel: %s", hipGetErrorString(e));
+  if (write) {
+    if ((e = timed(h, 2, stream, [&] { return fwpkm::launch_kc(a, stream); })) != hipSuccess)
+      return fail(FWPKM_ERR_HIP, "sort kernel: %s", hipGetErrorString(e));
+    if ((e = timed(h, 3, stream, [&] { return fwpkm::launch_kd(a, stream); })) != hipSuccess)
+      return fail(FWPKM_ERR_HIP, "update kernel: %s", hipGetErrorString(e));
+  }
+  g_err[0] = '\0';
+  return FWPKM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,301 @@
+// KB: Cartesian top-k, softmax weights, value gather-reduce and the
+// fast-weight backward, one wave per (unit, token).
+//
+// Read [sciencestack.ai "Fast-weight Product Key Memory", contents entry
+// "Top-k Key-value Memory"; gist.science summary, section 2]:
+//   candidates (a, b) from the per-half best-k lists, ordering key
+//   o1[a] + o2[b], slot a*n + b; keep the k best (key asc, slot asc).
+//   IDW weights  w_m = u_m / sum u,  u_m = 1 / (eps + D_m),
+//                D_m = ||q1||^2 + ||q2||^2 + o1 + o2  (= ||q - K_slot||^2),
+//   which is softmax(-log(eps + D)) written without the log/exp pair;
+//   dot weights  w = softmax(q.K_slot).
+//   out_t = sum_m w_m V[slot_m], summed in rank order.
+// Only candidates (i, j) with (i+1)(j+1) <= k can reach the top k (every
+// (i', j') with i' <= i, j' <= j orders before them), so at most
+// sum_i floor(k/i) <= 64 candidates (k <= 20) are ranked, one per lane.
+//
+// Backward of L = sum_t 1/2 ||out_t - y_t||^2 at the chunk's starting weights
+// [agifrontier tutorial, update equation; sciencestack.ai contents: MSE loss,
+// summation reduction, weighting gradient by row contribution]:
+//   g_t = out_t - y_t,  dL/dV[slot_m] = w_m g_t (left implicit: (slot, pair)
+//   and w are stored, the value gradient is formed in the update kernel),
+//   delta_m = w_m (g_t.V[slot_m] - g_t.out_t),
+//   IDW coefficient c_m = 2 delta_m u_m   (dL/dK1[a] = sum c_m (q1 - K1[a])),
+//   dot coefficient c_m = delta_m         (dL/dK1[a] = sum c_m q1).
+// Candidates of one token that share a K1 (K2) row are merged into one
+// (row, token) pair here, so that the update divides by the number of
+// tokens touching the row [gist.science section 2, gradient aggregation by
+// averaging].
+//
+// The k value rows are fetched as float4 per lane (coalesced 1 KiB per
+// wave-load) and kept in registers for the backward when they fit.
+
+#include "fwpkm_device.h"
+#include "fwpkm_launch.h"
+
+namespace fwpkm {
+
+template <int KMAX, int VR, bool WRITE>
+__global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
+  constexpr bool KEEP = KMAX * VR <= 32;
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int u = blockIdx.y;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  const int k = a.k;
+  const int n = a.n;
+  const int b = u / a.H, hh = u % a.H;
+  const int64_t ut = (int64_t)u * a.T + t;
+  const float inf = __builtin_inff();
+
+  // ---- 1. per-half best-k lists (lane m < k holds the m-th best)
+  float ho[2];
+  int hi[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t base = (ut * 2 + h) * a.nblk * k;
+    if (a.nblk == 1) {
+      ho[h] = lane < k ? a.half_o[base + lane] : inf;
+      hi[h] = lane < k ? a.half_i[base + lane] : kNoIndex;
+    } else {
+      const int nc = a.nblk * k;   // <= 16 * 32 = 512
+      float cv[8];
+      int ci[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = lane + 64 * j;
+        cv[j] = c < nc ? a.half_o[base + c] : inf;
+        ci[j] = c < nc ? a.half_i[base + c] : kNoIndex;
+      }
+      wave_select_k<8>(cv, ci, k, ho[h], hi[h]);
+    }
+  }
+
+  // ---- 2. pruned Cartesian candidates, then the k best
+  int npr = 0;
+  for (int i = 0; i < k; ++i) npr += k / (i + 1);
+  float sel_o;
+  int sel_s;
+  {
+    constexpr int J = 3;   // sum_i floor(32/i) = 130 <= 3 * 64
+    float cv[J];
+    int ci[J];
+#pragma unroll
+    for (int r = 0; r < J; ++r) {
+      int c = lane + 64 * r;
+      const bool in = c < npr;
+      int i = 0;
+      if (in) {
+        while (c >= k / (i + 1)) { c -= k / (i + 1); ++i; }
+      }
+      const int j = in ? c : 0;
+      const float oa = __shfl(ho[0], i, kWave);
+      const int ia = __shfl(hi[0], i, kWave);
+      const float ob = __shfl(ho[1], j, kWave);
+      const int ib = __shfl(hi[1], j, kWave);
+      if (in && ia != kNoIndex && ib != kNoIndex) {
+        cv[r] = order_key(oa + ob);
+        ci[r] = ia * n + ib;
+      } else {
+        cv[r] = inf;
+        ci[r] = kNoIndex;
+      }
+    }
+    if (npr <= 64) {
+      sel_o = cv[0];
+      sel_s = ci[0];
+      wave_bitonic_sort(sel_o, sel_s);
+    } else {
+      wave_select_k<J>(cv, ci, k, sel_o, sel_s);
+    }
+  }
+
+  // ---- 3. weights (lanes m < k)
+  const int64_t N = (int64_t)n * n;
+  const bool active = lane < k && sel_s != kNoIndex;
+  float w = 0.f, uinv = 0.f;
+  if (a.mode == 0) {
+    const float qn = a.qnorm[ut * 2] + a.qnorm[ut * 2 + 1];
+    float D = qn + sel_o;
+    D = D > 0.f ? D : 0.f;
+    uinv = active ? 1.0f / (a.eps + D) : 0.f;
+    const float s = wave_sum(uinv);
+    w = uinv / s;
+  } else {
+    const float smax = -readlane_f(sel_o, 0);
+    const float e = active ? expf(-sel_o - smax) : 0.f;
+    const float s = wave_sum(e);
+    w = e / s;
+  }
+  if (!active) w = 0.f;
+
+  // ---- 4. gather-reduce of the k value rows
+  const float* Vu = a.v + (int64_t)b * a.stride_v + (int64_t)hh * N * a.dv;
+  const int dv4 = a.dv >> 2;
+  float4 acc[VR];
+#pragma unroll
+  for (int j = 0; j < VR; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 rows[KEEP ? KMAX : 1][VR];
+  if (KEEP) {
+#pragma unroll
+    for (int m = 0; m < KMAX; ++m) {
+      if (m < k) {
+        const int s = readlane_i(sel_s, m);
+        const bool ok = s >= 0 && s < N;
+        const float4* row = reinterpret_cast<const float4*>(Vu + (int64_t)(ok ? s : 0) * a.dv);
+#pragma unroll
+        for (int j = 0; j < VR; ++j) {
+          const int c = lane + 64 * j;
+          rows[KEEP ? m : 0][j] = (ok && c < dv4) ? row[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < KMAX; ++m) {
+      if (m < k) {
+        const float wm = readlane_f(w, m);
+#pragma unroll
+        for (int j = 0; j < VR; ++j) {
+          const float4 r = rows[KEEP ? m : 0][j];
+          acc[j].x += wm * r.x; acc[j].y += wm * r.y; acc[j].z += wm * r.z; acc[j].w += wm * r.w;
+        }
+      }
+    }
+  } else {
+    for (int m = 0; m < k; ++m) {
+      const int s = readlane_i(sel_s, m);
+      const bool ok = s >= 0 && s < N;
+      const float wm = readlane_f(w, m);
+      const float4* row = reinterpret_cast<const float4*>(Vu + (int64_t)(ok ? s : 0) * a.dv);
+#pragma unroll
+      for (int j = 0; j < VR; ++j) {
+        const int c = lane + 64 * j;
+        const float4 r = (ok && c < dv4) ? row[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        acc[j].x += wm * r.x; acc[j].y += wm * r.y; acc[j].z += wm * r.z; acc[j].w += wm * r.w;
+      }
+    }
+  }
+
+  // ---- outputs of the read
+  const int64_t io = ((int64_t)(b * a.T + t) * a.H + hh);
+  float4* ret = reinterpret_cast<float4*>(a.retrieved + io * a.dv);
+#pragma unroll
+  for (int j = 0; j < VR; ++j) {
+    const int c = lane + 64 * j;
+    if (c < dv4) ret[c] = acc[j];
+  }
+  if (lane < k) {
+    if (a.out_slots) a.out_slots[io * k + lane] = sel_s;
+    if (a.out_weights) a.out_weights[io * k + lane] = w;
+  }
+  if (!WRITE) return;
+
+  // ---- 5. backward
+  const float4* yr = reinterpret_cast<const float4*>(a.y + io * a.dv);
+  float4* gw = reinterpret_cast<float4*>(a.g + ut * a.dv);
+  float4 g[VR];
+  float gout = 0.f;
+#pragma unroll
+  for (int j = 0; j < VR; ++j) {
+    const int c = lane + 64 * j;
+    g[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < dv4) {
+      const float4 yy = yr[c];
+      g[j] = make_float4(acc[j].x - yy.x, acc[j].y - yy.y, acc[j].z - yy.z, acc[j].w - yy.w);
+      gw[c] = g[j];
+      gout += g[j].x * acc[j].x + g[j].y * acc[j].y + g[j].z * acc[j].z + g[j].w * acc[j].w;
+    }
+  }
+  gout = wave_sum(gout);
+  float gv_mine = 0.f;
+  if (KEEP) {
+#pragma unroll
+    for (int m = 0; m < KMAX; ++m) {
+      if (m < k) {
+        float part = 0.f;
+#pragma unroll
+        for (int j = 0; j < VR; ++j) {
+          const float4 r = rows[KEEP ? m : 0][j];
+          part += g[j].x * r.x + g[j].y * r.y + g[j].z * r.z + g[j].w * r.w;
+        }
+        part = wave_sum(part);
+        if (lane == m) gv_mine = part;
+      }
+    }
+  } else {
+    for (int m = 0; m < k; ++m) {
+      const int s = readlane_i(sel_s, m);
+      const bool ok = s >= 0 && s < N;
+      const float4* row = reinterpret_cast<const float4*>(Vu + (int64_t)(ok ? s : 0) * a.dv);
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < VR; ++j) {
+        const int c = lane + 64 * j;
+        const float4 r = (ok && c < dv4) ? row[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        part += g[j].x * r.x + g[j].y * r.y + g[j].z * r.z + g[j].w * r.w;
+      }
+      part = wave_sum(part);
+      if (lane == m) gv_mine = part;
+    }
+  }
+  const float delta = w * (gv_mine - gout);
+  const float c = (a.mode == 0) ? 2.0f * delta * uinv : delta;
+
+  // ---- 6. pair lists: V (slot), K1 (row a), K2 (row b), merged per token
+  const int am = active ? sel_s / n : n;
+  const int bm = active ? sel_s - am * n : n;
+  float sum1 = 0.f, sum2 = 0.f;
+  bool first1 = true, first2 = true;
+  for (int m = 0; m < k; ++m) {
+    const int a2 = readlane_i(am, m);
+    const int b2 = readlane_i(bm, m);
+    const float c2 = readlane_f(c, m);
+    if (a2 == am) { sum1 += c2; if (m < lane) first1 = false; }
+    if (b2 == bm) { sum2 += c2; if (m < lane) first2 = false; }
+  }
+  if (lane < k) {
+    const int64_t p = (int64_t)u * a.P + (int64_t)t * k + lane;
+    const int64_t UP = (int64_t)a.U * a.P;
+    a.keys[p] = active ? sel_s : (int)N;   // N marks "no slot"; it sorts last
+    a.sel_w[p] = w;
+    const bool k1ok = active && first1;
+    const bool k2ok = active && first2;
+    a.keys[UP + p] = k1ok ? am : n;
+    a.keys[2 * UP + p] = k2ok ? bm : n;
+    a.coef[p] = k1ok ? sum1 : 0.f;
+    a.coef[UP + p] = k2ok ? sum2 : 0.f;
+  }
+}
+
+namespace {
+
+template <int KMAX, int VR>
+hipError_t launch_kb_t(const ChunkArgs& a, bool write, hipStream_t s) {
+  dim3 grid((a.T + 3) / 4, a.U);
+  if (write)
+    hipLaunchKernelGGL((kb_read<KMAX, VR, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((kb_read<KMAX, VR, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KMAX>
+hipError_t launch_kb_k(const ChunkArgs& a, bool write, hipStream_t s) {
+  const int vr = ((a.dv >> 2) + 63) / 64;
+  if (vr <= 1) return launch_kb_t<KMAX, 1>(a, write, s);
+  if (vr <= 2) return launch_kb_t<KMAX, 2>(a, write, s);
+  if (vr <= 4) return launch_kb_t<KMAX, 4>(a, write, s);
+  return launch_kb_t<KMAX, 8>(a, write, s);
+}
+
+}  // namespace
+
+hipError_t launch_kb(const ChunkArgs& a, bool write, hipStream_t s) {
+  if (a.k <= 4) return launch_kb_k<4>(a, write, s);
+  if (a.k <= 8) return launch_kb_k<8>(a, write, s);
+  if (a.k <= 16) return launch_kb_k<16>(a, write, s);
+  return launch_kb_k<32>(a, write, s);
+}
+
+}  // namespace fwpkm

@@ -1,0 +1,189 @@
+"""Python binding of the FwPKM chunk step (argument marshalling only).
+
+    mem = Memory(Config(sqrt_slots=256, dim_qk=512, dim_v=512, topk=8,
+                        chunk_size=256, max_batch=2))
+    retrieved, next_state = mem.forward_chunk(queries, targets, lr, past_state)
+
+mirrors the chained ``mem(tokens, past_memories=...) -> (retrieved,
+next_memories)`` usage on the PyPI page "fast-weight-product-key-memory",
+with queries and targets passed in directly.  Every step of the computation
+runs in the HIP library; torch provides device memory and the stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib
+
+
+class FwPKMError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"fwpkm error {code}: {message}")
+        self.code = code
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    sqrt_slots: int
+    dim_qk: int
+    dim_v: int
+    topk: int
+    chunk_size: int
+    num_heads: int = 1
+    max_batch: int = 1
+    eps: float = 1e-3
+    score_mode: str = "idw"      # "idw" or "dot"
+
+    @property
+    def num_slots(self) -> int:
+        return self.sqrt_slots * self.sqrt_slots
+
+    @property
+    def half(self) -> int:
+        return self.dim_qk // 2
+
+    def to_c(self) -> _lib.CConfig:
+        mode = {"idw": _lib.SCORE_IDW, "dot": _lib.SCORE_DOT}.get(self.score_mode, -1)
+        return _lib.CConfig(self.sqrt_slots, self.dim_qk, self.dim_v, self.topk,
+                            self.chunk_size, self.num_heads, self.max_batch,
+                            float(self.eps), mode)
+
+
+class State(NamedTuple):
+    """Fast weights on the GPU, fp32 contiguous.
+
+    Per-sequence tables: k1, k2 [B, H, n, d_h], v [B, H, N, d_v].
+    Shared tables (one set for the whole batch; past state only):
+    k1, k2 [H, n, d_h], v [H, N, d_v].
+    """
+    k1: torch.Tensor
+    k2: torch.Tensor
+    v: torch.Tensor
+
+    def clone(self) -> "State":
+        return State(self.k1.clone(), self.k2.clone(), self.v.clone())
+
+
+def _check_tensor(name, t, dtype=torch.float32):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _c_state(s: State, cfg: Config) -> _lib.CState:
+    per_k = cfg.num_heads * cfg.sqrt_slots * cfg.half
+    per_v = cfg.num_heads * cfg.num_slots * cfg.dim_v
+    for name, t in (("k1", s.k1), ("k2", s.k2), ("v", s.v)):
+        _check_tensor(f"state.{name}", t)
+    shared = s.k1.dim() == 3
+    if shared:
+        stride_k = stride_v = 0
+    else:
+        stride_k, stride_v = per_k, per_v
+    if s.k1.numel() % per_k or s.k2.numel() != s.k1.numel() or s.v.numel() % per_v:
+        raise ValueError("state tables do not match the configuration")
+    return _lib.CState(s.k1.data_ptr(), s.k2.data_ptr(), s.v.data_ptr(), stride_k, stride_v)
+
+
+def empty_state(cfg: Config, batch: int, device="cuda") -> State:
+    n, dh, N, dv, H = cfg.sqrt_slots, cfg.half, cfg.num_slots, cfg.dim_v, cfg.num_heads
+    return State(torch.empty((batch, H, n, dh), device=device),
+                 torch.empty((batch, H, n, dh), device=device),
+                 torch.empty((batch, H, N, dv), device=device))
+
+
+class Memory:
+    """One handle of the C ABI: a configuration plus its device workspace."""
+
+    def __init__(self, cfg: Config):
+        self.cfg = cfg
+        self._lib = _lib.load()
+        self._c_cfg = cfg.to_c()
+        h = ctypes.c_void_p()
+        rc = self._lib.fwpkm_create(ctypes.byref(self._c_cfg), ctypes.byref(h))
+        if rc != _lib.OK:
+            raise FwPKMError(rc, _lib.last_error())
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.fwpkm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def profile(self, enable: bool = True) -> None:
+        """Start (clearing totals) or stop per-kernel event timing."""
+        rc = self._lib.fwpkm_profile_enable(self._h, 1 if enable else 0)
+        if rc != _lib.OK:
+            raise FwPKMError(rc, _lib.last_error())
+
+    def profile_read(self) -> dict:
+        """{kernel name: (total ms, launches)} of the timed launches so far."""
+        ms = (ctypes.c_double * _lib.NUM_TIMED)()
+        cnt = (ctypes.c_int64 * _lib.NUM_TIMED)()
+        rc = self._lib.fwpkm_profile_read(self._h, ms, cnt)
+        if rc != _lib.OK:
+            raise FwPKMError(rc, _lib.last_error())
+        return {self._lib.fwpkm_kernel_name(i).decode(): (ms[i], int(cnt[i]))
+                for i in range(_lib.NUM_TIMED)}
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self._lib.fwpkm_workspace_bytes(ctypes.byref(self._c_cfg)))
+
+    def forward_chunk(self, queries: torch.Tensor, targets: torch.Tensor, lr: float,
+                      past: State, next: Optional[State] = None,
+                      return_selection: bool = False, retrieved: Optional[torch.Tensor] = None):
+        """One chunk: (retrieved [B, T, H, d_v], next state) from past state.
+
+        queries [B, T, H, d_qk] (or [B, T, d_qk] when H == 1), targets likewise
+        with d_v.  next=None allocates per-sequence tables and fills them
+        (functional update); next=past updates in place.
+        """
+        cfg = self.cfg
+        _check_tensor("queries", queries)
+        _check_tensor("targets", targets)
+        B, T = queries.shape[0], queries.shape[1]
+        if queries.numel() != B * T * cfg.num_heads * cfg.dim_qk:
+            raise ValueError("queries must be [B, T, H, d_qk]")
+        if targets.numel() != B * T * cfg.num_heads * cfg.dim_v or targets.shape[:2] != queries.shape[:2]:
+            raise ValueError("targets must be [B, T, H, d_v]")
+        if next is None:
+            next = empty_state(cfg, B, queries.device)
+        c_past = _c_state(past, cfg)
+        c_next = _c_state(next, cfg)
+        if retrieved is None:
+            retrieved = torch.empty((B, T, cfg.num_heads, cfg.dim_v), device=queries.device)
+        else:
+            _check_tensor("retrieved", retrieved)
+        slots = weights = None
+        if return_selection:
+            slots = torch.empty((B, T, cfg.num_heads, cfg.topk), device=queries.device, dtype=torch.int32)
+            weights = torch.empty((B, T, cfg.num_heads, cfg.topk), device=queries.device)
+        stream = torch.cuda.current_stream(queries.device).cuda_stream
+        rc = self._lib.fwpkm_forward_chunk(
+            self._h, queries.data_ptr(), targets.data_ptr(), B, T, float(lr),
+            ctypes.byref(c_past), ctypes.byref(c_next), retrieved.data_ptr(),
+            slots.data_ptr() if slots is not None else None,
+            weights.data_ptr() if weights is not None else None,
+            stream)
+        if rc != _lib.OK:
+            raise FwPKMError(rc, _lib.last_error())
+        if return_selection:
+            return retrieved, next, slots, weights
+        return retrieved, next

@@ -1,0 +1,243 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Small and edge-case shapes, every chunk compared in full, plus GPU
+properties: determinism, lr = 0, in-place vs copy, shared-state expansion,
+unit independence and checkpoint/resume.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fwpkm_oracle as O
+from parity_helpers import (ATOL_CHAIN, ATOL_CHUNK, RTOL_CHAIN, RTOL_CHUNK, assert_close,
+                            compare_chunk, need_gpu, oracle_units, say, selection_overrides,
+                            state_to_dev, state_to_host, to_dev)
+from workloads import chunk_inputs, draw_queries, draw_targets, get_config, initial_tables
+from workloads.generate import expand_tables
+
+pytestmark = pytest.mark.gpu
+
+
+def _mem(**kw):
+    from sparse_weight_memory_amd import Config, Memory
+    return Memory(Config(**kw))
+
+
+def _random_case(seed, B, H, C, n, half, dv, q_std=1.0):
+    rng = np.random.default_rng(seed)
+    U = B * H
+    st = {"k1": (rng.standard_normal((U, n, half)) / np.sqrt(half)).astype(np.float32),
+          "k2": (rng.standard_normal((U, n, half)) / np.sqrt(half)).astype(np.float32),
+          "v": (rng.standard_normal((U, n * n, dv)) * 0.14).astype(np.float32)}
+    q = (rng.standard_normal((B, C, H, 2 * half)) * q_std).astype(np.float32)
+    y = rng.standard_normal((B, C, H, dv)).astype(np.float32)
+    return st, q, y
+
+
+def _workload_state(cfg):
+    t = initial_tables(cfg)
+    ex = expand_tables(t, cfg.batch)
+    return {"k1": ex.k1, "k2": ex.k2, "v": ex.v}
+
+
+# ------------------------------------------------------------ tiny workload
+
+def test_tiny_workload_teacher_forced_every_chunk():
+    need_gpu()
+    w = get_config(1)
+    mem = _mem(sqrt_slots=w.sqrt_slots, dim_qk=w.dim_qk, dim_v=w.dim_v, topk=w.topk,
+               chunk_size=w.chunk, num_heads=w.heads, max_batch=w.batch, eps=w.eps)
+    st = _workload_state(w)
+    Q, Y = draw_queries(w), draw_targets(w)
+    total_ties = 0
+    for c in range(w.chunks):
+        ci = chunk_inputs(Q, Y, w, c)
+        st, ties, _ = compare_chunk(mem, st, ci.queries, ci.targets, w.lr, label=f"tiny c{c}")
+        total_ties += ties
+    say("tiny near-ties", total_ties)
+
+
+def test_tiny_workload_chained():
+    need_gpu()
+    w = get_config(1)
+    mem = _mem(sqrt_slots=w.sqrt_slots, dim_qk=w.dim_qk, dim_v=w.dim_v, topk=w.topk,
+               chunk_size=w.chunk, num_heads=w.heads, max_batch=w.batch, eps=w.eps)
+    st0 = _workload_state(w)
+    Q, Y = draw_queries(w), draw_targets(w)
+    dev = state_to_dev(st0, w.batch, w.heads)
+    ost = {k: v.copy() for k, v in st0.items()}
+    for c in range(w.chunks):
+        ci = chunk_inputs(Q, Y, w, c)
+        ret, dev, slots, _ = mem.forward_chunk(to_dev(ci.queries), to_dev(ci.targets), w.lr, dev,
+                                               next=dev, return_selection=True)
+        slots = slots.cpu().numpy()
+        rets, new, res = oracle_units(ost, ci.queries, ci.targets, w.lr, w.topk, w.eps, O.IDW, [0], 1)
+        ov, _ = selection_overrides(res, slots, 1, [0])
+        if ov:
+            rets, new, res = oracle_units(ost, ci.queries, ci.targets, w.lr, w.topk, w.eps, O.IDW, [0], 1, ov)
+        ost = new
+    got = state_to_host(dev)
+    assert_close("chained retrieved", ret.cpu().numpy()[0, :, 0], rets[0], RTOL_CHAIN, ATOL_CHAIN)
+    for name in ("k1", "k2", "v"):
+        assert_close(f"chained {name}", got[name], ost[name], RTOL_CHAIN, ATOL_CHAIN)
+
+
+# ------------------------------------------------------------ edge shapes
+
+EDGE = [
+    # (label, B, H, C_max, T, n, half, dv, k, mode)
+    ("ragged-tail", 2, 1, 64, 37, 16, 8, 12, 3, "idw"),
+    ("one-token", 1, 1, 64, 1, 8, 4, 8, 2, "idw"),
+    ("k-equals-n", 1, 1, 32, 32, 6, 4, 8, 6, "idw"),
+    ("k1", 2, 2, 40, 40, 12, 4, 8, 1, "idw"),
+    ("n-not-multiple", 1, 2, 48, 48, 300, 20, 36, 5, "idw"),
+    ("wide-dv", 1, 1, 32, 32, 16, 8, 1040, 4, "idw"),
+    ("k16-two-blocks", 1, 1, 64, 64, 520, 16, 64, 16, "idw"),
+    ("k24-fallback", 1, 1, 32, 32, 64, 8, 32, 24, "idw"),
+    ("k32-max", 1, 1, 32, 32, 40, 4, 600, 32, "idw"),
+    ("dot-small", 2, 1, 64, 64, 16, 8, 12, 4, "dot"),
+    ("dot-k16", 1, 2, 64, 50, 64, 16, 32, 16, "dot"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_shapes(case):
+    need_gpu()
+    label, B, H, Cmax, T, n, half, dv, k, mode = case
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=Cmax, num_heads=H,
+               max_batch=B + 1, score_mode=mode)
+    st, q, y = _random_case(zlib.crc32(label.encode()) % 1000, B, H, T, n, half, dv)
+    for c, lr in enumerate((1.0, 0.5)):
+        st, _, _ = compare_chunk(mem, st, q, y, lr, label=f"{label} step{c}")
+
+
+def test_closed_form_k1_single_token_writes_target():
+    need_gpu()
+    n, half, dv = 16, 8, 32
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=1, chunk_size=8)
+    st, q, y = _random_case(5, 1, 1, 1, n, half, dv)
+    dev = state_to_dev(st, 1, 1)
+    _, nxt, slots, w = mem.forward_chunk(to_dev(q), to_dev(y), 1.0, dev, next=dev, return_selection=True)
+    hit = int(slots[0, 0, 0, 0])
+    assert float(w[0, 0, 0, 0]) == 1.0
+    # in fp32 the step is V - (V - y): exact up to the rounding of V - y
+    got = nxt.v[0, 0, hit].cpu().numpy().astype(np.float64)
+    bound = 2 * np.finfo(np.float32).eps * (np.abs(y[0, 0, 0]) + np.abs(st["v"][0, hit]))
+    assert np.all(np.abs(got - y[0, 0, 0]) <= bound)
+
+
+# ------------------------------------------------------------ properties
+
+def _small_mem_and_case(seed=11, B=3, H=2, C=64, n=32, half=16, dv=64, k=4):
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=C, num_heads=H, max_batch=B)
+    return mem, _random_case(seed, B, H, C, n, half, dv)
+
+
+def test_lr_zero_leaves_state_bitwise_and_reads_match():
+    need_gpu()
+    mem, (st, q, y) = _small_mem_and_case()
+    dev = state_to_dev(st, 3, 2)
+    before = [t.clone() for t in dev]
+    ret, nxt = mem.forward_chunk(to_dev(q), to_dev(y), 0.0, dev, next=dev)
+    for a, b in zip(before, nxt):
+        assert torch.equal(a, b)
+    compare_chunk(mem, st, q, y, 0.0, label="lr0")
+
+
+def test_repeat_runs_are_bitwise_identical():
+    need_gpu()
+    mem, (st, q, y) = _small_mem_and_case(seed=12)
+    outs = []
+    for _ in range(3):
+        dev = state_to_dev(st, 3, 2)
+        ret, nxt = mem.forward_chunk(to_dev(q), to_dev(y), 1.0, dev, next=dev)
+        torch.cuda.synchronize()
+        outs.append((ret.cpu(), [t.cpu() for t in nxt]))
+    for ret, tabs in outs[1:]:
+        assert torch.equal(ret, outs[0][0])
+        for a, b in zip(tabs, outs[0][1]):
+            assert torch.equal(a, b)
+
+
+def test_in_place_equals_copy_mode_and_shared_expansion():
+    need_gpu()
+    from sparse_weight_memory_amd import State
+    mem, (st, q, y) = _small_mem_and_case(seed=13)
+    # shared initial tables: make every sequence's tables equal to sequence 0's
+    B, H = 3, 2
+    for name in st:
+        per = st[name].reshape(B, H, *st[name].shape[1:])
+        per[:] = per[0:1]
+    dev = state_to_dev(st, B, H)
+    r1, n1 = mem.forward_chunk(to_dev(q), to_dev(y), 1.0, dev, next=dev)       # in place
+    shared = State(to_dev(st["k1"].reshape(B, H, *st["k1"].shape[1:])[0]),
+                   to_dev(st["k2"].reshape(B, H, *st["k2"].shape[1:])[0]),
+                   to_dev(st["v"].reshape(B, H, *st["v"].shape[1:])[0]))
+    keep = [t.clone() for t in shared]
+    r2, n2 = mem.forward_chunk(to_dev(q), to_dev(y), 1.0, shared)              # copy + expand
+    torch.cuda.synchronize()
+    assert torch.equal(r1, r2)
+    for a, b in zip(n1, n2):
+        assert torch.equal(a, b)
+    for a, b in zip(keep, shared):                                             # past untouched
+        assert torch.equal(a, b)
+
+
+def test_units_are_independent_on_gpu():
+    need_gpu()
+    mem, (st, q, y) = _small_mem_and_case(seed=14)
+    dev1 = state_to_dev(st, 3, 2)
+    r1, n1 = mem.forward_chunk(to_dev(q), to_dev(y), 1.0, dev1, next=dev1)
+    q2, y2 = q.copy(), y.copy()
+    q2[1, :, 1] += 0.5
+    y2[1, :, 1] -= 1.0
+    dev2 = state_to_dev(st, 3, 2)
+    r2, n2 = mem.forward_chunk(to_dev(q2), to_dev(y2), 1.0, dev2, next=dev2)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (0, 1), (1, 0), (2, 0), (2, 1)]:
+        assert torch.equal(r1[b, :, h], r2[b, :, h])
+        for a, c in zip(n1, n2):
+            assert torch.equal(a[b, h], c[b, h])
+    assert not torch.equal(r1[1, :, 1], r2[1, :, 1])
+
+
+def test_checkpoint_resume_is_bitwise():
+    need_gpu()
+    from sparse_weight_memory_amd import State
+    w = get_config(1)
+    mem = _mem(sqrt_slots=w.sqrt_slots, dim_qk=w.dim_qk, dim_v=w.dim_v, topk=w.topk,
+               chunk_size=w.chunk, max_batch=1)
+    st0 = _workload_state(w)
+    Q, Y = draw_queries(w), draw_targets(w)
+    chunks = [chunk_inputs(Q, Y, w, c) for c in range(w.chunks)]
+    a = state_to_dev(st0, 1, 1)
+    for ci in chunks:
+        ra, a = mem.forward_chunk(to_dev(ci.queries), to_dev(ci.targets), 1.0, a, next=a)
+    b = state_to_dev(st0, 1, 1)
+    for ci in chunks[:2]:
+        rb, b = mem.forward_chunk(to_dev(ci.queries), to_dev(ci.targets), 1.0, b, next=b)
+    saved = [t.cpu().numpy().copy() for t in b]                                 # "checkpoint"
+    del b
+    b = State(*[to_dev(x) for x in saved])
+    for ci in chunks[2:]:
+        rb, b = mem.forward_chunk(to_dev(ci.queries), to_dev(ci.targets), 1.0, b, next=b)
+    torch.cuda.synchronize()
+    assert torch.equal(ra, rb)
+    for x, z in zip(a, b):
+        assert torch.equal(x, z)
+
+
+def test_errors_leave_outputs_untouched():
+    need_gpu()
+    from sparse_weight_memory_amd import FwPKMError
+    mem, (st, q, y) = _small_mem_and_case(seed=15)
+    dev = state_to_dev(st, 3, 2)
+    ret = torch.full((3, 64, 2, 64), 7.0, device="cuda")
+    with pytest.raises(FwPKMError) as ei:
+        mem.forward_chunk(to_dev(q), to_dev(y), float("nan"), dev, next=dev, retrieved=ret)
+    assert ei.value.code == -1
+    torch.cuda.synchronize()
+    assert bool((ret == 7.0).all())
