@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
-DEFAULT_WORKLOAD = 2            # 65,536 slots, d_v 512, top-8, batch 2 x 256 tokens
+DEFAULT_WORKLOAD = 3            # 65,536 slots, d_v 512, top-8: 8 x 4096 tokens in 16 chained chunks
 
 
 def parse():
@@ -43,7 +43,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile-pass", action="store_true",
                     help="skip the per-kernel event pass (for external profilers)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB, 5 times (to "
+                         "calibrate HBM byte counters against a known size), then exit")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "copies": 5}))
 
 
 def algorithmic_cost(cfg, kernel, tokens, uniq_v, uniq_k):
@@ -108,6 +124,9 @@ def cpu_baseline(cfg, tables, Q, Y, seconds):
 
 def main():
     args = parse()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "memory units are independent, so N GPUs would each run this step on "

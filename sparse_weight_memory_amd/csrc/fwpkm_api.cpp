@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -28,17 +29,12 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int bit_length(int64_t x) {
-  int b = 0;
-  while (x > 0) { ++b; x >>= 1; }
-  return b;
-}
-
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Byte sizes of the workspace regions for `units` units of `tokens` tokens.
 struct WsLayout {
-  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, sorted, seg, nseg, total;
+  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, sorted, seg, nseg;
+  size_t long_seg, short_seg, seg_kinds, total;
 };
 
 WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
@@ -57,6 +53,9 @@ WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
   L.sorted = take(sizeof(int) * 3 * units * P);
   L.seg = take(sizeof(int) * 3 * units * (P + 1));
   L.nseg = take(sizeof(int) * 3 * units);
+  L.long_seg = take(sizeof(int) * 3 * units * P);
+  L.short_seg = take(sizeof(int) * 3 * units * P);
+  L.seg_kinds = take(sizeof(int) * 3 * units * 2);
   L.total = off;
   return L;
 }
@@ -85,7 +84,8 @@ int check_config(const fwpkm_config* c) {
   if ((int64_t)c->chunk_size * c->topk > fwpkm::kSortMaxPairs)
     return fail(FWPKM_ERR_UNSUPPORTED, "chunk_size * topk > %d", fwpkm::kSortMaxPairs);
   const int64_t units = (int64_t)c->max_batch * c->num_heads;
-  if (units > (1 << 20)) return fail(FWPKM_ERR_UNSUPPORTED, "max_batch * num_heads too large");
+  if (3 * units > fwpkm::kUpdMaxLists)
+    return fail(FWPKM_ERR_UNSUPPORTED, "max_batch * num_heads > %d", fwpkm::kUpdMaxLists / 3);
   return FWPKM_OK;
 }
 
@@ -130,19 +130,18 @@ hipEvent_t take_event(fwpkm_handle* h) {
   return e;
 }
 
-// Launch `fn` on `s`, bracketed by timing events when profiling is on.
+// Run `fn(timing)`: with profiling on, `timing` carries a start/stop event
+// pair that the launch stamps (kernels: from the dispatch itself).
 template <typename F>
-hipError_t timed(fwpkm_handle* h, int kernel, hipStream_t s, F&& fn) {
-  if (!h->prof) return fn();
-  hipEvent_t b = take_event(h), e = take_event(h);
-  if (!b || !e) return hipErrorOutOfMemory;
-  hipError_t r = hipEventRecord(b, s);
+hipError_t timed(fwpkm_handle* h, int kernel, F&& fn) {
+  if (!h->prof) return fn(nullptr);
+  fwpkm::LaunchTiming tm;
+  tm.beg = take_event(h);
+  tm.end = take_event(h);
+  if (!tm.beg || !tm.end) return hipErrorOutOfMemory;
+  hipError_t r = fn(&tm);
   if (r != hipSuccess) return r;
-  r = fn();
-  if (r != hipSuccess) return r;
-  r = hipEventRecord(e, s);
-  if (r != hipSuccess) return r;
-  h->marks.push_back({b, e, kernel});
+  h->marks.push_back({tm.beg, tm.end, kernel});
   return hipSuccess;
 }
 
@@ -308,15 +307,16 @@ int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targ
         {next->k1, past->k1, next->batch_stride_k, past->batch_stride_k, sk},
         {next->k2, past->k2, next->batch_stride_k, past->batch_stride_k, sk},
         {next->v, past->v, next->batch_stride_v, past->batch_stride_v, sv}};
-    e = timed(h, 4, stream, [&]() {
+    e = timed(h, 4, [&](const fwpkm::LaunchTiming* tm) {
+      hipError_t r = tm ? hipEventRecord(tm->beg, stream) : hipSuccess;
       for (const auto& cp : cps) {
-        for (int b = 0; b < batch; ++b) {
-          hipError_t r = hipMemcpyAsync(cp.d + (int64_t)b * cp.ds, cp.s + (int64_t)b * cp.ss,
-                                        sizeof(float) * cp.n, hipMemcpyDeviceToDevice, stream);
-          if (r != hipSuccess) return r;
+        for (int b = 0; b < batch && r == hipSuccess; ++b) {
+          r = hipMemcpyAsync(cp.d + (int64_t)b * cp.ds, cp.s + (int64_t)b * cp.ss,
+                             sizeof(float) * cp.n, hipMemcpyDeviceToDevice, stream);
         }
       }
-      return hipSuccess;
+      if (r == hipSuccess && tm) r = hipEventRecord(tm->end, stream);
+      return r;
     });
     if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "state copy: %s", hipGetErrorString(e));
   }
@@ -333,10 +333,9 @@ int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targ
   a.T = tokens;
   a.H = H;
   a.U = (int)U;
-  a.nblk = (n + fwpkm::kKeyBlock - 1) / fwpkm::kKeyBlock;
+  a.key_block = fwpkm::score_key_block((int)U, tokens, n);
+  a.nblk = (n + a.key_block - 1) / a.key_block;
   a.P = tokens * k;
-  a.key_bits_v = bit_length(N);
-  a.key_bits_k = bit_length(n);
   a.mode = c.score_mode;
   a.eps = c.eps;
   a.lr = lr;
@@ -360,16 +359,21 @@ int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targ
   a.sorted = reinterpret_cast<int*>(ws + L.sorted);
   a.seg_start = reinterpret_cast<int*>(ws + L.seg);
   a.nseg = reinterpret_cast<int*>(ws + L.nseg);
+  a.long_seg = reinterpret_cast<int*>(ws + L.long_seg);
+  a.short_seg = reinterpret_cast<int*>(ws + L.short_seg);
+  a.seg_kinds = reinterpret_cast<int*>(ws + L.seg_kinds);
+  a.pw = std::max(c.dim_v, half);
 
   const bool write = lr != 0.0f;
-  if ((e = timed(h, 0, stream, [&] { return fwpkm::launch_ka(a, stream); })) != hipSuccess)
+  using fwpkm::LaunchTiming;
+  if ((e = timed(h, 0, [&](const LaunchTiming* tm) { return fwpkm::launch_ka(a, stream, tm); })) != hipSuccess)
     return fail(FWPKM_ERR_HIP, "score kernel: %s", hipGetErrorString(e));
-  if ((e = timed(h, 1, stream, [&] { return fwpkm::launch_kb(a, write, stream); })) != hipSuccess)
+  if ((e = timed(h, 1, [&](const LaunchTiming* tm) { return fwpkm::launch_kb(a, write, stream, tm); })) != hipSuccess)
     return fail(FWPKM_ERR_HIP, "read kernel: %s", hipGetErrorString(e));
   if (write) {
-    if ((e = timed(h, 2, stream, [&] { return fwpkm::launch_kc(a, stream); })) != hipSuccess)
+    if ((e = timed(h, 2, [&](const LaunchTiming* tm) { return fwpkm::launch_kc(a, stream, tm); })) != hipSuccess)
       return fail(FWPKM_ERR_HIP, "sort kernel: %s", hipGetErrorString(e));
-    if ((e = timed(h, 3, stream, [&] { return fwpkm::launch_kd(a, stream); })) != hipSuccess)
+    if ((e = timed(h, 3, [&](const LaunchTiming* tm) { return fwpkm::launch_kd(a, stream, tm); })) != hipSuccess)
       return fail(FWPKM_ERR_HIP, "update kernel: %s", hipGetErrorString(e));
   }
   g_err[0] = '\0';

@@ -8,12 +8,13 @@
 namespace fwpkm {
 
 constexpr int kWave = 64;
-constexpr int kKeyBlock = 256;      // sub-keys scored by one score workgroup
+constexpr int kKeyBlock = 64;       // smallest key block of the score kernel
 constexpr int kTokTile = 16;        // tokens per score workgroup (MFMA N)
 constexpr int kSortThreads = 1024;  // threads of one sort workgroup
 constexpr int kSortMaxPairs = 8192; // C*k limit of the in-LDS sort
-constexpr int kDigitBits = 6;       // radix digit of the sort
+constexpr int kShortSeg = 16;       // longest segment one update wave sums alone
 constexpr int kUpdWaves = 4;        // waves per update workgroup
+constexpr int kUpdMaxLists = 3072;  // 3 * units the update kernel can index
 #define FWPKM_MAX_HALF_DIM 1024     // largest d_h the score kernel stages
 
 // Invalid entries: they order after every real candidate.
@@ -30,10 +31,9 @@ struct ChunkArgs {
   int T;          // tokens of this call
   int H;          // heads
   int U;          // units = batch * H
-  int nblk;       // key blocks per half = ceil(n / kKeyBlock)
+  int key_block;  // sub-keys per score workgroup (64, 128 or 256)
+  int nblk;       // key blocks per half = ceil(n / key_block)
   int P;          // pairs per unit = T * k
-  int key_bits_v; // bits of a V key (slot)
-  int key_bits_k; // bits of a K key (row, with the n marker)
   int mode;       // 0 IDW, 1 dot
   float eps;
   float lr;
@@ -61,6 +61,10 @@ struct ChunkArgs {
   int* sorted;     // [3, U, P] pair indices ordered by key (stable)
   int* seg_start;  // [3, U, P + 1] first sorted position of each segment
   int* nseg;       // [3, U] segments per list
+  int* long_seg;   // [3, U, P] segments of more than kShortSeg pairs
+  int* short_seg;  // [3, U, P] the other segments
+  int* seg_kinds;  // [3 * U, 2] (long count, short count)
+  int pw;          // floats per row = max(d_v, d_h)
 };
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
@@ -70,8 +74,42 @@ __device__ __forceinline__ bool precedes(float a, int ia, float b, int ib) {
   return a < b || (a == b && ia < ib);
 }
 
-__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, kWave); }
-__device__ __forceinline__ int shfl_xor_i(int x, int m) { return __shfl_xor(x, m, kWave); }
+// ---- cross-lane exchange with lane ^ S, without the LDS permute unit:
+// DPP quad permutes for S = 1, 2; row shifts for S = 4; a row rotation for
+// S = 8; the gfx950 half-swap instructions for S = 16, 32.  All lanes of the
+// wave must be active.
+template <int S>
+__device__ __forceinline__ int xor_lane(int x) {
+  static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "stride");
+  if constexpr (S == 1) {
+    return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (S == 2) {
+    return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (S == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0xF, false);   // row_shl:4
+    const int dn = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    return (lane_id() & 4) ? dn : up;
+  } else if constexpr (S == 8) {
+    return __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (S == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane_id() & 16) ? (int)p[0] : (int)p[1];
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane_id() & 32) ? (int)p[0] : (int)p[1];
+  }
+}
+template <int S>
+__device__ __forceinline__ float xor_lane(float x) {
+  return __int_as_float(xor_lane<S>(__float_as_int(x)));
+}
+template <int S>
+__device__ __forceinline__ double xor_lane(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = xor_lane<S>((int)(b & 0xffffffffll));
+  const int hi = xor_lane<S>((int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
 
 // Value of lane l (l uniform across the wave); reads the lane even when it
 // is inactive.
@@ -82,45 +120,62 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = kWave / 2; m > 0; m >>= 1) x += shfl_xor_f(x, m);
+// Butterfly sum over the wave (every lane gets the total, in one fixed order).
+template <typename T>
+__device__ __forceinline__ T wave_sum(T x) {
+  x += xor_lane<32>(x);
+  x += xor_lane<16>(x);
+  x += xor_lane<8>(x);
+  x += xor_lane<4>(x);
+  x += xor_lane<2>(x);
+  x += xor_lane<1>(x);
   return x;
 }
+__device__ __forceinline__ double wave_sum_d(double x) { return wave_sum<double>(x); }
 
-__device__ __forceinline__ double wave_sum_d(double x) {
-#pragma unroll
-  for (int m = kWave / 2; m > 0; m >>= 1) x += __shfl_xor(x, m, kWave);
-  return x;
+template <int S>
+__device__ __forceinline__ void best_step(float& v, int& i) {
+  const float ov = xor_lane<S>(v);
+  const int oi = xor_lane<S>(i);
+  if (precedes(ov, oi, v, i)) { v = ov; i = oi; }
 }
 
 // Wave-wide best (value, index) under `precedes`; every lane gets it.
 __device__ __forceinline__ void wave_best(float& v, int& i) {
-#pragma unroll
-  for (int m = kWave / 2; m > 0; m >>= 1) {
-    float ov = shfl_xor_f(v, m);
-    int oi = shfl_xor_i(i, m);
-    if (precedes(ov, oi, v, i)) { v = ov; i = oi; }
-  }
+  best_step<32>(v, i);
+  best_step<16>(v, i);
+  best_step<8>(v, i);
+  best_step<4>(v, i);
+  best_step<2>(v, i);
+  best_step<1>(v, i);
+}
+
+// One compare-exchange of a bitonic network with partner lane ^ S.
+template <int S>
+__device__ __forceinline__ void cas_step(float& v, int& i, bool ascending) {
+  const float ov = xor_lane<S>(v);
+  const int oi = xor_lane<S>(i);
+  const bool lower = (lane_id() & S) == 0;
+  const bool want_better = (lower == ascending);
+  const bool self_better = precedes(v, i, ov, oi);
+  if (want_better != self_better && (v != ov || i != oi)) { v = ov; i = oi; }
+}
+
+template <int SIZE, int S>
+__device__ __forceinline__ void bitonic_merge_steps(float& v, int& i) {
+  const bool ascending = SIZE == kWave || (lane_id() & SIZE) == 0;
+  cas_step<S>(v, i, ascending);
+  if constexpr (S > 1) bitonic_merge_steps<SIZE, S / 2>(v, i);
+}
+
+template <int SIZE>
+__device__ __forceinline__ void bitonic_stages(float& v, int& i) {
+  if constexpr (SIZE > 2) bitonic_stages<SIZE / 2>(v, i);
+  bitonic_merge_steps<SIZE, SIZE / 2>(v, i);
 }
 
 // Bitonic sort of one (value, index) per lane across the wave, best first.
-__device__ __forceinline__ void wave_bitonic_sort(float& v, int& i) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      float ov = shfl_xor_f(v, stride);
-      int oi = shfl_xor_i(i, stride);
-      const bool ascending = (lane & size) == 0 || size == kWave;
-      const bool lower = (lane & stride) == 0;
-      const bool want_better = (lower == ascending);
-      const bool self_better = precedes(v, i, ov, oi);
-      if (want_better != self_better && (v != ov || i != oi)) { v = ov; i = oi; }
-    }
-  }
-}
+__device__ __forceinline__ void wave_bitonic_sort(float& v, int& i) { bitonic_stages<kWave>(v, i); }
 
 // k rounds of wave-wide argmin over J candidates per lane; lane r < k ends
 // up holding the r-th best (value, index).  Removed or empty entries are

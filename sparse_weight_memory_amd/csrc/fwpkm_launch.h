@@ -1,6 +1,7 @@
 // Host-side launchers of the FwPKM kernels (one per kernel family).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
@@ -8,19 +9,37 @@
 
 namespace fwpkm {
 
-// KA: score GEMM + per-half top-k per 256-key block.
-size_t ka_smem_bytes(int half);
-hipError_t launch_ka(const ChunkArgs& a, hipStream_t s);
+// Optional start/stop events stamped by the kernel dispatch itself
+// (hipExtLaunchKernelGGL), so the measured time is the kernel's own.
+struct LaunchTiming {
+  hipEvent_t beg = nullptr;
+  hipEvent_t end = nullptr;
+};
+
+template <typename K, typename... Args>
+inline hipError_t fw_launch(K kernel, dim3 grid, dim3 block, uint32_t smem, hipStream_t s,
+                            const LaunchTiming* tm, Args... args) {
+  if (tm)
+    hipExtLaunchKernelGGL(kernel, grid, block, smem, s, tm->beg, tm->end, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, smem, s, args...);
+  return hipGetLastError();
+}
+
+// KA: score GEMM + per-half top-k per key block.  score_key_block() picks the
+// block (64, 128 or 256 keys) for a chunk shape.
+int score_key_block(int units, int tokens, int n);
+hipError_t launch_ka(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 
 // KB: Cartesian top-k, softmax weights, value gather-reduce and, when
 // `write`, the fast-weight backward that emits the (row, pair) lists.
-hipError_t launch_kb(const ChunkArgs& a, bool write, hipStream_t s);
+hipError_t launch_kb(const ChunkArgs& a, bool write, hipStream_t s, const LaunchTiming* tm);
 
-// KC: per (unit, list) stable radix sort of the pair lists + segments.
+// KC: per (unit, list) stable radix sort of the pair lists, segments by length.
 size_t kc_smem_bytes(int P);
-hipError_t launch_kc(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_kc(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 
 // KD: per segment mean gradient and in-place SGD on V, K1 and K2 rows.
-hipError_t launch_kd(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_kd(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 
 }  // namespace fwpkm

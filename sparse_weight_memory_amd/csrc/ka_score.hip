@@ -4,25 +4,33 @@
 // ordering key o_h[t, i] whose ascending order is best-first:
 //   IDW  o = ||K_h[i]||^2 - 2 q_h[t].K_h[i]   (= ||q_h - K_h[i]||^2 - ||q_h||^2)
 //   dot  o = -(q_h[t].K_h[i])
-// and keeps, per 256-key block, the k best (o asc, index asc).  The query's
-// own norm ||q_h||^2 is common to every candidate of a half, so it is kept
-// apart (qnorm) and added back only for the weights.
+// and keeps, per key block, the k best (o asc, index asc).  The query's own
+// norm ||q_h||^2 is common to every candidate of a half, so it is kept apart
+// (qnorm) and added back only for the weights.
 // [gist.science "Fast-weight Product Key Memory", section 2: sub-key
 // codebooks K(1), K(2) scored in O(sqrt N), IDW score -log(eps+||q-K||^2);
 // agifrontier tutorial, Product Key addressing: query split in two halves]
 //
 // The q.K contraction is a dense [keys x d_h] x [d_h x tokens] product per
-// unit and half: it runs on v_mfma_f32_16x16x4_f32 with the query tile staged
-// in LDS.  Every 32 dims the fp32 MFMA partial sums are folded into fp64
-// accumulators and the key norms are summed in fp64, so the ordering keys
-// carry far less rounding than the 1e-6 relative gap at which two candidates
-// count as tied.
+// unit and half: it runs on v_mfma_f32_16x16x4_f32.  A workgroup of 16 waves
+// owns (unit, half, key block, 16-token tile) with the tile's queries staged
+// in LDS.  The key block (64, 128 or 256 keys) is chosen per launch so that
+// small chunks still spread over the whole chip: wave w multiplies key tile
+// (w mod blk/16) over its share of the dims; dim shares are summed in LDS.
+// Key norms are summed in fp64, so the ordering keys carry far less rounding
+// than the 1e-6 relative gap at which two candidates count as tied.
 //
-// Workgroup = 4 waves = one (unit, half, 256-key block, 16-token tile); wave w
-// scores keys [w*64, w*64+64) of the block as four 16-key MFMA tiles.  Work
-// items are laid out so that the token tiles sharing one key block run on one
-// XCD (workgroup i is dispatched to XCD i % 8), which keeps the block's keys
-// in that XCD's L2.
+// Selection, one wave per token: a bitonic sort of the first 64 candidates
+// gives a threshold (the k-th best); the remaining candidates are filtered
+// against it with one ballot per 64, the few that pass are compacted into
+// LDS, and a final bitonic sort of the k best plus the survivors gives the
+// block's top-k.  Every step orders by (value, index), which is unique, so
+// the result is deterministic.
+// Work items are laid out so that the token tiles sharing one key block run
+// on one XCD (workgroup i is dispatched to XCD i % 8), which keeps the block's
+// keys in that XCD's L2.
+
+#include <algorithm>
 
 #include "fwpkm_device.h"
 #include "fwpkm_launch.h"
@@ -31,13 +39,23 @@ namespace fwpkm {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void ka_score_topk(ChunkArgs a) {
+constexpr int kScoreWaves = 16;
+constexpr int kMaxBlk = 256;       // largest key block
+constexpr int kStepGroup = 8;      // 16-dim steps whose key operands are loaded together
+
+__global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a) {
   extern __shared__ float smem[];
   const int half = a.half;
+  const int blk = a.key_block;             // 64, 128 or 256
+  const int nkt = blk / 16;                // key tiles per block
+  const int ndq = kScoreWaves / nkt;       // dim shares per key tile
   const int qpitch = half + 4;
-  float* qs = smem;                             // [16][qpitch]
-  float* sc = smem + kTokTile * qpitch;         // [16][kKeyBlock + 4]
-  constexpr int spitch = kKeyBlock + 4;
+  float* qs = smem;                                      // [16][qpitch]
+  float* part = qs + kTokTile * qpitch;                  // [ndq][16][blk + 1]
+  double* knp = reinterpret_cast<double*>(part + ndq * kTokTile * (blk + 1));  // [ndq][blk]
+  float* sc = part;                                      // [16][blk + 1], reuses part[0]
+  float* surv_v = reinterpret_cast<float*>(knp + ndq * blk);  // [16][blk] filter survivors
+  int* surv_i = reinterpret_cast<int*>(surv_v + kTokTile * blk);
 
   const int ntt = (a.T + kTokTile - 1) / kTokTile;
   const int total = a.U * 2 * a.nblk * ntt;
@@ -52,14 +70,13 @@ __global__ __launch_bounds__(256) void ka_score_topk(ChunkArgs a) {
   const int u = rest / 2;
   const int b = u / a.H, hh = u % a.H;
   const int t0 = tt * kTokTile;
-
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = lane_id();
 
   // ---- stage the 16-token query tile (this half) in LDS
   const int half4 = half >> 2;
-  for (int e = tid; e < kTokTile * half4; e += 256) {
+  for (int e = tid; e < kTokTile * half4; e += kScoreWaves * kWave) {
     const int r = e / half4, c4 = e - r * half4;
     const int t = t0 + r;
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -71,137 +88,183 @@ __global__ __launch_bounds__(256) void ka_score_topk(ChunkArgs a) {
   }
   __syncthreads();
 
-  // ---- query norms (fp64 sums), once per token and half
-  if (kb == 0) {
-    for (int r = wave * 4; r < wave * 4 + 4; ++r) {
-      const int t = t0 + r;
-      double s = 0.0;
-      for (int d = lane; d < half; d += kWave) {
-        const double x = qs[r * qpitch + d];
-        s += x * x;
-      }
-      s = wave_sum_d(s);
-      if (lane == 0 && t < a.T) a.qnorm[((int64_t)u * a.T + t) * 2 + h] = (float)s;
+  // ---- query norms (fp64 sums), once per token and half; wave w <-> token w
+  if (kb == 0 && t0 + wave < a.T) {
+    double s = 0.0;
+    for (int d = lane; d < half; d += kWave) {
+      const double x = qs[wave * qpitch + d];
+      s += x * x;
     }
+    s = wave_sum_d(s);
+    if (lane == 0) a.qnorm[((int64_t)u * a.T + t0 + wave) * 2 + h] = (float)s;
   }
 
-  // ---- scores of 16 tokens x 64 keys per wave on the matrix cores
-  const float* K = (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k + (int64_t)hh * a.n * half;
-  const int key_base = kb * kKeyBlock + wave * 64;
-  const int row = lane & 15;     // A row (key within tile) / B column (token)
-  const int quad = lane >> 4;    // which 4-dim group of each 16-dim step
-  const bool any_key = key_base < a.n;
-
-  v4f acc[4];
-  double acc64[4][4];
-  double ksq[4];
+  // ---- scores: wave (kt, dq) = key tile kt over dim share dq
+  const int kt = wave % nkt;
+  const int dq = wave / nkt;
+  const int row = lane & 15;          // A row (key) / B column (token)
+  const int quad = lane >> 4;         // 4-dim group inside a 16-dim step
+  const int share = ((half + 16 * ndq - 1) / (16 * ndq)) * 16;   // dims per share
+  const int d_lo = dq * share;
+  const int steps = share / 16;
+  const int key = kb * blk + kt * 16 + row;
+  const bool kvalid = key < a.n;
+  const float* krow = (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k +
+                      ((int64_t)hh * a.n + (kvalid ? key : 0)) * half;
+  // two independent accumulator chains (x,y and z,w components of each step)
+  v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
+  double ksq = 0.0;
+  for (int s0 = 0; s0 < steps; s0 += kStepGroup) {
+    // every key operand of the group is requested before the first MFMA
+    float4 ak[kStepGroup];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    acc[kt] = v4f{0.f, 0.f, 0.f, 0.f};
-    ksq[kt] = 0.0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc64[kt][r] = 0.0;
-  }
-  if (any_key) {
-    const float* krow[4];
-    bool kvalid[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int key = key_base + kt * 16 + row;
-      kvalid[kt] = key < a.n;
-      krow[kt] = K + (int64_t)(kvalid[kt] ? key : 0) * half;
-    }
-    int steps = 0;
-    for (int d0 = 0; d0 < half; d0 += 16) {
-      const int d = d0 + quad * 4;
-      const bool dvalid = d < half;
-      float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (dvalid) bq = *reinterpret_cast<const float4*>(&qs[row * qpitch + d]);
-      float4 ak[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        ak[kt] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (dvalid && kvalid[kt]) ak[kt] = *reinterpret_cast<const float4*>(krow[kt] + d);
-        ksq[kt] += (double)ak[kt].x * ak[kt].x + (double)ak[kt].y * ak[kt].y +
-                   (double)ak[kt].z * ak[kt].z + (double)ak[kt].w * ak[kt].w;
-      }
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[kt].x, bq.x, acc[kt], 0, 0, 0);
-        acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[kt].y, bq.y, acc[kt], 0, 0, 0);
-        acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[kt].z, bq.z, acc[kt], 0, 0, 0);
-        acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[kt].w, bq.w, acc[kt], 0, 0, 0);
-      }
-      if (++steps == 2) {  // fold every 32 dims into fp64
-        steps = 0;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc64[kt][r] += (double)acc[kt][r];
-          acc[kt] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
-      }
+    for (int j = 0; j < kStepGroup; ++j) {
+      const int d = d_lo + (s0 + j) * 16 + quad * 4;
+      const bool ok = s0 + j < steps && d < half;
+      ak[j] = (ok && kvalid) ? *reinterpret_cast<const float4*>(krow + d) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc64[kt][r] += (double)acc[kt][r];
+    for (int j = 0; j < kStepGroup; ++j) {
+      const int d = d_lo + (s0 + j) * 16 + quad * 4;
+      const bool ok = s0 + j < steps && d < half;
+      const float4 bq = ok ? *reinterpret_cast<const float4*>(&qs[row * qpitch + d])
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      ksq += (double)ak[j].x * ak[j].x + (double)ak[j].y * ak[j].y +
+             (double)ak[j].z * ak[j].z + (double)ak[j].w * ak[j].w;
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[j].x, bq.x, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[j].z, bq.z, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[j].y, bq.y, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[j].w, bq.w, acc1, 0, 0, 0);
     }
   }
-
-  // ---- epilogue: ordering keys into LDS.  Lane holds keys 4*quad + r of each
-  // tile for token `row`; the key norm of tile-key j sits in lanes j, j+16, ...
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    double kn = ksq[kt];
-    kn += __shfl_xor(kn, 16, kWave);
-    kn += __shfl_xor(kn, 32, kWave);
+  ksq += xor_lane<16>(ksq);
+  ksq += xor_lane<32>(ksq);
+  // acc[r] = dim-share sum of K[key 4*quad + r of the tile] . Q[token row]
+  const int ppitch = blk + 1;
+  if (ndq == 1) {
+    // one wave holds every dim: ordering keys go straight to LDS
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int j = quad * 4 + r;                 // key within the tile
-      const double knj = __shfl(kn, j, kWave);
-      const int key = key_base + kt * 16 + j;
-      const int t = t0 + row;
-      float o;
-      if (key < a.n && t < a.T) {
-        const double dot = acc64[kt][r];
-        o = (a.mode == 0) ? (float)(knj - 2.0 * dot) : (float)(-dot);
-        o = order_key(o);
-      } else {
-        o = __builtin_inff();
+      const int j = quad * 4 + r;
+      const double kn = __shfl(ksq, j, kWave);      // norm of tile key j sits in lane j
+      const int gkey = kb * blk + kt * 16 + j;
+      float o = __builtin_inff();
+      if (gkey < a.n && t0 + row < a.T) {
+        const double dot = (double)acc0[r] + (double)acc1[r];
+        o = order_key(a.mode == 0 ? (float)(kn - 2.0 * dot) : (float)(-dot));
       }
-      sc[row * spitch + wave * 64 + kt * 16 + j] = o;
+      sc[row * ppitch + kt * 16 + j] = o;
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      part[(dq * kTokTile + row) * ppitch + kt * 16 + quad * 4 + r] = acc0[r] + acc1[r];
+    if (lane < 16) knp[dq * blk + kt * 16 + lane] = ksq;
+    __syncthreads();
+
+    // combine dim shares -> ordering keys (thread <-> (token, key))
+    float oval[kMaxBlk * kTokTile / (kScoreWaves * kWave)];
+    const int nent = kTokTile * blk;
+#pragma unroll
+    for (int i = 0; i < kMaxBlk * kTokTile / (kScoreWaves * kWave); ++i) {
+      const int e = tid + i * kScoreWaves * kWave;
+      float o = __builtin_inff();
+      if (e < nent) {
+        const int tok = e / blk, kk = e - tok * blk;
+        const int gkey = kb * blk + kk;
+        if (gkey < a.n && t0 + tok < a.T) {
+          double dot = 0.0, kn = 0.0;
+          for (int s = 0; s < ndq; ++s) {
+            dot += (double)part[(s * kTokTile + tok) * ppitch + kk];
+            kn += knp[s * blk + kk];
+          }
+          o = order_key(a.mode == 0 ? (float)(kn - 2.0 * dot) : (float)(-dot));
+        }
+      }
+      oval[i] = o;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kMaxBlk * kTokTile / (kScoreWaves * kWave); ++i) {
+      const int e = tid + i * kScoreWaves * kWave;
+      if (e < nent) {
+        const int tok = e / blk, kk = e - tok * blk;
+        sc[tok * ppitch + kk] = oval[i];
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- per token (wave w <-> token w): the k best of the block
+  const int tw = t0 + wave;
+  if (tw >= a.T) return;
+  const int k = a.k;
+  const float* srow = sc + wave * ppitch;
+  auto cand = [&](int c, float& v, int& i) {
+    const int gkey = kb * blk + c;
+    i = gkey < a.n ? gkey : kNoIndex;
+    v = i == kNoIndex ? __builtin_inff() : srow[c];
+  };
+  float v;
+  int ix;
+  cand(lane, v, ix);
+  wave_bitonic_sort(v, ix);                       // best 64 of the first 64
+  if (blk > kWave) {
+    const float th_v = readlane_f(v, k - 1);
+    const int th_i = readlane_i(ix, k - 1);
+    float* sv = surv_v + wave * blk;
+    int* si = surv_i + wave * blk;
+    int nsurv = 0;
+    for (int c0 = kWave; c0 < blk; c0 += kWave) {
+      float cv;
+      int ci;
+      cand(c0 + lane, cv, ci);
+      const bool pass = precedes(cv, ci, th_v, th_i);
+      const unsigned long long m = __ballot(pass);
+      if (pass) {
+        const int pos = nsurv + __popcll(m & ((1ull << lane) - 1ull));
+        sv[pos] = cv;
+        si[pos] = ci;
+      }
+      nsurv += __popcll(m);
+    }
+    // merge the k best with the survivors, 64 - k at a time
+    const int fresh = kWave - k;
+    for (int pos = 0; pos < nsurv; pos += fresh) {
+      const float mv = __shfl(v, lane - fresh, kWave);
+      const int mi = __shfl(ix, lane - fresh, kWave);
+      if (lane < fresh) {
+        const int c = pos + lane;
+        v = c < nsurv ? sv[c] : __builtin_inff();
+        ix = c < nsurv ? si[c] : kNoIndex;
+      } else {
+        v = mv;
+        ix = mi;
+      }
+      wave_bitonic_sort(v, ix);
     }
   }
-  __syncthreads();
-
-  // ---- per token: the k best of the block's 256 keys (k rounds of argmin)
-  for (int r = wave * 4; r < wave * 4 + 4; ++r) {
-    const int t = t0 + r;
-    if (t >= a.T) break;
-    float cv[4];
-    int ci[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int local = lane + 64 * j;
-      const int key = kb * kKeyBlock + local;
-      cv[j] = sc[r * spitch + local];
-      ci[j] = key < a.n ? key : kNoIndex;
-      if (ci[j] == kNoIndex) cv[j] = __builtin_inff();
-    }
-    float mine_v;
-    int mine_i;
-    wave_select_k<4>(cv, ci, a.k, mine_v, mine_i);
-    if (lane < a.k) {
-      const int64_t base = ((((int64_t)u * a.T + t) * 2 + h) * a.nblk + kb) * a.k;
-      a.half_o[base + lane] = mine_v;
-      a.half_i[base + lane] = mine_i;
-    }
+  if (lane < k) {
+    const int64_t base = ((((int64_t)u * a.T + tw) * 2 + h) * a.nblk + kb) * k;
+    a.half_o[base + lane] = v;
+    a.half_i[base + lane] = ix;
   }
 }
 
-size_t ka_smem_bytes(int half) {
-  return sizeof(float) * (size_t)kTokTile * ((half + 4) + (kKeyBlock + 4));
+int score_key_block(int units, int tokens, int n) {
+  const int ntt = (tokens + kTokTile - 1) / kTokTile;
+  int blk = kMaxBlk;
+  while (blk > 64 && (int64_t)units * 2 * ntt * ((n + blk - 1) / blk) < 256) blk /= 2;
+  return blk;
+}
+
+size_t ka_smem_bytes(int half, int blk) {
+  const int ndq = kScoreWaves / (blk / 16);
+  return sizeof(float) * kTokTile * (half + 4)                       // queries
+         + sizeof(float) * ndq * kTokTile * (blk + 1)                // dim-share partials / scores
+         + sizeof(double) * ndq * blk                                // key-norm partials
+         + (sizeof(float) + sizeof(int)) * kTokTile * blk;           // filter survivors
 }
 
 int ka_grid(const ChunkArgs& a) {
@@ -210,14 +273,13 @@ int ka_grid(const ChunkArgs& a) {
   return 8 * ((total + 7) / 8);
 }
 
-hipError_t launch_ka(const ChunkArgs& a, hipStream_t s) {
-  const size_t smem = ka_smem_bytes(a.half);
+hipError_t launch_ka(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&ka_score_topk), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)ka_smem_bytes(FWPKM_MAX_HALF_DIM));
+      (int)std::max(ka_smem_bytes(FWPKM_MAX_HALF_DIM, 64), ka_smem_bytes(FWPKM_MAX_HALF_DIM, kMaxBlk)));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(ka_score_topk, dim3(ka_grid(a)), dim3(256), smem, s, a);
-  return hipGetLastError();
+  return fw_launch(ka_score_topk, dim3(ka_grid(a)), dim3(kScoreWaves * kWave),
+                   (uint32_t)ka_smem_bytes(a.half, a.key_block), s, tm, a);
 }
 
 }  // namespace fwpkm

@@ -48,6 +48,18 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   const int b = u / a.H, hh = u % a.H;
   const int64_t ut = (int64_t)u * a.T + t;
   const float inf = __builtin_inff();
+  const int64_t io = ((int64_t)(b * a.T + t) * a.H + hh);
+  const int dv4 = a.dv >> 2;
+
+  // loads that do not depend on the selection go out first
+  const float qn = (a.mode == 0) ? a.qnorm[ut * 2] + a.qnorm[ut * 2 + 1] : 0.f;
+  float4 yv[VR];
+#pragma unroll
+  for (int j = 0; j < VR; ++j) {
+    const int c = lane + 64 * j;
+    yv[j] = (WRITE && c < dv4) ? reinterpret_cast<const float4*>(a.y + io * a.dv)[c]
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 
   // ---- 1. per-half best-k lists (lane m < k holds the m-th best)
   float ho[2];
@@ -59,16 +71,29 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
       ho[h] = lane < k ? a.half_o[base + lane] : inf;
       hi[h] = lane < k ? a.half_i[base + lane] : kNoIndex;
     } else {
-      const int nc = a.nblk * k;   // <= 16 * 32 = 512
-      float cv[8];
-      int ci[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = lane + 64 * j;
-        cv[j] = c < nc ? a.half_o[base + c] : inf;
-        ci[j] = c < nc ? a.half_i[base + c] : kNoIndex;
+      // merge the per-block lists: the best k so far sit in lanes 64-k..63,
+      // the next 64-k candidates fill lanes 0..63-k, and a bitonic sort
+      // brings the best k of both to lanes 0..k-1
+      const int nc = a.nblk * k;
+      const int fresh = kWave - k;
+      float v = inf;
+      int ix = kNoIndex;
+      for (int pos = 0; pos < nc; pos += fresh) {
+        const float mv = __shfl(v, lane - fresh, kWave);
+        const int mi = __shfl(ix, lane - fresh, kWave);
+        const int c = pos + lane;
+        if (lane < fresh) {
+          v = c < nc ? order_key(a.half_o[base + c]) : inf;
+          ix = c < nc ? a.half_i[base + c] : kNoIndex;
+          if (ix == kNoIndex) v = inf;
+        } else {
+          v = pos == 0 ? inf : mv;
+          ix = pos == 0 ? kNoIndex : mi;
+        }
+        wave_bitonic_sort(v, ix);
       }
-      wave_select_k<8>(cv, ci, k, ho[h], hi[h]);
+      ho[h] = lane < k ? v : inf;
+      hi[h] = lane < k ? ix : kNoIndex;
     }
   }
 
@@ -116,7 +141,6 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   const bool active = lane < k && sel_s != kNoIndex;
   float w = 0.f, uinv = 0.f;
   if (a.mode == 0) {
-    const float qn = a.qnorm[ut * 2] + a.qnorm[ut * 2 + 1];
     float D = qn + sel_o;
     D = D > 0.f ? D : 0.f;
     uinv = active ? 1.0f / (a.eps + D) : 0.f;
@@ -132,7 +156,6 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
 
   // ---- 4. gather-reduce of the k value rows
   const float* Vu = a.v + (int64_t)b * a.stride_v + (int64_t)hh * N * a.dv;
-  const int dv4 = a.dv >> 2;
   float4 acc[VR];
 #pragma unroll
   for (int j = 0; j < VR; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -178,7 +201,6 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   }
 
   // ---- outputs of the read
-  const int64_t io = ((int64_t)(b * a.T + t) * a.H + hh);
   float4* ret = reinterpret_cast<float4*>(a.retrieved + io * a.dv);
 #pragma unroll
   for (int j = 0; j < VR; ++j) {
@@ -192,7 +214,6 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   if (!WRITE) return;
 
   // ---- 5. backward
-  const float4* yr = reinterpret_cast<const float4*>(a.y + io * a.dv);
   float4* gw = reinterpret_cast<float4*>(a.g + ut * a.dv);
   float4 g[VR];
   float gout = 0.f;
@@ -201,7 +222,7 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
     const int c = lane + 64 * j;
     g[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < dv4) {
-      const float4 yy = yr[c];
+      const float4 yy = yv[j];
       g[j] = make_float4(acc[j].x - yy.x, acc[j].y - yy.y, acc[j].z - yy.z, acc[j].w - yy.w);
       gw[c] = g[j];
       gout += g[j].x * acc[j].x + g[j].y * acc[j].y + g[j].z * acc[j].z + g[j].w * acc[j].w;
@@ -271,31 +292,28 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
 namespace {
 
 template <int KMAX, int VR>
-hipError_t launch_kb_t(const ChunkArgs& a, bool write, hipStream_t s) {
+hipError_t launch_kb_t(const ChunkArgs& a, bool write, hipStream_t s, const LaunchTiming* tm) {
   dim3 grid((a.T + 3) / 4, a.U);
-  if (write)
-    hipLaunchKernelGGL((kb_read<KMAX, VR, true>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((kb_read<KMAX, VR, false>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  if (write) return fw_launch(kb_read<KMAX, VR, true>, grid, dim3(256), 0, s, tm, a);
+  return fw_launch(kb_read<KMAX, VR, false>, grid, dim3(256), 0, s, tm, a);
 }
 
 template <int KMAX>
-hipError_t launch_kb_k(const ChunkArgs& a, bool write, hipStream_t s) {
+hipError_t launch_kb_k(const ChunkArgs& a, bool write, hipStream_t s, const LaunchTiming* tm) {
   const int vr = ((a.dv >> 2) + 63) / 64;
-  if (vr <= 1) return launch_kb_t<KMAX, 1>(a, write, s);
-  if (vr <= 2) return launch_kb_t<KMAX, 2>(a, write, s);
-  if (vr <= 4) return launch_kb_t<KMAX, 4>(a, write, s);
-  return launch_kb_t<KMAX, 8>(a, write, s);
+  if (vr <= 1) return launch_kb_t<KMAX, 1>(a, write, s, tm);
+  if (vr <= 2) return launch_kb_t<KMAX, 2>(a, write, s, tm);
+  if (vr <= 4) return launch_kb_t<KMAX, 4>(a, write, s, tm);
+  return launch_kb_t<KMAX, 8>(a, write, s, tm);
 }
 
 }  // namespace
 
-hipError_t launch_kb(const ChunkArgs& a, bool write, hipStream_t s) {
-  if (a.k <= 4) return launch_kb_k<4>(a, write, s);
-  if (a.k <= 8) return launch_kb_k<8>(a, write, s);
-  if (a.k <= 16) return launch_kb_k<16>(a, write, s);
-  return launch_kb_k<32>(a, write, s);
+hipError_t launch_kb(const ChunkArgs& a, bool write, hipStream_t s, const LaunchTiming* tm) {
+  if (a.k <= 4) return launch_kb_k<4>(a, write, s, tm);
+  if (a.k <= 8) return launch_kb_k<8>(a, write, s, tm);
+  if (a.k <= 16) return launch_kb_k<16>(a, write, s, tm);
+  return launch_kb_k<32>(a, write, s, tm);
 }
 
 }  // namespace fwpkm

@@ -114,6 +114,20 @@ def test_edge_shapes(case):
         st, _, _ = compare_chunk(mem, st, q, y, lr, label=f"{label} step{c}")
 
 
+@pytest.mark.parametrize("mode", ["idw", "dot"])
+def test_long_segments_split_into_pieces(mode):
+    """Every token asks the same few queries, so each touched row is hit by
+    dozens of tokens: its gradient is summed over several pieces."""
+    need_gpu()
+    B, H, C, n, half, dv, k = 2, 1, 200, 24, 8, 20, 6
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=C, num_heads=H,
+               max_batch=B, score_mode=mode)
+    st, q, y = _random_case(77, B, H, C, n, half, dv)
+    q[:] = q[:, [t % 3 for t in range(C)]]             # three distinct queries per sequence
+    for c, lr in enumerate((1.0, 0.3)):
+        st, _, _ = compare_chunk(mem, st, q, y, lr, label=f"long-segments {mode} step{c}")
+
+
 def test_closed_form_k1_single_token_writes_target():
     need_gpu()
     n, half, dv = 16, 8, 32
