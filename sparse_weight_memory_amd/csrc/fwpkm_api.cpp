@@ -33,8 +33,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Byte sizes of the workspace regions for `units` units of `tokens` tokens.
 struct WsLayout {
-  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, sorted, seg, nseg;
-  size_t long_seg, short_seg, seg_kinds, total;
+  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, pay, long_rec, short_rec, kinds, total;
 };
 
 WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
@@ -50,12 +49,11 @@ WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
   L.g = take(sizeof(float) * units * tokens * c.dim_v);
   L.keys = take(sizeof(int) * 3 * units * P);
   L.coef = take(sizeof(float) * 2 * units * P);
-  L.sorted = take(sizeof(int) * 3 * units * P);
-  L.seg = take(sizeof(int) * 3 * units * (P + 1));
-  L.nseg = take(sizeof(int) * 3 * units);
-  L.long_seg = take(sizeof(int) * 3 * units * P);
-  L.short_seg = take(sizeof(int) * 3 * units * P);
-  L.seg_kinds = take(sizeof(int) * 3 * units * 2);
+  L.pay = take(sizeof(int2) * 3 * units * P);
+  L.long_rec = take(sizeof(int4) * 3 * units * P);
+  L.short_rec = take(sizeof(int4) * 3 * units * P);
+  // regions per list shrink as units grow: 3 * units * regions <= max(256, 3 * units)
+  L.kinds = take(sizeof(int4) * std::max<int64_t>(256, 3 * units));
   L.total = off;
   return L;
 }
@@ -356,12 +354,13 @@ int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targ
   a.g = reinterpret_cast<float*>(ws + L.g);
   a.keys = reinterpret_cast<int*>(ws + L.keys);
   a.coef = reinterpret_cast<float*>(ws + L.coef);
-  a.sorted = reinterpret_cast<int*>(ws + L.sorted);
-  a.seg_start = reinterpret_cast<int*>(ws + L.seg);
-  a.nseg = reinterpret_cast<int*>(ws + L.nseg);
-  a.long_seg = reinterpret_cast<int*>(ws + L.long_seg);
-  a.short_seg = reinterpret_cast<int*>(ws + L.short_seg);
-  a.seg_kinds = reinterpret_cast<int*>(ws + L.seg_kinds);
+  a.pay = reinterpret_cast<int2*>(ws + L.pay);
+  a.long_rec = reinterpret_cast<int4*>(ws + L.long_rec);
+  a.short_rec = reinterpret_cast<int4*>(ws + L.short_rec);
+  a.kinds = reinterpret_cast<int4*>(ws + L.kinds);
+  a.regions = fwpkm::group_regions((int)U);
+  a.region_bits = 0;
+  while ((1 << a.region_bits) < a.regions) ++a.region_bits;
   a.pw = std::max(c.dim_v, half);
 
   const bool write = lr != 0.0f;

@@ -10,10 +10,9 @@ namespace fwpkm {
 constexpr int kWave = 64;
 constexpr int kKeyBlock = 64;       // smallest key block of the score kernel
 constexpr int kTokTile = 16;        // tokens per score workgroup (MFMA N)
-constexpr int kSortThreads = 1024;  // threads of one sort workgroup
+constexpr int kGroupWaves = 8;      // waves of one grouping workgroup
 constexpr int kSortMaxPairs = 8192; // C*k limit of the in-LDS sort
 constexpr int kShortSeg = 16;       // longest segment one update wave sums alone
-constexpr int kUpdWaves = 4;        // waves per update workgroup
 constexpr int kUpdMaxLists = 3072;  // 3 * units the update kernel can index
 #define FWPKM_MAX_HALF_DIM 1024     // largest d_h the score kernel stages
 
@@ -58,12 +57,14 @@ struct ChunkArgs {
   float* g;        // [U, T, dv] retrieved - target
   int* keys;       // [3, U, P] V slot | K1 row (n = none) | K2 row (n = none)
   float* coef;     // [2, U, P] merged key coefficient of a K1 / K2 pair
-  int* sorted;     // [3, U, P] pair indices ordered by key (stable)
-  int* seg_start;  // [3, U, P + 1] first sorted position of each segment
-  int* nseg;       // [3, U] segments per list
-  int* long_seg;   // [3, U, P] segments of more than kShortSeg pairs
-  int* short_seg;  // [3, U, P] the other segments
-  int* seg_kinds;  // [3 * U, 2] (long count, short count)
+  // grouping output, per (list, unit) in [3, U, P] arrays; region r of a list
+  // owns entries [offset_r, offset_r + its pairs)
+  int2* pay;       // sorted (token, coefficient bits) of each list's pairs
+  int4* long_rec;  // (row, first pair, pairs, 0) of segments > kShortSeg pairs
+  int4* short_rec; // the same for the other segments
+  int4* kinds;     // [3, U, regions] (long segments, short segments, offset_r, 0)
+  int regions;     // hash regions per (list, unit), a power of two
+  int region_bits; // log2(regions)
   int pw;          // floats per row = max(d_v, d_h)
 };
 

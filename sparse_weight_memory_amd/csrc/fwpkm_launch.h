@@ -35,7 +35,9 @@ hipError_t launch_ka(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 // `write`, the fast-weight backward that emits the (row, pair) lists.
 hipError_t launch_kb(const ChunkArgs& a, bool write, hipStream_t s, const LaunchTiming* tm);
 
-// KC: per (unit, list) stable radix sort of the pair lists, segments by length.
+// KC: per (region, list, unit) stable radix sort of the pair lists, segment
+// records by length.  group_regions() picks the hash regions per list.
+int group_regions(int units);
 size_t kc_smem_bytes(int P);
 hipError_t launch_kc(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 

@@ -1,16 +1,22 @@
 // KC: deterministic grouping of the chunk's (row, pair) lists.
 //
-// One workgroup per (list, unit) -- lists are V slots, K1 rows and K2 rows --
-// first drops the entries the read kernel marked as merged away (K rows a
-// token already listed, key = n; V key n*n = no slot), keeping the order,
-// then sorts the remaining (row, pair index) entries by row with a stable LSD
-// radix sort held entirely in LDS (8-bit digits; as many passes as the
-// largest row present needs).  Stability keeps every row's pairs in ascending
-// (token, rank) order, so each row's gradients are summed in one fixed order
-// and no float atomics are used.
+// Lists are V slots, K1 rows and K2 rows, one of each per unit.  The rows of
+// a list are split into `regions` hash classes and one workgroup handles one
+// (region, list, unit): it scans the whole list once, keeps its own entries
+// in their original order (dropping those the read kernel marked as merged
+// away: K rows a token already listed, key n; V key n*n = no slot) and counts
+// the entries of lower regions, which fixes where its output goes.  Then it
+// sorts its entries by row with a stable LSD radix sort held entirely in LDS
+// (8-bit digits; as many passes as its largest row needs).  Stability keeps
+// every row's pairs in ascending (token, rank) order, so each row's gradient
+// is summed in one fixed order and no float atomics are used.
 // [gist.science "Fast-weight Product Key Memory", section 2, Key Technical
 // Choices: gradients of slots accessed several times in a chunk are
 // aggregated (averaged)]
+//
+// Splitting a list over several workgroups spreads the sort over many
+// compute units; a row lands in exactly one region, so segments never cross
+// regions and the result does not depend on the region count.
 //
 // Ranking inside a wave uses ballots: the lanes holding the same digit are
 // found with one ballot per digit bit, a lane's rank among them is the
@@ -20,10 +26,12 @@
 // row shifts; rows and pair indices move together, so no pass looks a key up
 // indirectly.
 //
-// Outputs per (list, unit): the sorted pair indices, the segments (runs of
-// one row), and the segments split by length: short ones (at most kShortSeg
-// pairs) get one wave of the update kernel each, long ones -- a row touched
-// by dozens or hundreds of tokens -- a whole workgroup.
+// Outputs per region, at its offset in the (list, unit) arrays:
+//   pay        (token, coefficient) of every kept pair in sorted order -- the
+//              update kernel reads a segment's pairs with one load;
+//   long_rec   (row, first pair, pairs) of segments longer than kShortSeg;
+//   short_rec  the same for the other segments;
+//   kinds      (long count, short count, offset).
 
 #include "fwpkm_device.h"
 #include "fwpkm_launch.h"
@@ -34,7 +42,14 @@ namespace {
 
 constexpr int kBits = 8;
 constexpr int kDigits = 1 << kBits;
-constexpr int kSortWaves = kSortThreads / kWave;
+constexpr int kGroupThreads = kGroupWaves * kWave;
+constexpr int kScanTiles = kSortMaxPairs / (kWave * kGroupWaves);   // key tiles per wave, at most
+
+// Region of a row: multiplicative (Fibonacci) hashing, so rows that many
+// tokens share spread over the regions.
+__device__ __forceinline__ int region_of(int key, int bits) {
+  return bits == 0 ? 0 : (int)(((unsigned)key * 0x9E3779B1u) >> (32 - bits));
+}
 
 // Inclusive scan across the wave: DPP row shifts, then row totals by readlane.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
@@ -55,7 +70,7 @@ __device__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
   __syncthreads();
   int base = 0, sum = 0;
 #pragma unroll
-  for (int w = 0; w < kSortWaves; ++w) {
+  for (int w = 0; w < kGroupWaves; ++w) {
     const int t = wave_tot[w];
     base += w < wave ? t : 0;
     sum += t;
@@ -77,7 +92,7 @@ __device__ int block_max(int x, int* wave_tot) {
   __syncthreads();
   int m = wave_tot[0];
 #pragma unroll
-  for (int w = 1; w < kSortWaves; ++w) m = m > wave_tot[w] ? m : wave_tot[w];
+  for (int w = 1; w < kGroupWaves; ++w) m = m > wave_tot[w] ? m : wave_tot[w];
   __syncthreads();
   return m;
 }
@@ -93,113 +108,137 @@ __device__ __forceinline__ unsigned long long digit_peers(int d, bool valid) {
   return peers;
 }
 
+__device__ __forceinline__ unsigned long long lanes_below() {
+  return (1ull << lane_id()) - 1ull;
+}
+
 }  // namespace
 
-__global__ __launch_bounds__(kSortThreads) void kc_sort(ChunkArgs a) {
+__global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   extern __shared__ int lds[];
-  const int list = blockIdx.x;   // 0 = V slots, 1 = K1 rows, 2 = K2 rows
-  const int u = blockIdx.y;
+  const int region = blockIdx.x;
+  const int list = blockIdx.y;   // 0 = V slots, 1 = K1 rows, 2 = K2 rows
+  const int u = blockIdx.z;
   const int P = a.P;
   int* key0 = lds;                        // [P] rows (ping)
   int* idx0 = key0 + P;                   // [P] pair indices (ping)
   int* key1 = idx0 + P;                   // [P] (pong)
   int* idx1 = key1 + P;                   // [P] (pong)
-  int* cnt = idx1 + P;                    // [kSortWaves][kDigits]
-  int* wave_tot = cnt + kSortWaves * kDigits;   // [kSortWaves]
+  int* cnt = idx1 + P;                    // [kGroupWaves][kDigits]
+  int* red = cnt + kGroupWaves * kDigits; // [2][kGroupWaves]
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
-  const int lu = list * a.U + u;
-  const int64_t UP = (int64_t)a.U * P;
-  const int* keys = a.keys + list * UP + (int64_t)u * P;
+  const int64_t lbase = ((int64_t)list * a.U + u) * P;   // this (list, unit) in [3, U, P]
+  const int* keys = a.keys + lbase;
   const int invalid_key = (list == 0) ? a.n * a.n : a.n;
 
-  // ---- load by 64-entry tiles (wave w owns tiles [w*tpw, (w+1)*tpw)), drop
-  // marked entries keeping the order, find the largest row
+  // ---- scan the list: wave w owns key tiles [w*tpw, (w+1)*tpw); all loads
+  // are issued before any is used
   const int tiles = (P + kWave - 1) / kWave;
-  const int tpw = (tiles + kSortWaves - 1) / kSortWaves;
-  int kept = 0, kmax = 0;
-  for (int tile = wave * tpw; tile < min(tiles, (wave + 1) * tpw); ++tile) {
-    const int i = tile * kWave + lane;
-    const int key = i < P ? keys[i] : invalid_key;
-    const bool ok = key != invalid_key;
-    kept += __popcll(__ballot(ok));
-    kmax = ok && key > kmax ? key : kmax;
-  }
-  if (lane == 0) wave_tot[wave] = kept;
-  __syncthreads();
-  int base = 0, Pv = 0;
+  const int tpw = (tiles + kGroupWaves - 1) / kGroupWaves;   // <= kScanTiles
+  int kreg[kScanTiles];
 #pragma unroll
-  for (int w = 0; w < kSortWaves; ++w) {
-    const int t = wave_tot[w];
-    base += w < wave ? t : 0;
-    Pv += t;
+  for (int j = 0; j < kScanTiles; ++j) {
+    const int i = (wave * tpw + j) * kWave + lane;
+    kreg[j] = (j < tpw && i < P) ? keys[i] : invalid_key;
+  }
+  int kept = 0, below = 0, kmax = 0;
+#pragma unroll
+  for (int j = 0; j < kScanTiles; ++j) {
+    if (j >= tpw) break;
+    const int key = kreg[j];
+    const bool ok = key != invalid_key;
+    const int rg = region_of(key, a.region_bits);
+    const bool mine = ok && rg == region;
+    below += __popcll(__ballot(ok && rg < region));
+    kept += __popcll(__ballot(mine));
+    kmax = mine && key > kmax ? key : kmax;
+  }
+  if (lane == 0) {
+    red[wave] = kept;
+    red[kGroupWaves + wave] = below;
   }
   __syncthreads();
-  for (int tile = wave * tpw; tile < min(tiles, (wave + 1) * tpw); ++tile) {
-    const int i = tile * kWave + lane;
-    const int key = i < P ? keys[i] : invalid_key;
-    const bool ok = key != invalid_key;
-    const unsigned long long m = __ballot(ok);
-    if (ok) {
-      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+  int base = 0, M = 0, off = 0;
+#pragma unroll
+  for (int w = 0; w < kGroupWaves; ++w) {
+    const int t = red[w];
+    base += w < wave ? t : 0;
+    M += t;
+    off += red[kGroupWaves + w];
+  }
+  __syncthreads();
+  int4* kinds = a.kinds + ((int64_t)list * a.U + u) * a.regions + region;
+  if (M == 0) {                     // block-uniform
+    if (tid == 0) *kinds = make_int4(0, 0, off, 0);
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < kScanTiles; ++j) {
+    if (j >= tpw) break;
+    const int key = kreg[j];
+    const bool mine = key != invalid_key && region_of(key, a.region_bits) == region;
+    const unsigned long long m = __ballot(mine);
+    if (mine) {
+      const int pos = base + __popcll(m & lanes_below());
       key0[pos] = key;
-      idx0[pos] = i;
+      idx0[pos] = (wave * tpw + j) * kWave + lane;
     }
     base += __popcll(m);
   }
-  kmax = block_max(kmax, wave_tot);
+  kmax = block_max(kmax, red);
   int bits = 0;
   while (bits < 31 && (kmax >> bits) != 0) ++bits;
   const int passes = (bits + kBits - 1) / kBits;
 
-  // ---- LSD radix passes over the Pv kept entries
-  const int vtiles = (Pv + kWave - 1) / kWave;
-  const int vtpw = (vtiles + kSortWaves - 1) / kSortWaves;
+  // ---- LSD radix passes over the M kept entries
+  const int vtiles = (M + kWave - 1) / kWave;
+  const int vtpw = (vtiles + kGroupWaves - 1) / kGroupWaves;
   const int t_lo = wave * vtpw;
   const int t_hi = min(vtiles, t_lo + vtpw);
   int *ks = key0, *is = idx0, *kd = key1, *id = idx1;
   int* mycnt = cnt + wave * kDigits;
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * kBits;
-    for (int i = tid; i < kSortWaves * kDigits; i += kSortThreads) cnt[i] = 0;
+    for (int i = tid; i < kGroupWaves * kDigits; i += kGroupThreads) cnt[i] = 0;
     __syncthreads();
     for (int tile = t_lo; tile < t_hi; ++tile) {
       const int i = tile * kWave + lane;
-      const bool valid = i < Pv;
+      const bool valid = i < M;
       const int d = valid ? (((unsigned)ks[i] >> shift) & (kDigits - 1)) : 0;
       const unsigned long long peers = digit_peers(d, valid);
-      if (valid && (peers & ((1ull << lane) - 1ull)) == 0ull) mycnt[d] += __popcll(peers);
+      if (valid && (peers & lanes_below()) == 0ull) mycnt[d] += __popcll(peers);
     }
     __syncthreads();
-    {  // exclusive scan, digit-major / wave-minor: flat f = d * kSortWaves + w
-      constexpr int E = kSortWaves * kDigits / kSortThreads;
+    {  // exclusive scan, digit-major / wave-minor: flat f = d * kGroupWaves + w
+      constexpr int E = kGroupWaves * kDigits / kGroupThreads;
       int v[E];
       int local = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int f = tid * E + e;
-        v[e] = cnt[(f % kSortWaves) * kDigits + f / kSortWaves];
+        v[e] = cnt[(f % kGroupWaves) * kDigits + f / kGroupWaves];
         local += v[e];
       }
       int total;
-      int run = block_exclusive_scan(local, wave_tot, &total);
+      int run = block_exclusive_scan(local, red, &total);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int f = tid * E + e;
-        cnt[(f % kSortWaves) * kDigits + f / kSortWaves] = run;
+        cnt[(f % kGroupWaves) * kDigits + f / kGroupWaves] = run;
         run += v[e];
       }
     }
     __syncthreads();
     for (int tile = t_lo; tile < t_hi; ++tile) {
       const int i = tile * kWave + lane;
-      const bool valid = i < Pv;
+      const bool valid = i < M;
       const int key = valid ? ks[i] : 0;
       const int d = ((unsigned)key >> shift) & (kDigits - 1);
       const unsigned long long peers = digit_peers(d, valid);
-      const unsigned long long lower = peers & ((1ull << lane) - 1ull);
+      const unsigned long long lower = peers & lanes_below();
       const int b0 = valid ? mycnt[d] : 0;
       if (valid) {
         const int dst = b0 + __popcll(lower);
@@ -214,51 +253,50 @@ __global__ __launch_bounds__(kSortThreads) void kc_sort(ChunkArgs a) {
     t = is; is = id; id = t;
   }
 
+  // ---- payloads in sorted order: (token, coefficient)
+  {
+    int2* pay = a.pay + lbase + off;
+    const float* cf = list == 0 ? a.sel_w + (int64_t)u * P
+                                : a.coef + (int64_t)(list - 1) * a.U * P + (int64_t)u * P;
+    for (int i = tid; i < M; i += kGroupThreads) {
+      const int p = is[i];
+      pay[i] = make_int2(p / a.k, __float_as_int(cf[p]));
+    }
+  }
+
   // ---- segments: heads of runs of equal rows.  The pong buffers are free
   // now; segment starts go to kd[0..nseg], whose last entry may spill into
   // id[0] (kd and id are adjacent and both unused).
   int* segl = kd;
-  int* sorted = a.sorted + list * UP + (int64_t)u * P;
-  int* seg = a.seg_start + list * (UP + a.U) + (int64_t)u * (P + 1);
   int heads_w = 0;
   for (int tile = t_lo; tile < t_hi; ++tile) {
     const int i = tile * kWave + lane;
-    const bool head = i < Pv && (i == 0 || ks[i - 1] != ks[i]);
+    const bool head = i < M && (i == 0 || ks[i - 1] != ks[i]);
     heads_w += __popcll(__ballot(head));
   }
-  if (lane == 0) wave_tot[wave] = heads_w;
+  if (lane == 0) red[wave] = heads_w;
   __syncthreads();
   int hbase = 0, nseg = 0;
 #pragma unroll
-  for (int w = 0; w < kSortWaves; ++w) {
-    const int t = wave_tot[w];
+  for (int w = 0; w < kGroupWaves; ++w) {
+    const int t = red[w];
     hbase += w < wave ? t : 0;
     nseg += t;
   }
   __syncthreads();
   for (int tile = t_lo; tile < t_hi; ++tile) {
     const int i = tile * kWave + lane;
-    const bool in = i < Pv;
-    const bool head = in && (i == 0 || ks[i - 1] != ks[i]);
+    const bool head = i < M && (i == 0 || ks[i - 1] != ks[i]);
     const unsigned long long m = __ballot(head);
-    if (in) sorted[i] = is[i];
-    if (head) {
-      const int s = hbase + __popcll(m & ((1ull << lane) - 1ull));
-      segl[s] = i;
-      seg[s] = i;
-    }
+    if (head) segl[hbase + __popcll(m & lanes_below())] = i;
     hbase += __popcll(m);
   }
-  if (tid == 0) {
-    segl[nseg] = Pv;
-    seg[nseg] = Pv;
-    a.nseg[lu] = nseg;
-  }
+  if (tid == 0) segl[nseg] = M;
   __syncthreads();
 
-  // ---- short / long segment lists, each in row order
+  // ---- segment records, long and short ones apart, each in segment order
   const int stiles = (nseg + kWave - 1) / kWave;
-  const int stpw = (stiles + kSortWaves - 1) / kSortWaves;
+  const int stpw = (stiles + kGroupWaves - 1) / kGroupWaves;
   const int s_lo = wave * stpw, s_hi = min(stiles, s_lo + stpw);
   int nl = 0, ns = 0;
   for (int tile = s_lo; tile < s_hi; ++tile) {
@@ -268,37 +306,47 @@ __global__ __launch_bounds__(kSortThreads) void kc_sort(ChunkArgs a) {
     nl += __popcll(__ballot(lng));
     ns += __popcll(__ballot(in && !lng));
   }
-  if (lane == 0) { wave_tot[wave] = nl; cnt[wave] = ns; }
-  __syncthreads();
-  int lbase = 0, sbase = 0, tot_long = 0, tot_short = 0;
-#pragma unroll
-  for (int w = 0; w < kSortWaves; ++w) {
-    lbase += w < wave ? wave_tot[w] : 0;
-    sbase += w < wave ? cnt[w] : 0;
-    tot_long += wave_tot[w];
-    tot_short += cnt[w];
+  if (lane == 0) {
+    red[wave] = nl;
+    red[kGroupWaves + wave] = ns;
   }
-  int* long_seg = a.long_seg + list * UP + (int64_t)u * P;
-  int* short_seg = a.short_seg + list * UP + (int64_t)u * P;
+  __syncthreads();
+  int lb = 0, sb = 0, tot_long = 0, tot_short = 0;
+#pragma unroll
+  for (int w = 0; w < kGroupWaves; ++w) {
+    lb += w < wave ? red[w] : 0;
+    sb += w < wave ? red[kGroupWaves + w] : 0;
+    tot_long += red[w];
+    tot_short += red[kGroupWaves + w];
+  }
+  int4* lrec = a.long_rec + lbase + off;
+  int4* srec = a.short_rec + lbase + off;
   for (int tile = s_lo; tile < s_hi; ++tile) {
     const int s = tile * kWave + lane;
     const bool in = s < nseg;
-    const bool lng = in && segl[s + 1] - segl[s] > kShortSeg;
+    const int s0 = in ? segl[s] : 0;
+    const int len = in ? segl[s + 1] - s0 : 0;
+    const bool lng = in && len > kShortSeg;
     const unsigned long long ml = __ballot(lng), msh = __ballot(in && !lng);
-    const unsigned long long below = (1ull << lane) - 1ull;
-    if (lng) long_seg[lbase + __popcll(ml & below)] = s;
-    if (in && !lng) short_seg[sbase + __popcll(msh & below)] = s;
-    lbase += __popcll(ml);
-    sbase += __popcll(msh);
+    if (in) {
+      const int4 rec = make_int4(ks[s0], off + s0, len, 0);
+      if (lng) lrec[lb + __popcll(ml & lanes_below())] = rec;
+      else srec[sb + __popcll(msh & lanes_below())] = rec;
+    }
+    lb += __popcll(ml);
+    sb += __popcll(msh);
   }
-  if (tid == 0) {
-    a.seg_kinds[2 * lu] = tot_long;
-    a.seg_kinds[2 * lu + 1] = tot_short;
-  }
+  if (tid == 0) *kinds = make_int4(tot_long, tot_short, off, 0);
+}
+
+int group_regions(int units) {
+  int r = 1;
+  while (r < 64 && 3 * units * r * 2 <= 256) r *= 2;
+  return r;
 }
 
 size_t kc_smem_bytes(int P) {
-  return sizeof(int) * ((size_t)4 * P + (size_t)kSortWaves * kDigits + kSortWaves);
+  return sizeof(int) * ((size_t)4 * P + (size_t)kGroupWaves * kDigits + 2 * kGroupWaves);
 }
 
 hipError_t launch_kc(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
@@ -307,7 +355,7 @@ hipError_t launch_kc(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) 
       reinterpret_cast<const void*>(&kc_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)kc_smem_bytes(kSortMaxPairs));
   if (attr != hipSuccess) return attr;
-  return fw_launch(kc_sort, dim3(3, a.U), dim3(kSortThreads), (uint32_t)smem, s, tm, a);
+  return fw_launch(kc_sort, dim3(a.regions, 3, a.U), dim3(kGroupThreads), (uint32_t)smem, s, tm, a);
 }
 
 }  // namespace fwpkm

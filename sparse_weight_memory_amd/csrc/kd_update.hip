@@ -16,11 +16,14 @@
 // Value matrices updated online, gradients of a slot used several times in a
 // chunk averaged; sciencestack.ai contents: no gradient clipping]
 //
-// Work distribution, over every list and unit of the chunk: a task is either
-// one long segment (more than kShortSeg pairs), which the four waves of a
-// workgroup split into contiguous quarters and combine in LDS in wave order,
-// or up to four short segments, one per wave.  Every sum runs in a fixed
-// order, so results do not depend on scheduling, and no atomics are used.
+// Work distribution, over every region of every list and unit: a task is
+// either one long segment (more than kShortSeg pairs), which the W waves of a
+// workgroup split into contiguous pieces and combine in LDS in wave order,
+// or up to W short segments, one per wave.  A segment's record (row, first
+// pair, pairs) and its pairs' (token, coefficient) payloads come straight
+// from the grouping kernel, so a wave reaches the data rows after two
+// dependent loads.  Every sum runs in a fixed order, so results do not
+// depend on scheduling, and no atomics are used.
 
 #include "fwpkm_device.h"
 #include "fwpkm_launch.h"
@@ -29,16 +32,27 @@ namespace fwpkm {
 
 namespace {
 
-// pref[i] = tasks of lists [0, i) for i in [0, L]; all threads of the block.
-__device__ void task_prefix(const int* kinds, int L, int* pref, int* wtot) {
-  constexpr int NT = kUpdWaves * kWave;
+constexpr int kRowBatch = 8;   // data rows a wave has in flight
+
+// pref[i] = tasks of regions [0, i) for i in [0, L]; nlong / nshort / offs
+// receive the regions' counts.  All threads of the block take part.
+template <int W>
+__device__ void task_prefix(const int4* kinds, int L, int* pref, int* nlong, int* nshort,
+                            int* offs, int* wtot) {
+  constexpr int NT = W * kWave;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int per = (L + NT - 1) / NT;
   const int beg = tid * per;
-  auto tasks = [&](int i) { return kinds[2 * i] + (kinds[2 * i + 1] + kUpdWaves - 1) / kUpdWaves; };
   int local = 0;
-  for (int j = 0; j < per; ++j)
-    if (beg + j < L) local += tasks(beg + j);
+  for (int j = 0; j < per; ++j) {
+    if (beg + j < L) {
+      const int4 kd = kinds[beg + j];
+      nlong[beg + j] = kd.x;
+      nshort[beg + j] = kd.y;
+      offs[beg + j] = kd.z;
+      local += kd.x + (kd.y + W - 1) / W;
+    }
+  }
   int incl = local;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
@@ -53,31 +67,28 @@ __device__ void task_prefix(const int* kinds, int L, int* pref, int* wtot) {
   for (int j = 0; j < per; ++j) {
     if (beg + j < L) {
       pref[beg + j] = run;
-      run += tasks(beg + j);
+      run += nlong[beg + j] + (nshort[beg + j] + W - 1) / W;
     }
   }
   if (tid == NT - 1) pref[L] = run;
   __syncthreads();
 }
 
-// One wave's sum over sorted pairs [r0, r1) of a V list:  sum_p w_p g_{t_p}.
+// One wave's sum over the pairs pay[0, n) of a V segment:  sum_p w_p g_{t_p}.
 template <int R>
-__device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const int* sorted,
-                                                int r0, int r1, float4 (&acc)[R]) {
+__device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const int2* pay,
+                                                int n, float4 (&acc)[R]) {
   const int lane = lane_id();
   const int width4 = a.dv >> 2;
-  const float* sw = a.sel_w + (int64_t)u * a.P;
   const float* gbase = a.g + (int64_t)u * a.T * a.dv;
-  for (int base = r0; base < r1; base += kWave) {
-    const int nb = min(kWave, r1 - base);
-    const int pl = lane < nb ? sorted[base + lane] : 0;
-    const int tl = pl / a.k;
-    const float wl = lane < nb ? sw[pl] : 0.f;
-    for (int i = 0; i < nb; i += 8) {
-      float4 gv[8][R];
+  for (int base = 0; base < n; base += kWave) {
+    const int nb = min(kWave, n - base);
+    const int2 pl = lane < nb ? pay[base + lane] : make_int2(0, 0);
+    for (int i = 0; i < nb; i += kRowBatch) {
+      float4 gv[kRowBatch][R];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int t = readlane_i(tl, min(i + jj, nb - 1));
+      for (int jj = 0; jj < kRowBatch; ++jj) {
+        const int t = readlane_i(pl.x, min(i + jj, nb - 1));
         const float4* gr = reinterpret_cast<const float4*>(gbase + (int64_t)t * a.dv);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -86,9 +97,9 @@ __device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
+      for (int jj = 0; jj < kRowBatch; ++jj) {
         if (i + jj < nb) {
-          const float w = readlane_f(wl, i + jj);
+          const float w = __int_as_float(readlane_i(pl.y, i + jj));
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             acc[r].x += w * gv[jj][r].x; acc[r].y += w * gv[jj][r].y;
@@ -100,27 +111,23 @@ __device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const
   }
 }
 
-// One wave's sum over sorted pairs [r0, r1) of a K list (half h):
+// One wave's sum over the pairs pay[0, n) of a K segment (half h):
 //   IDW sum_p c_p (q_h[t_p] - old),  dot sum_p c_p q_h[t_p].
 template <int R>
-__device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, const int* sorted,
-                                              int r0, int r1, const float4 (&old)[R],
-                                              float4 (&acc)[R]) {
+__device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, const int2* pay,
+                                              int n, const float4 (&old)[R], float4 (&acc)[R]) {
   const int lane = lane_id();
   const int width4 = a.half >> 2;
   const int b = u / a.H, hh = u - b * a.H;
-  const float* cf = a.coef + (int64_t)h * a.U * a.P + (int64_t)u * a.P;
   const bool idw = a.mode == 0;
-  for (int base = r0; base < r1; base += kWave) {
-    const int nb = min(kWave, r1 - base);
-    const int pl = lane < nb ? sorted[base + lane] : 0;
-    const int tl = pl / a.k;
-    const float cl = lane < nb ? cf[pl] : 0.f;
-    for (int i = 0; i < nb; i += 8) {
-      float4 qv[8][R];
+  for (int base = 0; base < n; base += kWave) {
+    const int nb = min(kWave, n - base);
+    const int2 pl = lane < nb ? pay[base + lane] : make_int2(0, 0);
+    for (int i = 0; i < nb; i += kRowBatch) {
+      float4 qv[kRowBatch][R];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int t = readlane_i(tl, min(i + jj, nb - 1));
+      for (int jj = 0; jj < kRowBatch; ++jj) {
+        const int t = readlane_i(pl.x, min(i + jj, nb - 1));
         const float4* qr = reinterpret_cast<const float4*>(
             a.q + ((int64_t)(b * a.T + t) * a.H + hh) * a.dqk + h * a.half);
 #pragma unroll
@@ -130,9 +137,9 @@ __device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, 
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
+      for (int jj = 0; jj < kRowBatch; ++jj) {
         if (i + jj < nb) {
-          const float cc = readlane_f(cl, i + jj);
+          const float cc = __int_as_float(readlane_i(pl.y, i + jj));
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             float4 x = qv[jj][r];
@@ -145,56 +152,64 @@ __device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, 
   }
 }
 
+// LDS of one update workgroup for L regions: partial sums, then the region
+// table.
+template <int R, int W>
+__host__ __device__ constexpr size_t kd_parts_bytes() {
+  return sizeof(float4) * (size_t)W * kWave * R;
+}
+
 }  // namespace
 
-template <int R>
-__global__ __launch_bounds__(kUpdWaves * kWave) void kd_update(ChunkArgs a) {
-  __shared__ int pref[kUpdMaxLists + 1];
-  __shared__ int wtot[kUpdWaves];
-  __shared__ float4 parts[kUpdWaves][kWave * R];
-  const int L = 3 * a.U;
-  task_prefix(a.seg_kinds, L, pref, wtot);
+template <int R, int W>
+__global__ __launch_bounds__(W * kWave) void kd_update(ChunkArgs a) {
+  extern __shared__ float4 kd_lds[];
+  float4* parts = kd_lds;                                             // [W][64 R]
+  const int L = 3 * a.U * a.regions;
+  int* pref = reinterpret_cast<int*>(kd_lds + (size_t)W * kWave * R); // [L + 1]
+  int* nlong = pref + L + 1;                                          // [L]
+  int* nshort = nlong + L;                                            // [L]
+  int* offs = nshort + L;                                             // [L]
+  int* wtot = offs + L;                                               // [W]
+  task_prefix<W>(a.kinds, L, pref, nlong, nshort, offs, wtot);
   const int total = pref[L];
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int P = a.P;
   const float lr = a.lr;
-  const int64_t UP = (int64_t)a.U * P;
 
   for (int task = blockIdx.x; task < total; task += gridDim.x) {
-    // (list, unit) holding this task
+    // region holding this task
     int lo = 0, hi = L;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (pref[mid] <= task) lo = mid; else hi = mid;
     }
-    const int lu = lo;
-    const int j = task - pref[lu];
+    const int j = task - pref[lo];
+    const int lu = lo / a.regions;          // list * U + unit
     const int list = lu / a.U;
     const int u = lu - list * a.U;
     const int b = u / a.H, hh = u - b * a.H;
-    const int64_t off = list * UP + (int64_t)u * P;                  // [3, U, P] arrays
-    const int* sorted = a.sorted + off;
-    const int* seg = a.seg_start + list * (UP + a.U) + (int64_t)u * (P + 1);
-    const int n_long = a.seg_kinds[2 * lu];
-    const bool is_long = j < n_long;
-    int s;
+    const int64_t lbase = (int64_t)lu * P;
+    const int nl = nlong[lo];
+    const bool is_long = j < nl;
+    int4 rec;
     if (is_long) {
-      s = a.long_seg[off + j];
+      rec = a.long_rec[lbase + offs[lo] + j];
     } else {
-      const int si = (j - n_long) * kUpdWaves + wave;
-      if (si >= a.seg_kinds[2 * lu + 1]) continue;                  // no wave-level barrier below
-      s = a.short_seg[off + si];
+      const int si = (j - nl) * W + wave;
+      if (si >= nshort[lo]) continue;                              // no barrier on this path
+      rec = a.short_rec[lbase + offs[lo] + si];
     }
-    const int s0 = seg[s], s1 = seg[s + 1];
-    const int cnt = s1 - s0;
-    int r0 = s0, r1 = s1;
+    const int row = rec.x, cnt = rec.z;
+    int p0 = rec.y, np = cnt;
     if (is_long) {
-      const int ql = (cnt + kUpdWaves - 1) / kUpdWaves;
-      r0 = min(s1, s0 + wave * ql);
-      r1 = min(s1, r0 + ql);
+      const int ql = (cnt + W - 1) / W;
+      const int r0 = min(cnt, wave * ql);
+      np = min(cnt, r0 + ql) - r0;
+      p0 += r0;
     }
-    const int row = a.keys[off + sorted[s0]];
+    const int2* pay = a.pay + lbase + p0;
     const bool finisher = !is_long || wave == 0;
 
     float4* trow;
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(kUpdWaves * kWave) void kd_update(ChunkArgs a) {
         const int c = lane + 64 * r;
         old[r] = (finisher && c < width4) ? trow[c] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      sum_value_pairs<R>(a, u, sorted, r0, r1, acc);
+      sum_value_pairs<R>(a, u, pay, np, acc);
     } else {
       const int h = list - 1;
       width4 = a.half >> 2;
@@ -222,21 +237,20 @@ __global__ __launch_bounds__(kUpdWaves * kWave) void kd_update(ChunkArgs a) {
         const int c = lane + 64 * r;
         old[r] = c < width4 ? trow[c] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      sum_key_pairs<R>(a, u, h, sorted, r0, r1, old, acc);
+      sum_key_pairs<R>(a, u, h, pay, np, old, acc);
     }
 
     if (is_long) {
-      // combine the four quarters in wave order
+      // combine the W pieces in wave order
 #pragma unroll
-      for (int r = 0; r < R; ++r) parts[wave][lane + 64 * r] = acc[r];
+      for (int r = 0; r < R; ++r) parts[wave * kWave * R + lane + 64 * r] = acc[r];
       __syncthreads();
       if (wave == 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          float4 x = parts[0][lane + 64 * r];
-#pragma unroll
-          for (int w = 1; w < kUpdWaves; ++w) {
-            const float4 y = parts[w][lane + 64 * r];
+          float4 x = parts[lane + 64 * r];
+          for (int w = 1; w < W; ++w) {
+            const float4 y = parts[w * kWave * R + lane + 64 * r];
             x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
           }
           acc[r] = x;
@@ -260,16 +274,31 @@ __global__ __launch_bounds__(kUpdWaves * kWave) void kd_update(ChunkArgs a) {
   }
 }
 
+namespace {
+
+template <int R, int W>
+hipError_t launch_kd_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
+  const int64_t L = (int64_t)3 * a.U * a.regions;
+  const size_t smem = kd_parts_bytes<R, W>() + sizeof(int) * (size_t)(4 * L + 1 + W);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&kd_update<R, W>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)(kd_parts_bytes<R, W>() + sizeof(int) * (size_t)(4 * kUpdMaxLists + 1 + W)));
+  if (attr != hipSuccess) return attr;
+  // tasks cannot exceed long segments + short groups of W, per region
+  const int64_t most = (int64_t)3 * a.U * a.P / (kShortSeg + 1) +
+                       (int64_t)3 * a.U * a.P / W + L;
+  const int64_t gx = most < 1024 ? most : 1024;
+  return fw_launch(kd_update<R, W>, dim3((unsigned)gx), dim3(W * kWave), (uint32_t)smem, s, tm, a);
+}
+
+}  // namespace
+
 hipError_t launch_kd(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
   const int r = (a.pw / 4 + 63) / 64;
-  int64_t most = (int64_t)3 * a.U * (a.P / kUpdWaves + 1);   // tasks cannot exceed this
-  int64_t gx = most < 2048 ? most : 2048;
-  dim3 grid((unsigned)gx);
-  dim3 block(kUpdWaves * kWave);
-  if (r <= 1) return fw_launch(kd_update<1>, grid, block, 0, s, tm, a);
-  if (r <= 2) return fw_launch(kd_update<2>, grid, block, 0, s, tm, a);
-  if (r <= 4) return fw_launch(kd_update<4>, grid, block, 0, s, tm, a);
-  return fw_launch(kd_update<8>, grid, block, 0, s, tm, a);
+  if (r <= 1) return launch_kd_as<1, 16>(a, s, tm);
+  if (r <= 2) return launch_kd_as<2, 16>(a, s, tm);
+  if (r <= 4) return launch_kd_as<4, 8>(a, s, tm);
+  return launch_kd_as<8, 4>(a, s, tm);
 }
 
 }  // namespace fwpkm
