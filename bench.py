@@ -8,7 +8,9 @@ score -> per-half top-k -> Cartesian top-k -> softmax -> gather -> backward
 -> sort -> segmented SGD update, chained through the memory state (each step
 reads the tables the previous one wrote).  For a single-chunk workload a step
 is one chunk call; for a streamed workload it is every chunk of the pass.
-Inputs and tables sit in HBM before the timed region starts.
+Inputs and tables sit in HBM before the timed region starts.  The chunk
+calls of one step are captured once into a HIP graph and the graph is
+replayed for every timed step (--eager launches each chunk from Python).
 
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed
 with HIP events recorded around each kernel on its own stream) and the CPU
@@ -41,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time spent timing the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every chunk from Python instead of replaying a HIP graph")
     ap.add_argument("--no-profile-pass", action="store_true",
                     help="skip the per-kernel event pass (for external profilers)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -180,13 +184,30 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    print(f"[bench] timing {args.steps} step(s)", file=sys.stderr, flush=True)
+    # one step = the chain of all chunks, replayed from a HIP graph so the
+    # host does not pace the kernels (the warmup above already allocated the
+    # library's workspace, which must not happen under capture)
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+    def timed_step():
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+
+    print(f"[bench] timing {args.steps} step(s) ({'eager' if graph is None else 'graph'})",
+          file=sys.stderr, flush=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
-        step()
+        timed_step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -211,7 +232,8 @@ def main():
                    "chunks_per_step": cfg.chunks, "tokens_per_step": tokens_per_step,
                    "slots": cfg.num_slots, "dim_qk": cfg.dim_qk, "dim_v": cfg.dim_v,
                    "topk": cfg.topk, "lr": cfg.lr, "eps": cfg.eps,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "launch": "eager" if graph is None else "hip graph of one step"},
     }
 
     if not args.no_profile_pass:

@@ -49,7 +49,7 @@ WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
   L.g = take(sizeof(float) * units * tokens * c.dim_v);
   L.keys = take(sizeof(int) * 3 * units * P);
   L.coef = take(sizeof(float) * 2 * units * P);
-  L.pay = take(sizeof(int2) * 3 * units * P);
+  L.pay = take(sizeof(int) * 3 * units * P);
   L.long_rec = take(sizeof(int4) * 3 * units * P);
   L.short_rec = take(sizeof(int4) * 3 * units * P);
   // regions per list shrink as units grow: 3 * units * regions <= max(256, 3 * units)
@@ -354,7 +354,7 @@ int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targ
   a.g = reinterpret_cast<float*>(ws + L.g);
   a.keys = reinterpret_cast<int*>(ws + L.keys);
   a.coef = reinterpret_cast<float*>(ws + L.coef);
-  a.pay = reinterpret_cast<int2*>(ws + L.pay);
+  a.pay = reinterpret_cast<int*>(ws + L.pay);
   a.long_rec = reinterpret_cast<int4*>(ws + L.long_rec);
   a.short_rec = reinterpret_cast<int4*>(ws + L.short_rec);
   a.kinds = reinterpret_cast<int4*>(ws + L.kinds);

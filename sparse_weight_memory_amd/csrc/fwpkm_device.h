@@ -59,7 +59,7 @@ struct ChunkArgs {
   float* coef;     // [2, U, P] merged key coefficient of a K1 / K2 pair
   // grouping output, per (list, unit) in [3, U, P] arrays; region r of a list
   // owns entries [offset_r, offset_r + its pairs)
-  int2* pay;       // sorted (token, coefficient bits) of each list's pairs
+  int* pay;        // each list's kept pair indices, sorted by row (stable)
   int4* long_rec;  // (row, first pair, pairs, 0) of segments > kShortSeg pairs
   int4* short_rec; // the same for the other segments
   int4* kinds;     // [3, U, regions] (long segments, short segments, offset_r, 0)
@@ -69,11 +69,6 @@ struct ChunkArgs {
 };
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
-
-// (a, ia) strictly precedes (b, ib): smaller value, then smaller index.
-__device__ __forceinline__ bool precedes(float a, int ia, float b, int ib) {
-  return a < b || (a == b && ia < ib);
-}
 
 // ---- cross-lane exchange with lane ^ S, without the LDS permute unit:
 // DPP quad permutes for S = 1, 2; row shifts for S = 4; a row rotation for
@@ -121,6 +116,18 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
+// Inclusive prefix sum across the wave: DPP row shifts within each row of 16
+// lanes, then the lower rows' totals by readlane.  All lanes must be active.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  const int r0 = readlane_i(x, 15), r1 = readlane_i(x, 31), r2 = readlane_i(x, 47);
+  const int row = lane_id() >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 // Butterfly sum over the wave (every lane gets the total, in one fixed order).
 template <typename T>
 __device__ __forceinline__ T wave_sum(T x) {
@@ -134,71 +141,79 @@ __device__ __forceinline__ T wave_sum(T x) {
 }
 __device__ __forceinline__ double wave_sum_d(double x) { return wave_sum<double>(x); }
 
+// ---- packed sort keys.  A (value, index) candidate packs into one 64-bit
+// integer whose unsigned order is the (value asc, index asc) order of
+// `precedes`: the value's IEEE bits, made monotone (negative values have all
+// bits flipped, the others only the sign bit), in the high word and the
+// index in the low word.  -0 is folded to +0 first, so the two zeros compare
+// equal as they do as floats; values must not be NaN (see order_key).  The
+// empty candidate (+inf, kNoIndex) orders after every real one.
+typedef unsigned long long skey;
+
+__device__ __forceinline__ skey pack_key(float v, int i) {
+  unsigned int b = __float_as_uint(v == 0.0f ? 0.0f : v);
+  b ^= (b & 0x80000000u) ? 0xFFFFFFFFu : 0x80000000u;
+  return ((skey)b << 32) | (unsigned int)i;
+}
+__device__ __forceinline__ float key_value(skey x) {
+  unsigned int b = (unsigned int)(x >> 32);
+  b ^= (b & 0x80000000u) ? 0x80000000u : 0xFFFFFFFFu;
+  return __uint_as_float(b);
+}
+__device__ __forceinline__ int key_index(skey x) { return (int)(unsigned int)x; }
+constexpr skey kEmptyKey = 0xFF800000ull << 32 | 0x7fffffffull;   // pack_key(+inf, kNoIndex)
+
 template <int S>
-__device__ __forceinline__ void best_step(float& v, int& i) {
-  const float ov = xor_lane<S>(v);
-  const int oi = xor_lane<S>(i);
-  if (precedes(ov, oi, v, i)) { v = ov; i = oi; }
+__device__ __forceinline__ skey xor_lane(skey x) {
+  const unsigned int lo = (unsigned int)xor_lane<S>((int)(unsigned int)x);
+  const unsigned int hi = (unsigned int)xor_lane<S>((int)(unsigned int)(x >> 32));
+  return ((skey)hi << 32) | lo;
+}
+__device__ __forceinline__ skey readlane_k(skey x, int l) {
+  const unsigned int lo = (unsigned int)__builtin_amdgcn_readlane((int)(unsigned int)x, l);
+  const unsigned int hi = (unsigned int)__builtin_amdgcn_readlane((int)(unsigned int)(x >> 32), l);
+  return ((skey)hi << 32) | lo;
 }
 
-// Wave-wide best (value, index) under `precedes`; every lane gets it.
-__device__ __forceinline__ void wave_best(float& v, int& i) {
-  best_step<32>(v, i);
-  best_step<16>(v, i);
-  best_step<8>(v, i);
-  best_step<4>(v, i);
-  best_step<2>(v, i);
-  best_step<1>(v, i);
-}
-
-// One compare-exchange of a bitonic network with partner lane ^ S.
+// One compare-exchange of a bitonic network on packed keys, partner lane ^ S:
+// the lane keeps the smaller key when (it is the lower lane) == ascending.
 template <int S>
-__device__ __forceinline__ void cas_step(float& v, int& i, bool ascending) {
-  const float ov = xor_lane<S>(v);
-  const int oi = xor_lane<S>(i);
-  const bool lower = (lane_id() & S) == 0;
-  const bool want_better = (lower == ascending);
-  const bool self_better = precedes(v, i, ov, oi);
-  if (want_better != self_better && (v != ov || i != oi)) { v = ov; i = oi; }
+__device__ __forceinline__ void cas_key(skey& x, bool ascending) {
+  const skey o = xor_lane<S>(x);
+  const bool keep_min = ((lane_id() & S) == 0) == ascending;
+  x = ((o < x) == keep_min) ? o : x;
 }
 
-template <int SIZE, int S>
-__device__ __forceinline__ void bitonic_merge_steps(float& v, int& i) {
-  const bool ascending = SIZE == kWave || (lane_id() & SIZE) == 0;
-  cas_step<S>(v, i, ascending);
-  if constexpr (S > 1) bitonic_merge_steps<SIZE, S / 2>(v, i);
+template <int SIZE, int GROUP, int S>
+__device__ __forceinline__ void key_merge_steps(skey& x) {
+  const bool ascending = SIZE == GROUP || (lane_id() & SIZE) == 0;
+  cas_key<S>(x, ascending);
+  if constexpr (S > 1) key_merge_steps<SIZE, GROUP, S / 2>(x);
+}
+template <int SIZE, int GROUP>
+__device__ __forceinline__ void key_stages(skey& x) {
+  if constexpr (SIZE > 2) key_stages<SIZE / 2, GROUP>(x);
+  key_merge_steps<SIZE, GROUP, SIZE / 2>(x);
 }
 
-template <int SIZE>
-__device__ __forceinline__ void bitonic_stages(float& v, int& i) {
-  if constexpr (SIZE > 2) bitonic_stages<SIZE / 2>(v, i);
-  bitonic_merge_steps<SIZE, SIZE / 2>(v, i);
+// Smallest packed key of the wave, in every lane.
+__device__ __forceinline__ skey min_lanes(skey x) {
+  skey o;
+  o = xor_lane<32>(x); x = o < x ? o : x;
+  o = xor_lane<16>(x); x = o < x ? o : x;
+  o = xor_lane<8>(x);  x = o < x ? o : x;
+  o = xor_lane<4>(x);  x = o < x ? o : x;
+  o = xor_lane<2>(x);  x = o < x ? o : x;
+  o = xor_lane<1>(x);  x = o < x ? o : x;
+  return x;
 }
 
-// Bitonic sort of one (value, index) per lane across the wave, best first.
-__device__ __forceinline__ void wave_bitonic_sort(float& v, int& i) { bitonic_stages<kWave>(v, i); }
-
-// k rounds of wave-wide argmin over J candidates per lane; lane r < k ends
-// up holding the r-th best (value, index).  Removed or empty entries are
-// (+inf, kNoIndex) and order after every real candidate.
-template <int J>
-__device__ __forceinline__ void wave_select_k(float (&cv)[J], int (&ci)[J], int k,
-                                              float& mine_v, int& mine_i) {
-  const int lane = lane_id();
-  mine_v = __builtin_inff();
-  mine_i = kNoIndex;
-  for (int round = 0; round < k; ++round) {
-    float bv = cv[0];
-    int bi = ci[0];
-#pragma unroll
-    for (int j = 1; j < J; ++j)
-      if (precedes(cv[j], ci[j], bv, bi)) { bv = cv[j]; bi = ci[j]; }
-    wave_best(bv, bi);
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-      if (ci[j] == bi && cv[j] == bv) { cv[j] = __builtin_inff(); ci[j] = kNoIndex; }
-    if (lane == round) { mine_v = bv; mine_i = bi; }
-  }
+// Bitonic sort of one packed key per lane within every aligned group of
+// GROUP lanes (16, 32 or 64), ascending in each group.  All lanes active.
+template <int GROUP>
+__device__ __forceinline__ void sort_keys(skey& x) {
+  static_assert(GROUP == 16 || GROUP == 32 || GROUP == 64, "group");
+  key_stages<GROUP, GROUP>(x);
 }
 
 // Sanitise an ordering key: NaN orders last.

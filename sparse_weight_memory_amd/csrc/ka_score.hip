@@ -20,12 +20,13 @@
 // Key norms are summed in fp64, so the ordering keys carry far less rounding
 // than the 1e-6 relative gap at which two candidates count as tied.
 //
-// Selection, one wave per token: a bitonic sort of the first 64 candidates
-// gives a threshold (the k-th best); the remaining candidates are filtered
-// against it with one ballot per 64, the few that pass are compacted into
-// LDS, and a final bitonic sort of the k best plus the survivors gives the
-// block's top-k.  Every step orders by (value, index), which is unique, so
-// the result is deterministic.
+// Selection, one wave per token, on packed 64-bit (value, index) keys: a
+// bitonic sort of the first 64 candidates gives a threshold (the k-th best);
+// the remaining candidates are filtered against it with one ballot per 64,
+// the few that pass are compacted into LDS, and a bitonic sort of the k best
+// plus the survivors (over 16, 32 or 64 lanes, whichever holds them) gives
+// the block's top-k.  Every step orders by (value, index), which is unique,
+// so the result is deterministic.
 // Work items are laid out so that the token tiles sharing one key block run
 // on one XCD (workgroup i is dispatched to XCD i % 8), which keeps the block's
 // keys in that XCD's L2.
@@ -54,8 +55,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   float* part = qs + kTokTile * qpitch;                  // [ndq][16][blk + 1]
   double* knp = reinterpret_cast<double*>(part + ndq * kTokTile * (blk + 1));  // [ndq][blk]
   float* sc = part;                                      // [16][blk + 1], reuses part[0]
-  float* surv_v = reinterpret_cast<float*>(knp + ndq * blk);  // [16][blk] filter survivors
-  int* surv_i = reinterpret_cast<int*>(surv_v + kTokTile * blk);
+  skey* surv = reinterpret_cast<skey*>(knp + ndq * blk);    // [16][blk] filter survivors
 
   const int ntt = (a.T + kTokTile - 1) / kTokTile;
   const int total = a.U * 2 * a.nblk * ntt;
@@ -73,6 +73,35 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = lane_id();
+
+  // ---- this wave's key operands: wave (kt, dq) = key tile kt over dim share
+  // dq.  The first step group is requested before anything else, so its
+  // latency overlaps the query staging.  (Requesting more at once does not
+  // pay: a wave-wide load here touches 16 key rows, and the compute unit's
+  // load path, not latency, then sets the pace.)
+  const int kt = wave % nkt;
+  const int dq = wave / nkt;
+  const int row = lane & 15;          // A row (key) / B column (token)
+  const int quad = lane >> 4;         // 4-dim group inside a 16-dim step
+  const int share = ((half + 16 * ndq - 1) / (16 * ndq)) * 16;   // dims per share
+  const int d_lo = dq * share;
+  const int steps = share / 16;
+  const int key = kb * blk + kt * 16 + row;
+  const bool kvalid = key < a.n;
+  const float* krow = (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k +
+                      ((int64_t)hh * a.n + (kvalid ? key : 0)) * half;
+  auto step_dim = [&](int st) { return d_lo + st * 16 + quad * 4; };   // this lane's first dim of step st
+  auto load_group = [&](float4 (&dst)[kStepGroup], int s0) {
+#pragma unroll
+    for (int j = 0; j < kStepGroup; ++j) {
+      const int d = step_dim(s0 + j);
+      const bool ok = s0 + j < steps && d < half;
+      dst[j] = (ok && kvalid) ? *reinterpret_cast<const float4*>(krow + d)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  float4 ak0[kStepGroup], ak1[kStepGroup];
+  load_group(ak0, 0);
 
   // ---- stage the 16-token query tile (this half) in LDS
   const int half4 = half >> 2;
@@ -99,33 +128,14 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     if (lane == 0) a.qnorm[((int64_t)u * a.T + t0 + wave) * 2 + h] = (float)s;
   }
 
-  // ---- scores: wave (kt, dq) = key tile kt over dim share dq
-  const int kt = wave % nkt;
-  const int dq = wave / nkt;
-  const int row = lane & 15;          // A row (key) / B column (token)
-  const int quad = lane >> 4;         // 4-dim group inside a 16-dim step
-  const int share = ((half + 16 * ndq - 1) / (16 * ndq)) * 16;   // dims per share
-  const int d_lo = dq * share;
-  const int steps = share / 16;
-  const int key = kb * blk + kt * 16 + row;
-  const bool kvalid = key < a.n;
-  const float* krow = (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k +
-                      ((int64_t)hh * a.n + (kvalid ? key : 0)) * half;
-  // two independent accumulator chains (x,y and z,w components of each step)
+  // ---- scores.  Two independent accumulator chains (x,y and z,w components
+  // of each step); a group's key operands are requested just before it runs.
   v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
   double ksq = 0.0;
-  for (int s0 = 0; s0 < steps; s0 += kStepGroup) {
-    // every key operand of the group is requested before the first MFMA
-    float4 ak[kStepGroup];
+  auto mfma_group = [&](const float4 (&ak)[kStepGroup], int s0) {
 #pragma unroll
     for (int j = 0; j < kStepGroup; ++j) {
-      const int d = d_lo + (s0 + j) * 16 + quad * 4;
-      const bool ok = s0 + j < steps && d < half;
-      ak[j] = (ok && kvalid) ? *reinterpret_cast<const float4*>(krow + d) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int j = 0; j < kStepGroup; ++j) {
-      const int d = d_lo + (s0 + j) * 16 + quad * 4;
+      const int d = step_dim(s0 + j);
       const bool ok = s0 + j < steps && d < half;
       const float4 bq = ok ? *reinterpret_cast<const float4*>(&qs[row * qpitch + d])
                            : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -136,6 +146,14 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
       acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[j].y, bq.y, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[j].w, bq.w, acc1, 0, 0, 0);
     }
+  };
+  for (int s0 = 0; s0 < steps; s0 += 2 * kStepGroup) {
+    mfma_group(ak0, s0);
+    if (s0 + kStepGroup < steps) {
+      load_group(ak1, s0 + kStepGroup);
+      mfma_group(ak1, s0 + kStepGroup);
+    }
+    if (s0 + 2 * kStepGroup < steps) load_group(ak0, s0 + 2 * kStepGroup);
   }
   ksq += xor_lane<16>(ksq);
   ksq += xor_lane<32>(ksq);
@@ -201,54 +219,41 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   if (tw >= a.T) return;
   const int k = a.k;
   const float* srow = sc + wave * ppitch;
-  auto cand = [&](int c, float& v, int& i) {
+  auto cand = [&](int c) -> skey {
     const int gkey = kb * blk + c;
-    i = gkey < a.n ? gkey : kNoIndex;
-    v = i == kNoIndex ? __builtin_inff() : srow[c];
+    return gkey < a.n ? pack_key(srow[c], gkey) : kEmptyKey;
   };
-  float v;
-  int ix;
-  cand(lane, v, ix);
-  wave_bitonic_sort(v, ix);                       // best 64 of the first 64
+  skey x = cand(lane);
+  sort_keys<64>(x);                               // the first 64, best first
   if (blk > kWave) {
-    const float th_v = readlane_f(v, k - 1);
-    const int th_i = readlane_i(ix, k - 1);
-    float* sv = surv_v + wave * blk;
-    int* si = surv_i + wave * blk;
+    const skey th = readlane_k(x, k - 1);         // k-th best so far
+    skey* sv = surv + wave * blk;
     int nsurv = 0;
     for (int c0 = kWave; c0 < blk; c0 += kWave) {
-      float cv;
-      int ci;
-      cand(c0 + lane, cv, ci);
-      const bool pass = precedes(cv, ci, th_v, th_i);
+      const skey cx = cand(c0 + lane);
+      const bool pass = cx < th;
       const unsigned long long m = __ballot(pass);
-      if (pass) {
-        const int pos = nsurv + __popcll(m & ((1ull << lane) - 1ull));
-        sv[pos] = cv;
-        si[pos] = ci;
-      }
+      if (pass) sv[nsurv + __popcll(m & ((1ull << lane) - 1ull))] = cx;
       nsurv += __popcll(m);
     }
-    // merge the k best with the survivors, 64 - k at a time
+    // the k best stay in lanes 0..k-1; survivors fill lanes k.. in batches,
+    // and only the lane group that holds them is sorted
     const int fresh = kWave - k;
     for (int pos = 0; pos < nsurv; pos += fresh) {
-      const float mv = __shfl(v, lane - fresh, kWave);
-      const int mi = __shfl(ix, lane - fresh, kWave);
-      if (lane < fresh) {
-        const int c = pos + lane;
-        v = c < nsurv ? sv[c] : __builtin_inff();
-        ix = c < nsurv ? si[c] : kNoIndex;
-      } else {
-        v = mv;
-        ix = mi;
+      if (lane >= k) {
+        const int c = pos + lane - k;
+        x = c < nsurv ? sv[c] : kEmptyKey;
       }
-      wave_bitonic_sort(v, ix);
+      const int cnt = k + min(fresh, nsurv - pos);
+      if (cnt <= 16) sort_keys<16>(x);
+      else if (cnt <= 32) sort_keys<32>(x);
+      else sort_keys<64>(x);
     }
   }
   if (lane < k) {
     const int64_t base = ((((int64_t)u * a.T + tw) * 2 + h) * a.nblk + kb) * k;
-    a.half_o[base + lane] = v;
-    a.half_i[base + lane] = ix;
+    a.half_o[base + lane] = key_value(x);
+    a.half_i[base + lane] = key_index(x);
   }
 }
 
@@ -264,7 +269,7 @@ size_t ka_smem_bytes(int half, int blk) {
   return sizeof(float) * kTokTile * (half + 4)                       // queries
          + sizeof(float) * ndq * kTokTile * (blk + 1)                // dim-share partials / scores
          + sizeof(double) * ndq * blk                                // key-norm partials
-         + (sizeof(float) + sizeof(int)) * kTokTile * blk;           // filter survivors
+         + sizeof(skey) * kTokTile * blk;                            // filter survivors
 }
 
 int ka_grid(const ChunkArgs& a) {

@@ -61,51 +61,41 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
                                : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
-  // ---- 1. per-half best-k lists (lane m < k holds the m-th best)
-  float ho[2];
-  int hi[2];
+  // ---- 1. per-half best-k lists (lane m < k holds the m-th best), as
+  // packed (ordering key, sub-key index) keys
+  skey hk[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int64_t base = (ut * 2 + h) * a.nblk * k;
     if (a.nblk == 1) {
-      ho[h] = lane < k ? a.half_o[base + lane] : inf;
-      hi[h] = lane < k ? a.half_i[base + lane] : kNoIndex;
+      const int ix = lane < k ? a.half_i[base + lane] : kNoIndex;
+      hk[h] = ix == kNoIndex ? kEmptyKey : pack_key(order_key(a.half_o[base + lane]), ix);
     } else {
-      // merge the per-block lists: the best k so far sit in lanes 64-k..63,
-      // the next 64-k candidates fill lanes 0..63-k, and a bitonic sort
-      // brings the best k of both to lanes 0..k-1
+      // merge the per-block lists: the best k so far stay in lanes 0..k-1,
+      // the next 64-k candidates fill lanes k..63, and a bitonic sort brings
+      // the best k of both back to lanes 0..k-1
       const int nc = a.nblk * k;
       const int fresh = kWave - k;
-      float v = inf;
-      int ix = kNoIndex;
+      skey x = kEmptyKey;
       for (int pos = 0; pos < nc; pos += fresh) {
-        const float mv = __shfl(v, lane - fresh, kWave);
-        const int mi = __shfl(ix, lane - fresh, kWave);
-        const int c = pos + lane;
-        if (lane < fresh) {
-          v = c < nc ? order_key(a.half_o[base + c]) : inf;
-          ix = c < nc ? a.half_i[base + c] : kNoIndex;
-          if (ix == kNoIndex) v = inf;
-        } else {
-          v = pos == 0 ? inf : mv;
-          ix = pos == 0 ? kNoIndex : mi;
+        const int c = pos + lane - k;
+        if (lane >= k) {
+          const int ix = c < nc ? a.half_i[base + c] : kNoIndex;
+          x = ix == kNoIndex ? kEmptyKey : pack_key(order_key(a.half_o[base + c]), ix);
         }
-        wave_bitonic_sort(v, ix);
+        sort_keys<64>(x);
       }
-      ho[h] = lane < k ? v : inf;
-      hi[h] = lane < k ? ix : kNoIndex;
+      hk[h] = lane < k ? x : kEmptyKey;
     }
   }
 
   // ---- 2. pruned Cartesian candidates, then the k best
   int npr = 0;
   for (int i = 0; i < k; ++i) npr += k / (i + 1);
-  float sel_o;
-  int sel_s;
+  skey sel;
   {
     constexpr int J = 3;   // sum_i floor(32/i) = 130 <= 3 * 64
-    float cv[J];
-    int ci[J];
+    skey cx[J];
 #pragma unroll
     for (int r = 0; r < J; ++r) {
       int c = lane + 64 * r;
@@ -115,26 +105,38 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
         while (c >= k / (i + 1)) { c -= k / (i + 1); ++i; }
       }
       const int j = in ? c : 0;
-      const float oa = __shfl(ho[0], i, kWave);
-      const int ia = __shfl(hi[0], i, kWave);
-      const float ob = __shfl(ho[1], j, kWave);
-      const int ib = __shfl(hi[1], j, kWave);
-      if (in && ia != kNoIndex && ib != kNoIndex) {
-        cv[r] = order_key(oa + ob);
-        ci[r] = ia * n + ib;
-      } else {
-        cv[r] = inf;
-        ci[r] = kNoIndex;
+      const skey ka = __shfl(hk[0], i, kWave);
+      const skey kb = __shfl(hk[1], j, kWave);
+      const int ia = key_index(ka), ib = key_index(kb);
+      cx[r] = (in && ia != kNoIndex && ib != kNoIndex)
+                  ? pack_key(order_key(key_value(ka) + key_value(kb)), ia * n + ib)
+                  : kEmptyKey;
+    }
+    if (npr <= 16) {
+      sel = cx[0];
+      sort_keys<16>(sel);
+    } else if (npr <= 32) {
+      sel = cx[0];
+      sort_keys<32>(sel);
+    } else if (npr <= 64) {
+      sel = cx[0];
+      sort_keys<64>(sel);
+    } else {
+      // k rounds of wave-wide minimum; lane r keeps the r-th best
+      sel = kEmptyKey;
+      for (int round = 0; round < k; ++round) {
+        skey m = cx[0];
+#pragma unroll
+        for (int r = 1; r < J; ++r) m = cx[r] < m ? cx[r] : m;
+        m = min_lanes(m);
+#pragma unroll
+        for (int r = 0; r < J; ++r) cx[r] = cx[r] == m ? kEmptyKey : cx[r];
+        if (lane == round) sel = m;
       }
     }
-    if (npr <= 64) {
-      sel_o = cv[0];
-      sel_s = ci[0];
-      wave_bitonic_sort(sel_o, sel_s);
-    } else {
-      wave_select_k<J>(cv, ci, k, sel_o, sel_s);
-    }
   }
+  const float sel_o = key_value(sel);
+  const int sel_s = sel == kEmptyKey ? kNoIndex : key_index(sel);
 
   // ---- 3. weights (lanes m < k)
   const int64_t N = (int64_t)n * n;

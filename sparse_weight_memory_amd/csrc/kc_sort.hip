@@ -27,8 +27,8 @@
 // indirectly.
 //
 // Outputs per region, at its offset in the (list, unit) arrays:
-//   pay        (token, coefficient) of every kept pair in sorted order -- the
-//              update kernel reads a segment's pairs with one load;
+//   pay        the kept pair indices in sorted order -- the update kernel
+//              reads a segment's pairs with one load;
 //   long_rec   (row, first pair, pairs) of segments longer than kShortSeg;
 //   short_rec  the same for the other segments;
 //   kinds      (long count, short count, offset).
@@ -51,18 +51,8 @@ __device__ __forceinline__ int region_of(int key, int bits) {
   return bits == 0 ? 0 : (int)(((unsigned)key * 0x9E3779B1u) >> (32 - bits));
 }
 
-// Inclusive scan across the wave: DPP row shifts, then row totals by readlane.
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
-  const int r0 = readlane_i(x, 15), r1 = readlane_i(x, 31), r2 = readlane_i(x, 47);
-  const int row = lane_id() >> 4;
-  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
-}
-
 // Exclusive scan of one int per thread across the block; *total = block sum.
+// wave_tot must not be written again before the caller's next barrier.
 __device__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
   const int wave = threadIdx.x / kWave;
   const int incl = wave_inclusive_scan(x);
@@ -75,26 +65,8 @@ __device__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
     base += w < wave ? t : 0;
     sum += t;
   }
-  __syncthreads();          // wave_tot may be reused right after
   *total = sum;
   return base + incl - x;
-}
-
-__device__ int block_max(int x, int* wave_tot) {
-  x = max(x, xor_lane<32>(x));
-  x = max(x, xor_lane<16>(x));
-  x = max(x, xor_lane<8>(x));
-  x = max(x, xor_lane<4>(x));
-  x = max(x, xor_lane<2>(x));
-  x = max(x, xor_lane<1>(x));
-  const int wave = threadIdx.x / kWave;
-  if (lane_id() == 0) wave_tot[wave] = x;
-  __syncthreads();
-  int m = wave_tot[0];
-#pragma unroll
-  for (int w = 1; w < kGroupWaves; ++w) m = m > wave_tot[w] ? m : wave_tot[w];
-  __syncthreads();
-  return m;
 }
 
 // Lanes of this wave holding the same digit (among `valid` lanes).
@@ -125,7 +97,7 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   int* key1 = idx0 + P;                   // [P] (pong)
   int* idx1 = key1 + P;                   // [P] (pong)
   int* cnt = idx1 + P;                    // [kGroupWaves][kDigits]
-  int* red = cnt + kGroupWaves * kDigits; // [2][kGroupWaves]
+  int* red = cnt + kGroupWaves * kDigits; // [3][kGroupWaves]
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -156,20 +128,28 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
     kept += __popcll(__ballot(mine));
     kmax = mine && key > kmax ? key : kmax;
   }
+  kmax = max(kmax, xor_lane<32>(kmax));
+  kmax = max(kmax, xor_lane<16>(kmax));
+  kmax = max(kmax, xor_lane<8>(kmax));
+  kmax = max(kmax, xor_lane<4>(kmax));
+  kmax = max(kmax, xor_lane<2>(kmax));
+  kmax = max(kmax, xor_lane<1>(kmax));
   if (lane == 0) {
     red[wave] = kept;
     red[kGroupWaves + wave] = below;
+    red[2 * kGroupWaves + wave] = kmax;
   }
   __syncthreads();
   int base = 0, M = 0, off = 0;
+  kmax = 0;
 #pragma unroll
   for (int w = 0; w < kGroupWaves; ++w) {
     const int t = red[w];
     base += w < wave ? t : 0;
     M += t;
     off += red[kGroupWaves + w];
+    kmax = max(kmax, red[2 * kGroupWaves + w]);
   }
-  __syncthreads();
   int4* kinds = a.kinds + ((int64_t)list * a.U + u) * a.regions + region;
   if (M == 0) {                     // block-uniform
     if (tid == 0) *kinds = make_int4(0, 0, off, 0);
@@ -188,7 +168,9 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
     }
     base += __popcll(m);
   }
-  kmax = block_max(kmax, red);
+  int* mycnt = cnt + wave * kDigits;   // only this wave counts into / scatters from it
+  for (int i = lane; i < kDigits; i += kWave) mycnt[i] = 0;
+  __syncthreads();
   int bits = 0;
   while (bits < 31 && (kmax >> bits) != 0) ++bits;
   const int passes = (bits + kBits - 1) / kBits;
@@ -199,11 +181,8 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   const int t_lo = wave * vtpw;
   const int t_hi = min(vtiles, t_lo + vtpw);
   int *ks = key0, *is = idx0, *kd = key1, *id = idx1;
-  int* mycnt = cnt + wave * kDigits;
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * kBits;
-    for (int i = tid; i < kGroupWaves * kDigits; i += kGroupThreads) cnt[i] = 0;
-    __syncthreads();
     for (int tile = t_lo; tile < t_hi; ++tile) {
       const int i = tile * kWave + lane;
       const bool valid = i < M;
@@ -247,21 +226,11 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
       }
       if (valid && lower == 0ull) mycnt[d] = b0 + __popcll(peers);
     }
+    for (int i = lane; i < kDigits; i += kWave) mycnt[i] = 0;   // for the next pass
     __syncthreads();
     int* t;
     t = ks; ks = kd; kd = t;
     t = is; is = id; id = t;
-  }
-
-  // ---- payloads in sorted order: (token, coefficient)
-  {
-    int2* pay = a.pay + lbase + off;
-    const float* cf = list == 0 ? a.sel_w + (int64_t)u * P
-                                : a.coef + (int64_t)(list - 1) * a.U * P + (int64_t)u * P;
-    for (int i = tid; i < M; i += kGroupThreads) {
-      const int p = is[i];
-      pay[i] = make_int2(p / a.k, __float_as_int(cf[p]));
-    }
   }
 
   // ---- segments: heads of runs of equal rows.  The pong buffers are free
@@ -283,12 +252,13 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
     hbase += w < wave ? t : 0;
     nseg += t;
   }
-  __syncthreads();
+  int* pay = a.pay + lbase + off;
   for (int tile = t_lo; tile < t_hi; ++tile) {
     const int i = tile * kWave + lane;
     const bool head = i < M && (i == 0 || ks[i - 1] != ks[i]);
     const unsigned long long m = __ballot(head);
     if (head) segl[hbase + __popcll(m & lanes_below())] = i;
+    if (i < M) pay[i] = is[i];
     hbase += __popcll(m);
   }
   if (tid == 0) segl[nseg] = M;
@@ -346,7 +316,7 @@ int group_regions(int units) {
 }
 
 size_t kc_smem_bytes(int P) {
-  return sizeof(int) * ((size_t)4 * P + (size_t)kGroupWaves * kDigits + 2 * kGroupWaves);
+  return sizeof(int) * ((size_t)4 * P + (size_t)kGroupWaves * kDigits + 3 * kGroupWaves);
 }
 
 hipError_t launch_kc(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {

@@ -20,9 +20,9 @@
 // either one long segment (more than kShortSeg pairs), which the W waves of a
 // workgroup split into contiguous pieces and combine in LDS in wave order,
 // or up to W short segments, one per wave.  A segment's record (row, first
-// pair, pairs) and its pairs' (token, coefficient) payloads come straight
-// from the grouping kernel, so a wave reaches the data rows after two
-// dependent loads.  Every sum runs in a fixed order, so results do not
+// pair, pairs) and its sorted pair indices come straight from the grouping
+// kernel; a pair's coefficient is loaded beside its data row, so a wave
+// reaches the data rows after two dependent loads.  Every sum runs in a fixed order, so results do not
 // depend on scheduling, and no atomics are used.
 
 #include "fwpkm_device.h"
@@ -32,7 +32,6 @@ namespace fwpkm {
 
 namespace {
 
-constexpr int kRowBatch = 8;   // data rows a wave has in flight
 
 // pref[i] = tasks of regions [0, i) for i in [0, L]; nlong / nshort / offs
 // receive the regions' counts.  All threads of the block take part.
@@ -40,7 +39,7 @@ template <int W>
 __device__ void task_prefix(const int4* kinds, int L, int* pref, int* nlong, int* nshort,
                             int* offs, int* wtot) {
   constexpr int NT = W * kWave;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int tid = threadIdx.x, wave = tid / kWave;
   const int per = (L + NT - 1) / NT;
   const int beg = tid * per;
   int local = 0;
@@ -53,13 +52,8 @@ __device__ void task_prefix(const int4* kinds, int L, int* pref, int* nlong, int
       local += kd.x + (kd.y + W - 1) / W;
     }
   }
-  int incl = local;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += y;
-  }
-  if (lane == kWave - 1) wtot[wave] = incl;
+  const int incl = wave_inclusive_scan(local);
+  if (lane_id() == kWave - 1) wtot[wave] = incl;
   __syncthreads();
   int base = 0;
   for (int w = 0; w < wave; ++w) base += wtot[w];
@@ -74,21 +68,25 @@ __device__ void task_prefix(const int4* kinds, int L, int* pref, int* nlong, int
   __syncthreads();
 }
 
-// One wave's sum over the pairs pay[0, n) of a V segment:  sum_p w_p g_{t_p}.
-template <int R>
-__device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const int2* pay,
+// One wave's sum over the sorted pairs pay[0, n) of a V segment:
+// sum_p w_p g_{t_p}.  NB data rows are in flight at a time.
+template <int R, int NB>
+__device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const int* pay,
                                                 int n, float4 (&acc)[R]) {
   const int lane = lane_id();
   const int width4 = a.dv >> 2;
   const float* gbase = a.g + (int64_t)u * a.T * a.dv;
+  const float* sw = a.sel_w + (int64_t)u * a.P;
   for (int base = 0; base < n; base += kWave) {
     const int nb = min(kWave, n - base);
-    const int2 pl = lane < nb ? pay[base + lane] : make_int2(0, 0);
-    for (int i = 0; i < nb; i += kRowBatch) {
-      float4 gv[kRowBatch][R];
+    const int pl = lane < nb ? pay[base + lane] : 0;
+    const int tl = pl / a.k;
+    const float wl = lane < nb ? sw[pl] : 0.f;
+    for (int i = 0; i < nb; i += NB) {
+      float4 gv[NB][R];
 #pragma unroll
-      for (int jj = 0; jj < kRowBatch; ++jj) {
-        const int t = readlane_i(pl.x, min(i + jj, nb - 1));
+      for (int jj = 0; jj < NB; ++jj) {
+        const int t = readlane_i(tl, min(i + jj, nb - 1));
         const float4* gr = reinterpret_cast<const float4*>(gbase + (int64_t)t * a.dv);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -97,9 +95,9 @@ __device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < kRowBatch; ++jj) {
+      for (int jj = 0; jj < NB; ++jj) {
         if (i + jj < nb) {
-          const float w = __int_as_float(readlane_i(pl.y, i + jj));
+          const float w = readlane_f(wl, i + jj);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             acc[r].x += w * gv[jj][r].x; acc[r].y += w * gv[jj][r].y;
@@ -113,21 +111,24 @@ __device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const
 
 // One wave's sum over the pairs pay[0, n) of a K segment (half h):
 //   IDW sum_p c_p (q_h[t_p] - old),  dot sum_p c_p q_h[t_p].
-template <int R>
-__device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, const int2* pay,
+template <int R, int NB>
+__device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, const int* pay,
                                               int n, const float4 (&old)[R], float4 (&acc)[R]) {
   const int lane = lane_id();
   const int width4 = a.half >> 2;
   const int b = u / a.H, hh = u - b * a.H;
   const bool idw = a.mode == 0;
+  const float* cf = a.coef + (int64_t)h * a.U * a.P + (int64_t)u * a.P;
   for (int base = 0; base < n; base += kWave) {
     const int nb = min(kWave, n - base);
-    const int2 pl = lane < nb ? pay[base + lane] : make_int2(0, 0);
-    for (int i = 0; i < nb; i += kRowBatch) {
-      float4 qv[kRowBatch][R];
+    const int pl = lane < nb ? pay[base + lane] : 0;
+    const int tl = pl / a.k;
+    const float cl = lane < nb ? cf[pl] : 0.f;
+    for (int i = 0; i < nb; i += NB) {
+      float4 qv[NB][R];
 #pragma unroll
-      for (int jj = 0; jj < kRowBatch; ++jj) {
-        const int t = readlane_i(pl.x, min(i + jj, nb - 1));
+      for (int jj = 0; jj < NB; ++jj) {
+        const int t = readlane_i(tl, min(i + jj, nb - 1));
         const float4* qr = reinterpret_cast<const float4*>(
             a.q + ((int64_t)(b * a.T + t) * a.H + hh) * a.dqk + h * a.half);
 #pragma unroll
@@ -137,9 +138,9 @@ __device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, 
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < kRowBatch; ++jj) {
+      for (int jj = 0; jj < NB; ++jj) {
         if (i + jj < nb) {
-          const float cc = __int_as_float(readlane_i(pl.y, i + jj));
+          const float cc = readlane_f(cl, i + jj);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             float4 x = qv[jj][r];
@@ -152,6 +153,13 @@ __device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, 
   }
 }
 
+// Waves per SIMD each variant is compiled for: two workgroups of W waves per
+// compute unit (four SIMDs), so a chunk's tasks fit on the device at once
+// (the register budget per wave is 512 / waves).
+template <int W>
+constexpr int kd_waves_per_simd() { return 2 * W / 4; }
+constexpr int kKdResidentPerCu = 2;
+
 // LDS of one update workgroup for L regions: partial sums, then the region
 // table.
 template <int R, int W>
@@ -161,8 +169,8 @@ __host__ __device__ constexpr size_t kd_parts_bytes() {
 
 }  // namespace
 
-template <int R, int W>
-__global__ __launch_bounds__(W * kWave) void kd_update(ChunkArgs a) {
+template <int R, int W, int NB>
+__global__ __launch_bounds__(W * kWave, kd_waves_per_simd<W>()) void kd_update(ChunkArgs a) {
   extern __shared__ float4 kd_lds[];
   float4* parts = kd_lds;                                             // [W][64 R]
   const int L = 3 * a.U * a.regions;
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(W * kWave) void kd_update(ChunkArgs a) {
       np = min(cnt, r0 + ql) - r0;
       p0 += r0;
     }
-    const int2* pay = a.pay + lbase + p0;
+    const int* pay = a.pay + lbase + p0;
     const bool finisher = !is_long || wave == 0;
 
     float4* trow;
@@ -226,7 +234,7 @@ __global__ __launch_bounds__(W * kWave) void kd_update(ChunkArgs a) {
         const int c = lane + 64 * r;
         old[r] = (finisher && c < width4) ? trow[c] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      sum_value_pairs<R>(a, u, pay, np, acc);
+      sum_value_pairs<R, NB>(a, u, pay, np, acc);
     } else {
       const int h = list - 1;
       width4 = a.half >> 2;
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(W * kWave) void kd_update(ChunkArgs a) {
         const int c = lane + 64 * r;
         old[r] = c < width4 ? trow[c] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      sum_key_pairs<R>(a, u, h, pay, np, old, acc);
+      sum_key_pairs<R, NB>(a, u, h, pay, np, old, acc);
     }
 
     if (is_long) {
@@ -276,29 +284,45 @@ __global__ __launch_bounds__(W * kWave) void kd_update(ChunkArgs a) {
 
 namespace {
 
-template <int R, int W>
+int device_cus() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  }();
+  return cus;
+}
+
+template <int R, int W, int NB>
 hipError_t launch_kd_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
   const int64_t L = (int64_t)3 * a.U * a.regions;
   const size_t smem = kd_parts_bytes<R, W>() + sizeof(int) * (size_t)(4 * L + 1 + W);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&kd_update<R, W>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      reinterpret_cast<const void*>(&kd_update<R, W, NB>), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)(kd_parts_bytes<R, W>() + sizeof(int) * (size_t)(4 * kUpdMaxLists + 1 + W)));
   if (attr != hipSuccess) return attr;
-  // tasks cannot exceed long segments + short groups of W, per region
+  // tasks cannot exceed long segments + short groups of W, per region; more
+  // workgroups than fit on the device at once would only queue behind the
+  // first ones, so the grid stops at what is resident (tasks loop)
   const int64_t most = (int64_t)3 * a.U * a.P / (kShortSeg + 1) +
                        (int64_t)3 * a.U * a.P / W + L;
-  const int64_t gx = most < 1024 ? most : 1024;
-  return fw_launch(kd_update<R, W>, dim3((unsigned)gx), dim3(W * kWave), (uint32_t)smem, s, tm, a);
+  const int64_t resident = (int64_t)kKdResidentPerCu * device_cus();
+  const int64_t gx = most < resident ? most : resident;
+  return fw_launch(kd_update<R, W, NB>, dim3((unsigned)gx), dim3(W * kWave), (uint32_t)smem, s, tm, a);
 }
 
 }  // namespace
 
 hipError_t launch_kd(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
   const int r = (a.pw / 4 + 63) / 64;
-  if (r <= 1) return launch_kd_as<1, 16>(a, s, tm);
-  if (r <= 2) return launch_kd_as<2, 16>(a, s, tm);
-  if (r <= 4) return launch_kd_as<4, 8>(a, s, tm);
-  return launch_kd_as<8, 4>(a, s, tm);
+  // (float4 per lane per row, waves, rows in flight): the largest of each
+  // that keeps two workgroups per compute unit without register spills
+  if (r <= 1) return launch_kd_as<1, 16, 4>(a, s, tm);
+  if (r <= 2) return launch_kd_as<2, 8, 8>(a, s, tm);
+  if (r <= 4) return launch_kd_as<4, 4, 4>(a, s, tm);
+  return launch_kd_as<8, 4, 4>(a, s, tm);
 }
 
 }  // namespace fwpkm
