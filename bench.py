@@ -32,6 +32,41 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
 DEFAULT_WORKLOAD = 3            # 65,536 slots, d_v 512, top-8: 8 x 4096 tokens in 16 chained chunks
+KERNEL_SOURCES = {              # the sources that fix each kernel's code
+    "score": ["ka_score.hip", "fwpkm_device.h"],
+    "read": ["kb_read.hip", "fwpkm_device.h"],
+    "sort": ["kc_sort.hip", "fwpkm_device.h"],
+    "update": ["kd_update.hip", "fwpkm_device.h"],
+}
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of each kernel, from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary committed under profiles/ (already scaled by the plain
+    copy calibration), for kernels whose sources are unchanged since the
+    counters were taken; None where there is no summary or it is stale."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}.md")
+    if not os.path.exists(path):
+        return {}
+    text = open(path).read()
+    try:
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(block)
+    except (IndexError, ValueError):
+        return {}
+    out = {}
+    for name, entry in data.get("kernels", {}).items():
+        h = hashlib.sha256()
+        for f in entry.get("sources", KERNEL_SOURCES.get(name, [])):
+            fp = os.path.join(ROOT, "sparse_weight_memory_amd", "csrc", f)
+            if not os.path.exists(fp):
+                h = None
+                break
+            h.update(open(fp, "rb").read())
+        fresh = h is not None and h.hexdigest()[:16] == entry.get("source_sha256_16")
+        out[name] = entry["bytes_per_launch"] if fresh else None
+    return out
 
 
 def parse():
@@ -277,7 +312,10 @@ def main():
         else:
             roof = {"bound": "hbm", "achieved": kd["alg_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] / roof["peak"]
-        roof["traffic"] = None
+        traffic = measured_traffic(cfg.name)
+        for name in kernels:
+            kernels[name]["hbm_bytes_counted"] = traffic.get(name)
+        roof["traffic"] = traffic.get(dom)
         roof["kernel"] = dom
         result["roofline"] = roof
 
