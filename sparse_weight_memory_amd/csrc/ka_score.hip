@@ -17,8 +17,18 @@
 // in LDS.  The key block (64, 128 or 256 keys) is chosen per launch so that
 // small chunks still spread over the whole chip: wave w multiplies key tile
 // (w mod blk/16) over its share of the dims; dim shares are summed in LDS.
-// Key norms are summed in fp64, so the ordering keys carry far less rounding
-// than the 1e-6 relative gap at which two candidates count as tied.
+// Each wave stages its own 16 key rows through a private LDS slice, 64 (or,
+// for d_h > 256, 32) dims at a time, loaded with whole lines (a wave-wide
+// load of matrix operands straight from memory would touch 16 key rows at
+// once, which the load path serves at a fraction of its rate); two (four)
+// chunks are in flight in registers, two in LDS.  With no barrier inside the
+// contraction, the waves of a SIMD drift apart and one's LDS traffic overlaps
+// another's matrix work.
+// Key norms are summed in fp32 beside the contraction (on this chip fp32
+// matrix instructions share the vector issue, so every extra instruction in
+// that loop costs time): their rounding, ~1e-7 of ||K||^2, stays well below
+// the dot product's and the 1e-6 relative gap at which candidates count as
+// tied.
 //
 // Selection, one wave per token, on packed 64-bit (value, index) keys: a
 // bitonic sort of the first 64 candidates gives a threshold (the k-th best);
@@ -42,20 +52,57 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreWaves = 16;
 constexpr int kMaxBlk = 256;       // largest key block
-constexpr int kStepGroup = 8;      // 16-dim steps whose key operands are loaded together
+constexpr int kStageRows = kScoreWaves * 16;              // (dim share, key) rows = 256
 
+// kDimChunk dims of every key row are staged in LDS at a time (64 when it
+// fits, else 32); kPrefetch chunks are in flight in registers.
+template <int kDimChunk, int kPrefetch>
+struct Staging {
+  static constexpr int kKPitch = kDimChunk + 4;                  // floats per staged row (pad)
+  static constexpr int kStageF4 = 16 * kDimChunk / 4 / kWave;    // float4 per lane per chunk
+  static constexpr int kLanesPerRow = kDimChunk / 4;             // one float4 each
+  static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
+};
+
+// Chunks of DC dims per dim share, rounded up to a multiple of the ring
+// depth PF (the extra chunks hold zero keys).
+template <int DC, int PF>
+__host__ __device__ inline int ka_chunks(int half, int blk) {
+  const int ndq = kScoreWaves / (blk / 16);
+  const int share = ((half + 16 * ndq - 1) / (16 * ndq)) * 16;
+  const int nchunks = (share + DC - 1) / DC;
+  return (nchunks + PF - 1) / PF * PF;
+}
+
+// Width of a staged query row: every dim a chunk of any dim share may touch
+// (columns past d_h are zero), so operand reads need no bounds test.
+template <int DC, int PF>
+__host__ __device__ inline int ka_query_width(int half, int blk) {
+  const int ndq = kScoreWaves / (blk / 16);
+  const int share = ((half + 16 * ndq - 1) / (16 * ndq)) * 16;
+  return (ndq - 1) * share + ka_chunks<DC, PF>(half, blk) * DC;
+}
+
+template <int kDimChunk, int kPrefetch>
 __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a) {
+  constexpr int kKPitch = Staging<kDimChunk, kPrefetch>::kKPitch;
+  constexpr int kStageF4 = Staging<kDimChunk, kPrefetch>::kStageF4;
+  constexpr int kLanesPerRow = Staging<kDimChunk, kPrefetch>::kLanesPerRow;
+  constexpr int kRowsPerLoad = Staging<kDimChunk, kPrefetch>::kRowsPerLoad;
   extern __shared__ float smem[];
   const int half = a.half;
   const int blk = a.key_block;             // 64, 128 or 256
   const int nkt = blk / 16;                // key tiles per block
   const int ndq = kScoreWaves / nkt;       // dim shares per key tile
-  const int qpitch = half + 4;
+  const int qwidth = ka_query_width<kDimChunk, kPrefetch>(half, blk);
+  const int qpitch = qwidth + 4;
   float* qs = smem;                                      // [16][qpitch]
-  float* part = qs + kTokTile * qpitch;                  // [ndq][16][blk + 1]
-  double* knp = reinterpret_cast<double*>(part + ndq * kTokTile * (blk + 1));  // [ndq][blk]
+  float* kst = qs + kTokTile * qpitch;                   // [16 waves][2][16][kKPitch] staged keys
+  double* knp = reinterpret_cast<double*>(kst + 2 * kStageRows * kKPitch);  // [ndq][blk]
+  // after the contraction the staging buffers are free:
+  float* part = kst;                                     // [ndq][16][blk + 1]
   float* sc = part;                                      // [16][blk + 1], reuses part[0]
-  skey* surv = reinterpret_cast<skey*>(knp + ndq * blk);    // [16][blk] filter survivors
+  skey* surv = reinterpret_cast<skey*>(kst + kStageRows * kKPitch);   // [16][blk] survivors
 
   const int ntt = (a.T + kTokTile - 1) / kTokTile;
   const int total = a.U * 2 * a.nblk * ntt;
@@ -74,47 +121,76 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   const int wave = tid / kWave;
   const int lane = lane_id();
 
-  // ---- this wave's key operands: wave (kt, dq) = key tile kt over dim share
-  // dq.  The first step group is requested before anything else, so its
-  // latency overlaps the query staging.  (Requesting more at once does not
-  // pay: a wave-wide load here touches 16 key rows, and the compute unit's
-  // load path, not latency, then sets the pace.)
+  // ---- geometry: wave (kt, dq) = key tile kt over dim share dq
   const int kt = wave % nkt;
   const int dq = wave / nkt;
   const int row = lane & 15;          // A row (key) / B column (token)
   const int quad = lane >> 4;         // 4-dim group inside a 16-dim step
   const int share = ((half + 16 * ndq - 1) / (16 * ndq)) * 16;   // dims per share
-  const int d_lo = dq * share;
   const int steps = share / 16;
-  const int key = kb * blk + kt * 16 + row;
-  const bool kvalid = key < a.n;
-  const float* krow = (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k +
-                      ((int64_t)hh * a.n + (kvalid ? key : 0)) * half;
-  auto step_dim = [&](int st) { return d_lo + st * 16 + quad * 4; };   // this lane's first dim of step st
-  auto load_group = [&](float4 (&dst)[kStepGroup], int s0) {
+  const int nchunks = (share + kDimChunk - 1) / kDimChunk;      // chunks holding data
+  const int nchunks_p = ka_chunks<kDimChunk, kPrefetch>(half, blk); // chunks multiplied
+  const float* kbase = (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k + (int64_t)hh * a.n * half;
+
+  // ---- key staging, private to each wave: chunk c holds the wave's 16 key
+  // rows over dims [dq*share + c*kDimChunk, +kDimChunk).  The wave loads it
+  // with whole lines (kLanesPerRow consecutive lanes per row) and transposes
+  // it through its own LDS slice into the matrix-operand layout, so waves
+  // never wait for each other inside the contraction.  kPrefetch chunks are
+  // in flight in a register ring; every ring load is issued (chunks past the
+  // end read a valid address and are masked to zero), so the loop body is
+  // the same each time and the compiler waits only for the chunk it stores.
+  float* wbuf = kst + wave * 2 * 16 * kKPitch;           // [2][16][kKPitch]
+  float4 stg[kPrefetch][kStageF4];
+  // per-lane parts of the staging addresses, fixed for the whole loop.  Rows
+  // past n read row 0 instead (their scores are discarded); dims past the
+  // share or d_h are masked to zero, so they add nothing to a dot product
+  // or a norm.
+  const int lane_ds = (lane % kLanesPerRow) * 4;                 // dim offset inside a chunk
+  const int ds_lim = min(share, half - dq * share);              // dims of this share that exist
+  int lane_off[kStageF4];
 #pragma unroll
-    for (int j = 0; j < kStepGroup; ++j) {
-      const int d = step_dim(s0 + j);
-      const bool ok = s0 + j < steps && d < half;
-      dst[j] = (ok && kvalid) ? *reinterpret_cast<const float4*>(krow + d)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < kStageF4; ++j) {
+    const int gk = kb * blk + kt * 16 + j * kRowsPerLoad + lane / kLanesPerRow;
+    lane_off[j] = (gk < a.n ? gk : 0) * half + min(dq * share + lane_ds, half - 4);
+  }
+  auto stage_load = [&](float4 (&dst)[kStageF4], int c) {
+    const bool ok = c < nchunks && c * kDimChunk + lane_ds < ds_lim;
+    const unsigned int m = ok ? 0xFFFFFFFFu : 0u;    // masked, so the load is never skipped
+    const int cofs = ok ? c * kDimChunk : 0;
+#pragma unroll
+    for (int j = 0; j < kStageF4; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(kbase + lane_off[j] + cofs);
+      dst[j] = make_float4(__uint_as_float(__float_as_uint(v.x) & m), __uint_as_float(__float_as_uint(v.y) & m),
+                           __uint_as_float(__float_as_uint(v.z) & m), __uint_as_float(__float_as_uint(v.w) & m));
     }
   };
-  float4 ak0[kStepGroup], ak1[kStepGroup];
-  load_group(ak0, 0);
+  auto stage_store = [&](const float4 (&src)[kStageF4], int c) {
+    float* buf = wbuf + (c & 1) * 16 * kKPitch;
+#pragma unroll
+    for (int j = 0; j < kStageF4; ++j) {
+      const int r = j * kRowsPerLoad + lane / kLanesPerRow;
+      *reinterpret_cast<float4*>(&buf[r * kKPitch + (lane % kLanesPerRow) * 4]) = src[j];
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kPrefetch; ++i) stage_load(stg[i], i);   // in flight while queries are staged
 
   // ---- stage the 16-token query tile (this half) in LDS
   const int half4 = half >> 2;
-  for (int e = tid; e < kTokTile * half4; e += kScoreWaves * kWave) {
-    const int r = e / half4, c4 = e - r * half4;
+  const int qw4 = qwidth >> 2;
+  for (int e = tid; e < kTokTile * qw4; e += kScoreWaves * kWave) {
+    const int r = e / qw4, c4 = e - r * qw4;
     const int t = t0 + r;
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < a.T) {
+    if (t < a.T && c4 < half4) {
       const float* qrow = a.q + ((int64_t)(b * a.T + t) * a.H + hh) * a.dqk + h * half;
       x = reinterpret_cast<const float4*>(qrow)[c4];
     }
     *reinterpret_cast<float4*>(&qs[r * qpitch + c4 * 4]) = x;
   }
+  stage_store(stg[0], 0);
+  stage_load(stg[0], kPrefetch);
   __syncthreads();
 
   // ---- query norms (fp64 sums), once per token and half; wave w <-> token w
@@ -129,32 +205,41 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   }
 
   // ---- scores.  Two independent accumulator chains (x,y and z,w components
-  // of each step); a group's key operands are requested just before it runs.
+  // of each step); one barrier per staged chunk.
   v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
-  double ksq = 0.0;
-  auto mfma_group = [&](const float4 (&ak)[kStepGroup], int s0) {
+  float ksq = 0.f;     // key norm partial (fp32: its rounding is far below the dot product's)
+  const float* arow_base = &qs[row * qpitch + dq * share];
+  auto mfma_chunk = [&](int c) {
+    const float* krow_s = wbuf + (c & 1) * 16 * kKPitch + row * kKPitch;
 #pragma unroll
-    for (int j = 0; j < kStepGroup; ++j) {
-      const int d = step_dim(s0 + j);
-      const bool ok = s0 + j < steps && d < half;
-      const float4 bq = ok ? *reinterpret_cast<const float4*>(&qs[row * qpitch + d])
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-      ksq += (double)ak[j].x * ak[j].x + (double)ak[j].y * ak[j].y +
-             (double)ak[j].z * ak[j].z + (double)ak[j].w * ak[j].w;
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[j].x, bq.x, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[j].z, bq.z, acc1, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[j].y, bq.y, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[j].w, bq.w, acc1, 0, 0, 0);
+    for (int j = 0; j < kDimChunk / 16; ++j) {
+      // staged key dims outside this share (or past d_h) are zero, so the
+      // query operand is read unguarded from the zero-padded row
+      const int ds = (c * (kDimChunk / 16) + j) * 16 + quad * 4;   // dim inside the share
+      const float4 ak = *reinterpret_cast<const float4*>(&krow_s[j * 16 + quad * 4]);
+      const float4 bq = *reinterpret_cast<const float4*>(&arow_base[ds]);
+      ksq = fmaf(ak.x, ak.x, ksq); ksq = fmaf(ak.y, ak.y, ksq);
+      ksq = fmaf(ak.z, ak.z, ksq); ksq = fmaf(ak.w, ak.w, ksq);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.x, bq.x, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.z, bq.z, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.y, bq.y, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.w, bq.w, acc1, 0, 0, 0);
     }
   };
-  for (int s0 = 0; s0 < steps; s0 += 2 * kStepGroup) {
-    mfma_group(ak0, s0);
-    if (s0 + kStepGroup < steps) {
-      load_group(ak1, s0 + kStepGroup);
-      mfma_group(ak1, s0 + kStepGroup);
+  // chunk c lives in ring slot c % kPrefetch until it is copied to the
+  // wave's LDS buffer c & 1 (during chunk c - 1); the slot is then refilled
+  // with chunk c + kPrefetch.  A wave's LDS operations complete in order, so
+  // buffer c & 1 is rewritten only after chunk c - 2's reads of it.
+  for (int c0 = 0; c0 < nchunks_p; c0 += kPrefetch) {
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) {
+      const int c = c0 + i;
+      mfma_chunk(c);
+      stage_store(stg[(i + 1) % kPrefetch], c + 1);
+      stage_load(stg[(i + 1) % kPrefetch], c + 1 + kPrefetch);
     }
-    if (s0 + 2 * kStepGroup < steps) load_group(ak0, s0 + 2 * kStepGroup);
   }
+  __syncthreads();     // the score buffers below reuse every wave's staging slice
   ksq += xor_lane<16>(ksq);
   ksq += xor_lane<32>(ksq);
   // acc[r] = dim-share sum of K[key 4*quad + r of the tile] . Q[token row]
@@ -264,12 +349,17 @@ int score_key_block(int units, int tokens, int n) {
   return blk;
 }
 
+template <int kDimChunk, int kPrefetch>
 size_t ka_smem_bytes(int half, int blk) {
+  constexpr int kKPitch = kDimChunk + 4;
   const int ndq = kScoreWaves / (blk / 16);
-  return sizeof(float) * kTokTile * (half + 4)                       // queries
-         + sizeof(float) * ndq * kTokTile * (blk + 1)                // dim-share partials / scores
-         + sizeof(double) * ndq * blk                                // key-norm partials
-         + sizeof(skey) * kTokTile * blk;                            // filter survivors
+  // dim-share partials / scores and the filter survivors reuse the two key
+  // staging buffers once the contraction is done
+  static_assert(sizeof(float) * 4 * kTokTile * (64 + 1) <= sizeof(float) * kStageRows * kKPitch, "partials");
+  static_assert(sizeof(skey) * kTokTile * kMaxBlk <= sizeof(float) * kStageRows * kKPitch, "survivors");
+  return sizeof(float) * kTokTile * (ka_query_width<kDimChunk, kPrefetch>(half, blk) + 4)   // queries
+         + 2 * sizeof(float) * kStageRows * kKPitch                  // staged keys (double buffer)
+         + sizeof(double) * ndq * blk;                               // key-norm partials
 }
 
 int ka_grid(const ChunkArgs& a) {
@@ -278,13 +368,30 @@ int ka_grid(const ChunkArgs& a) {
   return 8 * ((total + 7) / 8);
 }
 
-hipError_t launch_ka(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
+namespace {
+
+constexpr size_t kLdsBytes = 160 * 1024;
+
+template <int DC, int PF>
+hipError_t launch_ka_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&ka_score_topk), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)std::max(ka_smem_bytes(FWPKM_MAX_HALF_DIM, 64), ka_smem_bytes(FWPKM_MAX_HALF_DIM, kMaxBlk)));
+      reinterpret_cast<const void*>(&ka_score_topk<DC, PF>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)kLdsBytes);
   if (attr != hipSuccess) return attr;
-  return fw_launch(ka_score_topk, dim3(ka_grid(a)), dim3(kScoreWaves * kWave),
-                   (uint32_t)ka_smem_bytes(a.half, a.key_block), s, tm, a);
+  return fw_launch(ka_score_topk<DC, PF>, dim3(ka_grid(a)), dim3(kScoreWaves * kWave),
+                   (uint32_t)ka_smem_bytes<DC, PF>(a.half, a.key_block), s, tm, a);
+}
+
+}  // namespace
+
+hipError_t launch_ka(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
+  // wider chunks halve the barriers per contraction; they fit for d_h <= 256.
+  // A ring deeper than the chunk count would only multiply zeros.
+  if (ka_smem_bytes<64, 2>(a.half, a.key_block) <= kLdsBytes) {
+    if (ka_chunks<64, 1>(a.half, a.key_block) == 1) return launch_ka_as<64, 1>(a, s, tm);
+    return launch_ka_as<64, 2>(a, s, tm);
+  }
+  return launch_ka_as<32, 4>(a, s, tm);
 }
 
 }  // namespace fwpkm
