@@ -362,6 +362,8 @@ int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targ
   a.region_bits = 0;
   while ((1 << a.region_bits) < a.regions) ++a.region_bits;
   a.pw = std::max(c.dim_v, half);
+  a.npr = 0;
+  for (int i = 0; i < k; ++i) a.npr += k / (i + 1);
 
   const bool write = lr != 0.0f;
   using fwpkm::LaunchTiming;

@@ -66,6 +66,7 @@ struct ChunkArgs {
   int regions;     // hash regions per (list, unit), a power of two
   int region_bits; // log2(regions)
   int pw;          // floats per row = max(d_v, d_h)
+  int npr;         // Cartesian candidates (i, j) with (i+1)(j+1) <= k: sum_i floor(k/(i+1))
 };
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

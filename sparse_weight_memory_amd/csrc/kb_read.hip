@@ -90,26 +90,34 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   }
 
   // ---- 2. pruned Cartesian candidates, then the k best
-  int npr = 0;
-  for (int i = 0; i < k; ++i) npr += k / (i + 1);
+  const int npr = a.npr;
+  // floor(k / (i + 1)) without an integer divide: (k + 1/2) / (i + 1) lies at
+  // least 1/66 away from an integer, far more than the reciprocal's error
+  const float kh = (float)k + 0.5f;
+  auto row_len = [&](int i) { return (int)(kh * __builtin_amdgcn_rcpf((float)(i + 1))); };
   skey sel;
   {
     constexpr int J = 3;   // sum_i floor(32/i) = 130 <= 3 * 64
+    const int jr = (npr + kWave - 1) / kWave;   // rounds that hold candidates (1 for k <= 20)
     skey cx[J];
 #pragma unroll
     for (int r = 0; r < J; ++r) {
+      cx[r] = kEmptyKey;
+      if (r >= jr) continue;                     // wave-uniform
       int c = lane + 64 * r;
       const bool in = c < npr;
       int i = 0;
       if (in) {
-        while (c >= k / (i + 1)) { c -= k / (i + 1); ++i; }
+        for (int len = row_len(0); c >= len; len = row_len(i)) { c -= len; ++i; }
       }
       const int j = in ? c : 0;
       const skey ka = __shfl(hk[0], i, kWave);
       const skey kb = __shfl(hk[1], j, kWave);
       const int ia = key_index(ka), ib = key_index(kb);
+      // tie-break index (a << 12) | b orders exactly as the slot a*n + b does
+      // (b < n <= 4096) and gives a and b back without a divide
       cx[r] = (in && ia != kNoIndex && ib != kNoIndex)
-                  ? pack_key(order_key(key_value(ka) + key_value(kb)), ia * n + ib)
+                  ? pack_key(order_key(key_value(ka) + key_value(kb)), (ia << 12) | ib)
                   : kEmptyKey;
     }
     if (npr <= 16) {
@@ -136,7 +144,8 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
     }
   }
   const float sel_o = key_value(sel);
-  const int sel_s = sel == kEmptyKey ? kNoIndex : key_index(sel);
+  const int sel_ab = key_index(sel);                          // (a << 12) | b
+  const int sel_s = sel == kEmptyKey ? kNoIndex : (sel_ab >> 12) * n + (sel_ab & 4095);
 
   // ---- 3. weights (lanes m < k)
   const int64_t N = (int64_t)n * n;
@@ -266,8 +275,8 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   const float c = (a.mode == 0) ? 2.0f * delta * uinv : delta;
 
   // ---- 6. pair lists: V (slot), K1 (row a), K2 (row b), merged per token
-  const int am = active ? sel_s / n : n;
-  const int bm = active ? sel_s - am * n : n;
+  const int am = active ? sel_ab >> 12 : n;
+  const int bm = active ? sel_ab & 4095 : n;
   float sum1 = 0.f, sum2 = 0.f;
   bool first1 = true, first2 = true;
   for (int m = 0; m < k; ++m) {
