@@ -51,6 +51,15 @@ The next chunk reads the new weights [gist.science section 2, Causality
 Preservation: updates applied after the chunk; predictions inside a chunk use
 only earlier chunks' fast weights].
 
+Token importance (optional) [sciencestack.ai contents: "Weighting MSE loss by
+token importance"; how the weights are produced is not on the pages]: with
+per-token weights lambda_t the loss is L = sum_t lambda_t/2 ||out_t - y_t||^2,
+so every gradient of token t is scaled by lambda_t (g_t -> lambda_t g_t), and
+a token with lambda_t = 0 reads but does not write: it is left out of the row
+sums and of the token counts W3 divides by (a masked token, such as the last
+one of a sequence, which has no lookahead target).  All weights 1 is the
+unweighted step.
+
 Dot-product scoring, the standard-PKM alternative the summary contrasts IDW
 with, is also provided: s = q1.K1[a] + q2.K2[b], best = largest, and
 ds/dK1[a] = q1.
@@ -230,12 +239,15 @@ def _sum_by_row(rows: np.ndarray, tokens: np.ndarray, contrib: np.ndarray):
     return uniq, sums, counts
 
 
-def chunk_gradients(k1, k2, v, q, y, slots, values, weights, eps=1e-3, mode=IDW):
+def chunk_gradients(k1, k2, v, q, y, slots, values, weights, eps=1e-3, mode=IDW,
+                    token_weights=None):
     """W1-W2 summed per row, with the token counts W3 divides by.
 
     Returns {"v"|"k1"|"k2": (rows, summed gradient [rows, d], token counts)}
-    where the summed gradient is dL/dtheta_r for L = sum_t 1/2||out_t - y_t||^2
-    at the given (fixed) selection.
+    where the summed gradient is dL/dtheta_r for
+    L = sum_t lambda_t/2 ||out_t - y_t||^2 at the given (fixed) selection
+    (lambda = token_weights [C], default all 1); tokens with lambda_t = 0 are
+    left out of the sums and the counts.
     """
     n, half = k1.shape
     C, k = slots.shape
@@ -245,6 +257,8 @@ def chunk_gradients(k1, k2, v, q, y, slots, values, weights, eps=1e-3, mode=IDW)
     w = weights
     out = _weighted_rows(w, vsel)
     g = out - np.asarray(y, np.float64)                        # W1
+    lam = np.ones(C) if token_weights is None else np.asarray(token_weights, np.float64)
+    g = lam[:, None] * g                                       # dL/d out_t
     gv = np.einsum("cd,ckd->ck", g, vsel)
     gout = np.einsum("cd,cd->c", g, out)
     delta = w * (gv - gout[:, None])                           # dL_t/ds_m
@@ -262,17 +276,20 @@ def chunk_gradients(k1, k2, v, q, y, slots, values, weights, eps=1e-3, mode=IDW)
     else:
         gK1 = (delta[:, :, None] * np.broadcast_to(q1[:, None, :], (C, k, half))).reshape(C * k, -1)
         gK2 = (delta[:, :, None] * np.broadcast_to(q2[:, None, :], (C, k, half))).reshape(C * k, -1)
+    keep = lam[tok] != 0.0                                     # pairs of writing tokens
     return {
-        "v": _sum_by_row(slots.reshape(-1), tok, gV),
-        "k1": _sum_by_row(a.reshape(-1), tok, gK1),
-        "k2": _sum_by_row(b.reshape(-1), tok, gK2),
+        "v": _sum_by_row(slots.reshape(-1)[keep], tok[keep], gV[keep]),
+        "k1": _sum_by_row(a.reshape(-1)[keep], tok[keep], gK1[keep]),
+        "k2": _sum_by_row(b.reshape(-1)[keep], tok[keep], gK2[keep]),
     }
 
 
-def unit_chunk(k1, k2, v, q, y, lr, k, eps=1e-3, mode=IDW, override=None) -> UnitChunkResult:
+def unit_chunk(k1, k2, v, q, y, lr, k, eps=1e-3, mode=IDW, override=None,
+               token_weights=None) -> UnitChunkResult:
     """Read, then (if lr != 0) the aggregated SGD step, for one unit.
 
-    k1, k2 [n, d_h] fp32; v [n*n, d_v] fp32; q [C, 2 d_h]; y [C, d_v].
+    k1, k2 [n, d_h] fp32; v [n*n, d_v] fp32; q [C, 2 d_h]; y [C, d_v];
+    token_weights [C] or None (all 1).
     The tables are not modified; the new values of every touched row are
     returned in ``updates`` (rounded to fp32).
     """
@@ -282,7 +299,7 @@ def unit_chunk(k1, k2, v, q, y, lr, k, eps=1e-3, mode=IDW, override=None) -> Uni
                           overridden=ex["overridden"], updates=None)
     if lr == 0.0:
         return res
-    grads = chunk_gradients(k1, k2, v, q, y, slots, vals, w, eps, mode)
+    grads = chunk_gradients(k1, k2, v, q, y, slots, vals, w, eps, mode, token_weights)
     updates = {}
     for name, table in (("v", v), ("k1", k1), ("k2", k2)):
         rows, sums, counts = grads[name]
@@ -308,12 +325,13 @@ def apply_updates(k1, k2, v, updates) -> None:
 def forward_chunk(state: dict, queries: np.ndarray, targets: np.ndarray, lr: float,
                   k: int, eps: float = 1e-3, mode: str = IDW,
                   overrides: Optional[Dict[int, Dict[int, Sequence[int]]]] = None,
-                  inplace: bool = False):
+                  inplace: bool = False, token_weights: Optional[np.ndarray] = None):
     """One chunk over every unit.
 
     state: {"k1": [U, n, d_h], "k2": [U, n, d_h], "v": [U, n*n, d_v]} fp32,
            unit u = b*H + h.
-    queries [B, C, H, d_qk], targets [B, C, H, d_v].
+    queries [B, C, H, d_qk], targets [B, C, H, d_v], token_weights [B, C, H]
+    or None (all 1).
     overrides: {u: {t: slot set}} selections imposed on given tokens.
     Returns (retrieved [B, C, H, d_v] float64, next state, per-unit results).
     With inplace=False the input state is left as it was.
@@ -327,8 +345,9 @@ def forward_chunk(state: dict, queries: np.ndarray, targets: np.ndarray, lr: flo
             u = b * H + h
             ov = overrides.get(u) if overrides else None
             # every unit reads the state as it was before this chunk
+            tw = None if token_weights is None else token_weights[b, :, h]
             r = unit_chunk(state["k1"][u], state["k2"][u], state["v"][u],
-                           queries[b, :, h], targets[b, :, h], lr, k, eps, mode, ov)
+                           queries[b, :, h], targets[b, :, h], lr, k, eps, mode, ov, tw)
             retrieved[b, :, h] = r.retrieved
             results.append(r)
     if lr != 0.0:
