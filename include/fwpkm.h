@@ -150,6 +150,30 @@ int fwpkm_forward_chunk(fwpkm_handle* h,
                         float* retrieved, int32_t* out_slots, float* out_weights,
                         hipStream_t stream);
 
+/* fwpkm_forward_chunk with per-token importance weights on the memorisation
+ * loss [sciencestack.ai "Fast-weight Product Key Memory", contents entry
+ * "Weighting MSE loss by token importance"]:
+ *
+ *   token_weights  nullable [batch, tokens, H] fp32, finite.  Token t's loss
+ *                  becomes lambda_t/2 ||retrieved_t - target_t||^2, so its
+ *                  gradients are scaled by lambda_t; a token with
+ *                  lambda_t == 0 is read (retrieved, out_slots, out_weights
+ *                  as usual) but writes nothing and is not counted in the
+ *                  per-row mean (e.g. the last token of a sequence, which
+ *                  has no lookahead target).  NULL means every weight is 1:
+ *                  the call is then exactly fwpkm_forward_chunk.
+ *
+ * Every other argument, the aliasing rules (token_weights is an input: it
+ * must not overlap retrieved or next_state) and the return codes are those
+ * of fwpkm_forward_chunk. */
+int fwpkm_forward_chunk_weighted(fwpkm_handle* h,
+                                 const float* queries, const float* targets,
+                                 const float* token_weights,
+                                 int32_t batch, int32_t tokens, float lr,
+                                 const fwpkm_state* past_state, const fwpkm_state* next_state,
+                                 float* retrieved, int32_t* out_slots, float* out_weights,
+                                 hipStream_t stream);
+
 /* Release the handle and its workspace (synchronises the device before the
  * workspace is freed).  NULL-safe. */
 void fwpkm_destroy(fwpkm_handle* h);

@@ -33,6 +33,7 @@ EXPORTS = (
     "fwpkm_create",
     "fwpkm_workspace_bytes",
     "fwpkm_forward_chunk",
+    "fwpkm_forward_chunk_weighted",
     "fwpkm_destroy",
     "fwpkm_last_error",
     "fwpkm_profile_enable",
@@ -96,6 +97,18 @@ def load() -> ctypes.CDLL:
         ctypes.c_void_p,                       # stream
     ]
     lib.fwpkm_forward_chunk.restype = ctypes.c_int
+    lib.fwpkm_forward_chunk_weighted.argtypes = [
+        ctypes.c_void_p,                       # handle
+        ctypes.c_void_p, ctypes.c_void_p,      # queries, targets
+        ctypes.c_void_p,                       # token_weights (nullable)
+        ctypes.c_int32, ctypes.c_int32,        # batch, tokens
+        ctypes.c_float,                        # lr
+        ctypes.POINTER(CState), ctypes.POINTER(CState),
+        ctypes.c_void_p,                       # retrieved
+        ctypes.c_void_p, ctypes.c_void_p,      # out_slots, out_weights
+        ctypes.c_void_p,                       # stream
+    ]
+    lib.fwpkm_forward_chunk_weighted.restype = ctypes.c_int
     lib.fwpkm_destroy.argtypes = [ctypes.c_void_p]
     lib.fwpkm_destroy.restype = None
     lib.fwpkm_last_error.argtypes = []

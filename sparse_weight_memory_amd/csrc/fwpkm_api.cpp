@@ -169,6 +169,31 @@ int fwpkm_create(const fwpkm_config* cfg, fwpkm_handle** out) {
   return FWPKM_OK;
 }
 
+// validation and enqueue shared by both chunk entry points (below)
+static int forward_impl(fwpkm_handle* h, const float* queries, const float* targets,
+                        const float* token_weights, int32_t batch, int32_t tokens, float lr,
+                        const fwpkm_state* past, const fwpkm_state* next,
+                        float* retrieved, int32_t* out_slots, float* out_weights,
+                        hipStream_t stream);
+
+int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targets,
+                        int32_t batch, int32_t tokens, float lr,
+                        const fwpkm_state* past, const fwpkm_state* next,
+                        float* retrieved, int32_t* out_slots, float* out_weights,
+                        hipStream_t stream) {
+  return forward_impl(h, queries, targets, nullptr, batch, tokens, lr, past, next, retrieved,
+                      out_slots, out_weights, stream);
+}
+
+int fwpkm_forward_chunk_weighted(fwpkm_handle* h, const float* queries, const float* targets,
+                                 const float* token_weights, int32_t batch, int32_t tokens,
+                                 float lr, const fwpkm_state* past, const fwpkm_state* next,
+                                 float* retrieved, int32_t* out_slots, float* out_weights,
+                                 hipStream_t stream) {
+  return forward_impl(h, queries, targets, token_weights, batch, tokens, lr, past, next, retrieved,
+                      out_slots, out_weights, stream);
+}
+
 void fwpkm_destroy(fwpkm_handle* h) {
   if (!h) return;
   if (h->ws) {
@@ -218,8 +243,8 @@ int fwpkm_profile_read(fwpkm_handle* h, double* ms, int64_t* launches) {
   return FWPKM_OK;
 }
 
-int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targets,
-                        int32_t batch, int32_t tokens, float lr,
+static int forward_impl(fwpkm_handle* h, const float* queries, const float* targets,
+                        const float* token_weights, int32_t batch, int32_t tokens, float lr,
                         const fwpkm_state* past, const fwpkm_state* next,
                         float* retrieved, int32_t* out_slots, float* out_weights,
                         hipStream_t stream) {
@@ -268,19 +293,22 @@ int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targ
   const Range rq = {reinterpret_cast<uintptr_t>(queries), reinterpret_cast<uintptr_t>(queries + rows * c.dim_qk)};
   const Range ry = {reinterpret_cast<uintptr_t>(targets), reinterpret_cast<uintptr_t>(targets + rows * c.dim_v)};
   const Range rr = {reinterpret_cast<uintptr_t>(retrieved), reinterpret_cast<uintptr_t>(retrieved + rows * c.dim_v)};
+  const Range rw = {reinterpret_cast<uintptr_t>(token_weights),
+                    reinterpret_cast<uintptr_t>(token_weights + (token_weights ? rows : 0))};
   const Range outs[3] = {rr,
                          {reinterpret_cast<uintptr_t>(out_slots), reinterpret_cast<uintptr_t>(out_slots + (out_slots ? rows * k : 0))},
                          {reinterpret_cast<uintptr_t>(out_weights), reinterpret_cast<uintptr_t>(out_weights + (out_weights ? rows * k : 0))}};
-  const Range ins[8] = {rq, ry, pk1, pk2, pv, nk1, nk2, nv};
+  const Range ins[9] = {rq, ry, pk1, pk2, pv, nk1, nk2, nv, rw};
   for (int i = 0; i < 3; ++i) {
     if (outs[i].lo == outs[i].hi) continue;
     for (const Range& b : ins)
-      if (overlap(outs[i], b)) return fail(FWPKM_ERR_ALIAS, "an output overlaps an input or the state");
+      if (b.lo != b.hi && overlap(outs[i], b)) return fail(FWPKM_ERR_ALIAS, "an output overlaps an input or the state");
     for (int j = i + 1; j < 3; ++j)
       if (outs[j].lo != outs[j].hi && overlap(outs[i], outs[j])) return fail(FWPKM_ERR_ALIAS, "outputs overlap each other");
   }
   for (const Range& b : {nk1, nk2, nv})
-    if (overlap(b, rq) || overlap(b, ry)) return fail(FWPKM_ERR_ALIAS, "next_state overlaps queries or targets");
+    if (overlap(b, rq) || overlap(b, ry) || (rw.lo != rw.hi && overlap(b, rw)))
+      return fail(FWPKM_ERR_ALIAS, "next_state overlaps queries, targets or token weights");
 
   // ---------------------------------------------------------- workspace
   int dev = -1;
@@ -339,6 +367,7 @@ int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targ
   a.lr = lr;
   a.q = queries;
   a.y = targets;
+  a.tw = token_weights;
   a.k1 = next->k1;
   a.k2 = next->k2;
   a.v = next->v;

@@ -39,6 +39,7 @@ struct ChunkArgs {
   // inputs
   const float* q;   // [B, T, H, dqk]
   const float* y;   // [B, T, H, dv]
+  const float* tw;  // nullable [B, T, H] token-importance weights (null = all 1)
   // state (tables the chunk reads; the update writes the same tables)
   float* k1;
   float* k2;

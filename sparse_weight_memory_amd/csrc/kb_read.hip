@@ -25,7 +25,10 @@
 // Candidates of one token that share a K1 (K2) row are merged into one
 // (row, token) pair here, so that the update divides by the number of
 // tokens touching the row [gist.science section 2, gradient aggregation by
-// averaging].
+// averaging].  With token-importance weights lambda_t [sciencestack.ai
+// contents: "Weighting MSE loss by token importance"] the loss of token t is
+// lambda_t/2 ||out_t - y_t||^2: g_t is scaled by lambda_t, and a token with
+// lambda_t = 0 emits no pairs (it reads only and is not counted).
 //
 // The k value rows are fetched as float4 per lane (coalesced 1 KiB per
 // wave-load) and kept in registers for the backward when they fit.
@@ -53,6 +56,8 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
 
   // loads that do not depend on the selection go out first
   const float qn = (a.mode == 0) ? a.qnorm[ut * 2] + a.qnorm[ut * 2 + 1] : 0.f;
+  // token-importance weight of this token's loss; 0 = read only, no write
+  const float lam = (WRITE && a.tw) ? a.tw[io] : 1.0f;
   float4 yv[VR];
 #pragma unroll
   for (int j = 0; j < VR; ++j) {
@@ -234,7 +239,8 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
     g[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < dv4) {
       const float4 yy = yv[j];
-      g[j] = make_float4(acc[j].x - yy.x, acc[j].y - yy.y, acc[j].z - yy.z, acc[j].w - yy.w);
+      g[j] = make_float4(lam * (acc[j].x - yy.x), lam * (acc[j].y - yy.y),
+                         lam * (acc[j].z - yy.z), lam * (acc[j].w - yy.w));
       gw[c] = g[j];
       gout += g[j].x * acc[j].x + g[j].y * acc[j].y + g[j].z * acc[j].z + g[j].w * acc[j].w;
     }
@@ -289,10 +295,11 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   if (lane < k) {
     const int64_t p = (int64_t)u * a.P + (int64_t)t * k + lane;
     const int64_t UP = (int64_t)a.U * a.P;
-    a.keys[p] = active ? sel_s : (int)N;   // N marks "no slot"; it sorts last
+    const bool writes = active && lam != 0.f;   // a zero-weight token only reads
+    a.keys[p] = writes ? sel_s : (int)N;   // N marks "no slot"; it sorts last
     a.sel_w[p] = w;
-    const bool k1ok = active && first1;
-    const bool k2ok = active && first2;
+    const bool k1ok = writes && first1;
+    const bool k2ok = writes && first2;
     a.keys[UP + p] = k1ok ? am : n;
     a.keys[2 * UP + p] = k2ok ? bm : n;
     a.coef[p] = k1ok ? sum1 : 0.f;

@@ -148,12 +148,15 @@ class Memory:
 
     def forward_chunk(self, queries: torch.Tensor, targets: torch.Tensor, lr: float,
                       past: State, next: Optional[State] = None,
-                      return_selection: bool = False, retrieved: Optional[torch.Tensor] = None):
+                      return_selection: bool = False, retrieved: Optional[torch.Tensor] = None,
+                      token_weights: Optional[torch.Tensor] = None):
         """One chunk: (retrieved [B, T, H, d_v], next state) from past state.
 
         queries [B, T, H, d_qk] (or [B, T, d_qk] when H == 1), targets likewise
         with d_v.  next=None allocates per-sequence tables and fills them
-        (functional update); next=past updates in place.
+        (functional update); next=past updates in place.  token_weights
+        [B, T, H] (or [B, T] when H == 1) scales each token's loss; a weight
+        of 0 reads without writing (fwpkm_forward_chunk_weighted).
         """
         cfg = self.cfg
         _check_tensor("queries", queries)
@@ -176,12 +179,21 @@ class Memory:
             slots = torch.empty((B, T, cfg.num_heads, cfg.topk), device=queries.device, dtype=torch.int32)
             weights = torch.empty((B, T, cfg.num_heads, cfg.topk), device=queries.device)
         stream = torch.cuda.current_stream(queries.device).cuda_stream
-        rc = self._lib.fwpkm_forward_chunk(
-            self._h, queries.data_ptr(), targets.data_ptr(), B, T, float(lr),
-            ctypes.byref(c_past), ctypes.byref(c_next), retrieved.data_ptr(),
-            slots.data_ptr() if slots is not None else None,
-            weights.data_ptr() if weights is not None else None,
-            stream)
+        sel_ptrs = (slots.data_ptr() if slots is not None else None,
+                    weights.data_ptr() if weights is not None else None)
+        if token_weights is None:
+            rc = self._lib.fwpkm_forward_chunk(
+                self._h, queries.data_ptr(), targets.data_ptr(), B, T, float(lr),
+                ctypes.byref(c_past), ctypes.byref(c_next), retrieved.data_ptr(),
+                *sel_ptrs, stream)
+        else:
+            _check_tensor("token_weights", token_weights)
+            if token_weights.numel() != B * T * cfg.num_heads or token_weights.shape[:2] != queries.shape[:2]:
+                raise ValueError("token_weights must be [B, T, H]")
+            rc = self._lib.fwpkm_forward_chunk_weighted(
+                self._h, queries.data_ptr(), targets.data_ptr(), token_weights.data_ptr(),
+                B, T, float(lr), ctypes.byref(c_past), ctypes.byref(c_next),
+                retrieved.data_ptr(), *sel_ptrs, stream)
         if rc != _lib.OK:
             raise FwPKMError(rc, _lib.last_error())
         if return_selection:

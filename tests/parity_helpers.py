@@ -64,8 +64,9 @@ def state_to_host(s, units=None):
     return out
 
 
-def oracle_units(state, q, y, lr, k, eps, mode, units, H, overrides=None):
+def oracle_units(state, q, y, lr, k, eps, mode, units, H, overrides=None, tw=None):
     """Run the oracle on the given units only (state holds those units, in order).
+    tw: token weights [B, C, H] or None.
 
     Returns (retrieved {u: [C, d_v]}, new state (same unit order), results).
     """
@@ -75,7 +76,7 @@ def oracle_units(state, q, y, lr, k, eps, mode, units, H, overrides=None):
         b, h = divmod(u, H)
         ov = overrides.get(u) if overrides else None
         r = O.unit_chunk(state["k1"][i], state["k2"][i], state["v"][i], q[b, :, h], y[b, :, h],
-                         lr, k, eps, mode, ov)
+                         lr, k, eps, mode, ov, None if tw is None else tw[b, :, h])
         rets[u] = r.retrieved
         results[u] = r
         if r.updates:
@@ -118,8 +119,9 @@ def assert_close(name, got, want, rtol, atol):
 
 
 def compare_chunk(mem, st_host, q, y, lr, units=None, rtol=RTOL_CHUNK, atol=ATOL_CHUNK,
-                  label=""):
-    """Teacher-forced parity of one chunk starting from st_host (all units).
+                  label="", tw=None):
+    """Teacher-forced parity of one chunk starting from st_host (all units);
+    tw = token weights [B, C, H] (numpy) or None.
 
     Returns (oracle next state for `units`, near-tie count, GPU next State).
     """
@@ -131,7 +133,8 @@ def compare_chunk(mem, st_host, q, y, lr, units=None, rtol=RTOL_CHUNK, atol=ATOL
     qd, yd = to_dev(q), to_dev(y)
     say(label, "gpu chunk", dict(B=B, C=C, H=H, n=cfg.sqrt_slots, k=cfg.topk, lr=lr))
     ret, nxt, slots, weights = mem.forward_chunk(qd, yd, lr, dev_state, next=dev_state,
-                                                 return_selection=True)
+                                                 return_selection=True,
+                                                 token_weights=None if tw is None else to_dev(tw))
     torch.cuda.synchronize()
     ret = ret.cpu().numpy()
     slots = slots.cpu().numpy()
@@ -139,10 +142,11 @@ def compare_chunk(mem, st_host, q, y, lr, units=None, rtol=RTOL_CHUNK, atol=ATOL
     sub = {name: a[units] for name, a in st_host.items()}
     mode = mode_name(cfg.score_mode)
     say(label, "oracle on units", units[:8], "..." if len(units) > 8 else "")
-    rets, new, results = oracle_units(sub, q, y, lr, cfg.topk, cfg.eps, mode, units, H)
+    rets, new, results = oracle_units(sub, q, y, lr, cfg.topk, cfg.eps, mode, units, H, tw=tw)
     overrides, ties = selection_overrides(results, slots, H, units)
     if overrides:
-        rets, new, results = oracle_units(sub, q, y, lr, cfg.topk, cfg.eps, mode, units, H, overrides)
+        rets, new, results = oracle_units(sub, q, y, lr, cfg.topk, cfg.eps, mode, units, H,
+                                          overrides, tw=tw)
     for u in units:
         b, h = divmod(u, H)
         assert_close(f"{label} retrieved u{u}", ret[b, :, h], rets[u], rtol, atol)

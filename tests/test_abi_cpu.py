@@ -170,3 +170,30 @@ def test_valid_call_without_gpu_reports_hip_error(fwpkm_lib, handle):
     rc = fwd(fwpkm_lib, handle, past=state(PK1, PK2, PV, 0, 0), nxt=state(NK1, NK2, NV))
     assert rc == _lib.ERR_HIP
     assert "hipGetDevice" in fwpkm_lib.fwpkm_last_error().decode()
+
+
+# --------------------------------------------------- token-weighted entry
+TW = 0xB0_0000_0000   # [batch, tokens, H] fp32 weights (fake address)
+
+
+def fwd_w(lib, h, tw=TW, r=R, nxt=None, batch=2, tokens=64, lr=1.0):
+    past = state(PK1, PK2, PV)
+    nxt = nxt if nxt is not None else state(PK1, PK2, PV)
+    return lib.fwpkm_forward_chunk_weighted(h, Q, Y, tw, batch, tokens, lr, ctypes.byref(past),
+                                            ctypes.byref(nxt), r, None, None, None)
+
+
+def test_weighted_entry_checks_like_the_plain_one(fwpkm_lib, handle):
+    L = fwpkm_lib
+    assert fwd_w(L, None) == _lib.ERR_INVALID_ARG
+    assert fwd_w(L, handle, batch=3) == _lib.ERR_INVALID_ARG
+    assert fwd_w(L, handle, lr=math.nan) == _lib.ERR_INVALID_ARG
+    # the weights are an input: outputs and the next state must not overlap them
+    # (2 sequences x 64 tokens x 1 head = 128 floats)
+    assert fwd_w(L, handle, r=TW + 4 * 100) == _lib.ERR_ALIAS
+    assert fwd_w(L, handle, nxt=state(NK1, NK2, TW)) == _lib.ERR_ALIAS
+    # just past the weights' end is fine (fails later, for want of a device)
+    import torch
+    if not torch.cuda.is_available():
+        assert fwd_w(L, handle, r=TW + 4 * 2 * 64) == _lib.ERR_HIP
+        assert fwd_w(L, handle, tw=None) == _lib.ERR_HIP      # NULL = all weights 1
