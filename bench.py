@@ -78,6 +78,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time spent timing the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weighted", action="store_true",
+                    help="run the token-weighted step (fwpkm_forward_chunk_weighted): weight 1 "
+                         "everywhere except 0 on the last token of every sequence, which has "
+                         "no lookahead target")
     ap.add_argument("--eager", action="store_true",
                     help="launch every chunk from Python instead of replaying a HIP graph")
     ap.add_argument("--no-profile-pass", action="store_true",
@@ -205,11 +209,18 @@ def main():
     ret = torch.empty((B, C, H, cfg.dim_v), device=dev)
     tokens_per_step = B * C * cfg.chunks
 
+    tw = None
+    if args.weighted:
+        # [chunks, B, C, H]: every token weighs 1 except each sequence's last
+        tw = torch.ones((cfg.chunks, B, C, H), device=dev)
+        tw[-1, :, -1, :] = 0.0
+
     def step(select=False):
         out = []
         for c in range(cfg.chunks):
             r = mem.forward_chunk(qd[c], yd[c], cfg.lr, st, next=st, retrieved=ret,
-                                  return_selection=select)
+                                  return_selection=select,
+                                  token_weights=None if tw is None else tw[c])
             if select:
                 out.append(r[2])
         return out
@@ -268,7 +279,8 @@ def main():
                    "slots": cfg.num_slots, "dim_qk": cfg.dim_qk, "dim_v": cfg.dim_v,
                    "topk": cfg.topk, "lr": cfg.lr, "eps": cfg.eps,
                    "parallelism": "single GPU",
-                   "launch": "eager" if graph is None else "hip graph of one step"},
+                   "launch": "eager" if graph is None else "hip graph of one step",
+                   "token_weights": "last token of each sequence 0, others 1" if args.weighted else None},
     }
 
     if not args.no_profile_pass:

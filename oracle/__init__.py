@@ -10,6 +10,7 @@ from .fwpkm_oracle import (  # noqa: F401
     IDW,
     NEAR_TIE_REL,
     UnitChunkResult,
+    addressing_gradients,
     apply_updates,
     cartesian_best,
     chunk_gradients,

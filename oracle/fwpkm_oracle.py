@@ -60,6 +60,21 @@ sums and of the token counts W3 divides by (a masked token, such as the last
 one of a sequence, which has no lookahead target).  All weights 1 is the
 unweighted step.
 
+Addressing loss (optional) [gist.science section 2, Core Architecture: an
+auxiliary loss based on negative entropy, applied to the key matrices, keeps
+slot usage balanced across a chunk; sciencestack.ai contents: "Addressing
+Optimization", "Marginal entropy loss"; repo-explainer: marginal entropy
+pressure against falling back to the same few addresses].  Reading taken
+(the pages give no formula): per half h, P_h[t, :] = softmax over all n
+sub-keys of the token's scores s_h[t, i] (the same scores R3 ranks), the
+chunk's marginal p_h = (1/C) sum_t P_h[t, :], and
+  L_addr = lambda_addr * sum_h sum_i p_h[i] log p_h[i]   (negative entropy).
+Its gradient reaches every sub-key (not only the selected ones), at the
+chunk's starting weights, and joins the same SGD step:
+  K_h[i] <- fp32(K_h[i] - eta * (mean MSE gradient of row i, if touched,
+                                  + dL_addr/dK_h[i])).
+lambda_addr = 0 (default) is the step without it.
+
 Dot-product scoring, the standard-PKM alternative the summary contrasts IDW
 with, is also provided: s = q1.K1[a] + q2.K2[b], best = largest, and
 ds/dK1[a] = q1.
@@ -284,12 +299,45 @@ def chunk_gradients(k1, k2, v, q, y, slots, values, weights, eps=1e-3, mode=IDW,
     }
 
 
+def addressing_gradients(k1, k2, q, eps=1e-3, mode=IDW, lam_addr=1.0):
+    """dL_addr/dK1, dL_addr/dK2 [n, d_h] (float64) for
+    L_addr = lam_addr * sum_h sum_i p_h[i] log p_h[i],
+    p_h = mean over the chunk's tokens of softmax_i(s_h[t, i]) over all n
+    sub-keys, s_h the R2/R3 scores.  With l_i = log p_i, the chain rule gives
+    dL/ds_h[t, j] = lam/C * P[t, j] (l_j - sum_i P[t, i] l_i)."""
+    n, half = k1.shape
+    q64 = np.asarray(q, np.float64)
+    C = q64.shape[0]
+    out = []
+    for h, K in enumerate((k1, k2)):
+        K64 = np.asarray(K, np.float64)
+        qh = q64[:, h * half:(h + 1) * half]
+        if mode == IDW:
+            d = sq_distances(qh, K64)                              # [C, n]
+            S = -np.log(eps + d)
+        else:
+            S = dot_scores(qh, K64)
+        E = np.exp(S - S.max(axis=1, keepdims=True))
+        P = E / E.sum(axis=1, keepdims=True)                       # per-token softmax
+        p = P.mean(axis=0)                                         # chunk marginal
+        ell = np.log(p)
+        G = lam_addr / C * P * (ell[None, :] - (P * ell[None, :]).sum(axis=1, keepdims=True))
+        if mode == IDW:
+            coef = G * 2.0 / (eps + d)                             # ds/dK_i = 2 (q - K_i) / (eps + d)
+            dK = coef.T @ qh - coef.sum(axis=0)[:, None] * K64
+        else:
+            dK = G.T @ qh                                          # ds/dK_i = q
+        out.append(dK)
+    return out[0], out[1]
+
+
 def unit_chunk(k1, k2, v, q, y, lr, k, eps=1e-3, mode=IDW, override=None,
-               token_weights=None) -> UnitChunkResult:
+               token_weights=None, addr_weight=0.0) -> UnitChunkResult:
     """Read, then (if lr != 0) the aggregated SGD step, for one unit.
 
     k1, k2 [n, d_h] fp32; v [n*n, d_v] fp32; q [C, 2 d_h]; y [C, d_v];
-    token_weights [C] or None (all 1).
+    token_weights [C] or None (all 1); addr_weight = lambda_addr of the
+    addressing loss (0: none; otherwise every K row is updated).
     The tables are not modified; the new values of every touched row are
     returned in ``updates`` (rounded to fp32).
     """
@@ -301,10 +349,19 @@ def unit_chunk(k1, k2, v, q, y, lr, k, eps=1e-3, mode=IDW, override=None,
         return res
     grads = chunk_gradients(k1, k2, v, q, y, slots, vals, w, eps, mode, token_weights)
     updates = {}
+    addr = {}
+    if addr_weight != 0.0:
+        addr["k1"], addr["k2"] = addressing_gradients(k1, k2, q, eps, mode, addr_weight)
     for name, table in (("v", v), ("k1", k1), ("k2", k2)):
         rows, sums, counts = grads[name]
         mean = sums / counts[:, None]                          # W3
-        new = (np.asarray(table[rows], np.float64) - lr * mean).astype(np.float32)  # W4
+        if name in addr:
+            grad = addr[name].copy()                           # every row: addressing
+            grad[rows] += mean                                 # touched rows: + MSE mean
+            rows = np.arange(table.shape[0])
+            new = (np.asarray(table, np.float64) - lr * grad).astype(np.float32)
+        else:
+            new = (np.asarray(table[rows], np.float64) - lr * mean).astype(np.float32)  # W4
         updates[name] = (rows, new)
     res.updates = updates
     return res
@@ -325,13 +382,14 @@ def apply_updates(k1, k2, v, updates) -> None:
 def forward_chunk(state: dict, queries: np.ndarray, targets: np.ndarray, lr: float,
                   k: int, eps: float = 1e-3, mode: str = IDW,
                   overrides: Optional[Dict[int, Dict[int, Sequence[int]]]] = None,
-                  inplace: bool = False, token_weights: Optional[np.ndarray] = None):
+                  inplace: bool = False, token_weights: Optional[np.ndarray] = None,
+                  addr_weight: float = 0.0):
     """One chunk over every unit.
 
     state: {"k1": [U, n, d_h], "k2": [U, n, d_h], "v": [U, n*n, d_v]} fp32,
            unit u = b*H + h.
     queries [B, C, H, d_qk], targets [B, C, H, d_v], token_weights [B, C, H]
-    or None (all 1).
+    or None (all 1); addr_weight = lambda_addr (0: no addressing loss).
     overrides: {u: {t: slot set}} selections imposed on given tokens.
     Returns (retrieved [B, C, H, d_v] float64, next state, per-unit results).
     With inplace=False the input state is left as it was.
@@ -347,7 +405,8 @@ def forward_chunk(state: dict, queries: np.ndarray, targets: np.ndarray, lr: flo
             # every unit reads the state as it was before this chunk
             tw = None if token_weights is None else token_weights[b, :, h]
             r = unit_chunk(state["k1"][u], state["k2"][u], state["v"][u],
-                           queries[b, :, h], targets[b, :, h], lr, k, eps, mode, ov, tw)
+                           queries[b, :, h], targets[b, :, h], lr, k, eps, mode, ov, tw,
+                           addr_weight)
             retrieved[b, :, h] = r.retrieved
             results.append(r)
     if lr != 0.0:
