@@ -37,6 +37,9 @@ KERNEL_SOURCES = {              # the sources that fix each kernel's code
     "read": ["kb_read.hip", "fwpkm_device.h"],
     "sort": ["kc_sort.hip", "fwpkm_device.h"],
     "update": ["kd_update.hip", "fwpkm_device.h"],
+    "addr_stats": ["ke_addr.hip", "fwpkm_device.h"],
+    "addr_grad": ["ke_addr.hip", "fwpkm_device.h"],
+    "addr_apply": ["ke_addr.hip", "fwpkm_device.h"],
 }
 
 
@@ -82,6 +85,9 @@ def parse():
                     help="run the token-weighted step (fwpkm_forward_chunk_weighted): weight 1 "
                          "everywhere except 0 on the last token of every sequence, which has "
                          "no lookahead target")
+    ap.add_argument("--addr-weight", type=float, default=0.0,
+                    help="weight of the marginal-entropy addressing loss on the sub-keys "
+                         "(0: the plain step)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every chunk from Python instead of replaying a HIP graph")
     ap.add_argument("--no-profile-pass", action="store_true",
@@ -105,19 +111,33 @@ def copy_probe(mib):
                       "copies": 5}))
 
 
-def algorithmic_cost(cfg, kernel, tokens, uniq_v, uniq_k):
+def algorithmic_cost(cfg, kernel, tokens, uniq_v, uniq_k, addr=False):
     """Compulsory bytes (and flops) one launch of `kernel` must move.
 
     tokens  = units * tokens per chunk in the launch
     uniq_v  = distinct value rows the launch updates
     uniq_k  = distinct K1 plus K2 rows the launch updates
+    addr    = the addressing loss is on (the score kernel also writes every
+              score, 2 halves x n per token)
     """
     f = 4  # fp32
     U = cfg.units
+    n, half = cfg.sqrt_slots, cfg.half
+    scores = f * tokens * 2 * n              # one fp32 score per (token, half, sub-key)
+    keys = f * U * 2 * n * half              # both sub-key tables
     if kernel == "score":
-        byts = f * (tokens * cfg.dim_qk + U * 2 * cfg.sqrt_slots * cfg.half)
-        flops = 2.0 * tokens * cfg.sqrt_slots * cfg.dim_qk
+        byts = f * tokens * cfg.dim_qk + keys + (scores if addr else 0)
+        flops = 2.0 * tokens * n * cfg.dim_qk
         return byts, flops
+    if kernel == "addr_stats":
+        # scores in, coefficients out (same buffer)
+        return 2 * scores, 0.0
+    if kernel == "addr_grad":
+        # coefficients and queries in, key tables in (IDW), key gradients out
+        return scores + f * tokens * cfg.dim_qk + 2 * keys, 2.0 * tokens * n * cfg.dim_qk
+    if kernel == "addr_apply":
+        # key gradients in, key tables read and written
+        return 3 * keys, 0.0
     if kernel == "read":
         # k gathered value rows + the target row read + the retrieved row written
         return f * tokens * (cfg.topk * cfg.dim_v + 2 * cfg.dim_v), 0.0
@@ -197,7 +217,8 @@ def main():
     B, H, C = cfg.batch, cfg.heads, cfg.chunk
 
     mem = Memory(Config(sqrt_slots=cfg.sqrt_slots, dim_qk=cfg.dim_qk, dim_v=cfg.dim_v,
-                        topk=cfg.topk, chunk_size=C, num_heads=H, max_batch=B, eps=cfg.eps))
+                        topk=cfg.topk, chunk_size=C, num_heads=H, max_batch=B, eps=cfg.eps,
+                        addr_weight=args.addr_weight))
     # per-sequence tables expanded from the shared initial ones (untimed)
     st = State(*(torch.from_numpy(a).to(dev).unsqueeze(0).repeat(B, *([1] * a.ndim)).contiguous()
                  for a in (tables.k1, tables.k2, tables.v)))
@@ -280,7 +301,8 @@ def main():
                    "topk": cfg.topk, "lr": cfg.lr, "eps": cfg.eps,
                    "parallelism": "single GPU",
                    "launch": "eager" if graph is None else "hip graph of one step",
-                   "token_weights": "last token of each sequence 0, others 1" if args.weighted else None},
+                   "token_weights": "last token of each sequence 0, others 1" if args.weighted else None,
+                   "addr_weight": args.addr_weight},
     }
 
     if not args.no_profile_pass:
@@ -309,7 +331,7 @@ def main():
             if n == 0:
                 continue
             avg_us = 1e3 * ms / n
-            byts, flops = algorithmic_cost(cfg, name, tokens_launch, uv, uk)
+            byts, flops = algorithmic_cost(cfg, name, tokens_launch, uv, uk, args.addr_weight != 0)
             kernels[name] = {"avg_us": avg_us, "launches": n,
                              "alg_bytes": byts, "alg_gbps": byts / (avg_us * 1e3) if byts else None,
                              "alg_tflops": flops / (avg_us * 1e6) if flops else None}
@@ -318,13 +340,15 @@ def main():
                                             "pairs": B * H * C * cfg.topk}
         dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
         kd = kernels[dom]
-        if dom == "score":
+        if kd["alg_tflops"] is not None and dom in ("score", "addr_grad"):
             roof = {"bound": "mfma", "achieved": kd["alg_tflops"], "peak": FP32_MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s"}
         else:
             roof = {"bound": "hbm", "achieved": kd["alg_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] / roof["peak"]
-        traffic = measured_traffic(cfg.name)
+        # the committed counters were taken on the plain step
+        plain = args.addr_weight == 0 and not args.weighted
+        traffic = measured_traffic(cfg.name) if plain else {}
         for name in kernels:
             kernels[name]["hbm_bytes_counted"] = traffic.get(name)
         roof["traffic"] = traffic.get(dom)

@@ -91,6 +91,15 @@ typedef struct {
     int32_t max_batch;   /* most sequences one call may carry; sizes the workspace     */
     float   eps;         /* IDW epsilon, finite and > 0 (the pages give no value)      */
     int32_t score_mode;  /* FWPKM_SCORE_IDW or FWPKM_SCORE_DOT                          */
+    float   addr_weight; /* lambda of the marginal-entropy addressing loss; finite; 0 = off.
+                          * [gist.science "Fast-weight Product Key Memory", section 2:
+                          * a negative-entropy loss on the key matrices keeps slot usage
+                          * balanced across a chunk.]  Per half h, p_h = chunk mean of the
+                          * per-token softmax of the scores over all n sub-keys; the loss
+                          * lambda * sum_i p_h[i] log p_h[i] adds its gradient to every
+                          * K1 / K2 row in the chunk's SGD step (at the chunk's starting
+                          * weights).  Non-zero costs three extra kernels per chunk and a
+                          * [units, 2, tokens, n] score buffer in the workspace.           */
 } fwpkm_config;
 
 /* Fast-weight state in caller-owned device memory (fp32, contiguous):
@@ -190,8 +199,11 @@ const char* fwpkm_last_error(void);
  *   1 read   (Cartesian top-k, weights, gather, backward)
  *   2 sort   (pair-list radix sort)
  *   3 update (segmented mean gradient + SGD)
- *   4 copy   (past -> next state copy, copy mode only)                      */
-#define FWPKM_NUM_TIMED 5
+ *   4 copy   (past -> next state copy, copy mode only)
+ *   5 addr_stats   (addressing loss: softmax statistics and marginal usage)
+ *   6 addr_grad    (addressing loss: key gradient contraction)
+ *   7 addr_apply   (addressing loss: key step)                              */
+#define FWPKM_NUM_TIMED 8
 
 /* enable != 0: clear the totals and start recording; 0: stop recording. */
 int fwpkm_profile_enable(fwpkm_handle* h, int32_t enable);

@@ -41,8 +41,8 @@ EXPORTS = (
     "fwpkm_kernel_name",
 )
 
-NUM_TIMED = 5
-KERNEL_NAMES = ("score", "read", "sort", "update", "copy")
+NUM_TIMED = 8
+KERNEL_NAMES = ("score", "read", "sort", "update", "copy", "addr_stats", "addr_grad", "addr_apply")
 
 
 class CConfig(ctypes.Structure):
@@ -56,6 +56,7 @@ class CConfig(ctypes.Structure):
         ("max_batch", ctypes.c_int32),
         ("eps", ctypes.c_float),
         ("score_mode", ctypes.c_int32),
+        ("addr_weight", ctypes.c_float),
     ]
 
 

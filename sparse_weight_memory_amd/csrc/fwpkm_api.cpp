@@ -33,7 +33,8 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Byte sizes of the workspace regions for `units` units of `tokens` tokens.
 struct WsLayout {
-  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, pay, long_rec, short_rec, kinds, total;
+  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, pay, long_rec, short_rec, kinds;
+  size_t addr_s, addr_dk, total;
 };
 
 WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
@@ -54,6 +55,12 @@ WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
   L.short_rec = take(sizeof(int4) * 3 * units * P);
   // regions per list shrink as units grow: 3 * units * regions <= max(256, 3 * units)
   L.kinds = take(sizeof(int4) * std::max<int64_t>(256, 3 * units));
+  // addressing loss (only with addr_weight != 0): every token's score over
+  // every sub-key (then its dL/ds coefficient), and the key gradient
+  const bool addr = c.addr_weight != 0.0f;
+  const int64_t n = c.sqrt_slots, half = c.dim_qk / 2;
+  L.addr_s = take(addr ? sizeof(float) * units * 2 * tokens * n : 0);
+  L.addr_dk = take(addr ? sizeof(float) * units * 2 * n * half : 0);
   L.total = off;
   return L;
 }
@@ -72,6 +79,7 @@ int check_config(const fwpkm_config* c) {
   if (!std::isfinite(c->eps) || !(c->eps > 0.f)) return fail(FWPKM_ERR_INVALID_ARG, "eps must be finite and > 0");
   if (c->score_mode != FWPKM_SCORE_IDW && c->score_mode != FWPKM_SCORE_DOT)
     return fail(FWPKM_ERR_INVALID_ARG, "unknown score_mode %d", c->score_mode);
+  if (!std::isfinite(c->addr_weight)) return fail(FWPKM_ERR_INVALID_ARG, "addr_weight must be finite");
   // kernel limits
   const int half = c->dim_qk / 2;
   if (c->sqrt_slots > FWPKM_MAX_SQRT_SLOTS) return fail(FWPKM_ERR_UNSUPPORTED, "sqrt_slots > %d", FWPKM_MAX_SQRT_SLOTS);
@@ -143,7 +151,8 @@ hipError_t timed(fwpkm_handle* h, int kernel, F&& fn) {
   return hipSuccess;
 }
 
-const char* const kKernelNames[FWPKM_NUM_TIMED] = {"score", "read", "sort", "update", "copy"};
+const char* const kKernelNames[FWPKM_NUM_TIMED] = {"score", "read", "sort", "update", "copy",
+                                                   "addr_stats", "addr_grad", "addr_apply"};
 
 }  // namespace
 
@@ -393,18 +402,33 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
   a.pw = std::max(c.dim_v, half);
   a.npr = 0;
   for (int i = 0; i < k; ++i) a.npr += k / (i + 1);
-
   const bool write = lr != 0.0f;
+  const bool addr = write && c.addr_weight != 0.0f;
+  a.addr_weight = c.addr_weight;
+  a.addr_s = addr ? reinterpret_cast<float*>(ws + L.addr_s) : nullptr;
+  a.addr_dk = reinterpret_cast<float*>(ws + L.addr_dk);
+
   using fwpkm::LaunchTiming;
   if ((e = timed(h, 0, [&](const LaunchTiming* tm) { return fwpkm::launch_ka(a, stream, tm); })) != hipSuccess)
     return fail(FWPKM_ERR_HIP, "score kernel: %s", hipGetErrorString(e));
   if ((e = timed(h, 1, [&](const LaunchTiming* tm) { return fwpkm::launch_kb(a, write, stream, tm); })) != hipSuccess)
     return fail(FWPKM_ERR_HIP, "read kernel: %s", hipGetErrorString(e));
   if (write) {
+    // the addressing gradient is taken at the starting keys, before the update
+    if (addr) {
+      if ((e = timed(h, 5, [&](const LaunchTiming* tm) { return fwpkm::launch_ke_stats(a, stream, tm); })) != hipSuccess)
+        return fail(FWPKM_ERR_HIP, "addressing statistics kernel: %s", hipGetErrorString(e));
+      if ((e = timed(h, 6, [&](const LaunchTiming* tm) { return fwpkm::launch_ke_grad(a, stream, tm); })) != hipSuccess)
+        return fail(FWPKM_ERR_HIP, "addressing gradient kernel: %s", hipGetErrorString(e));
+    }
     if ((e = timed(h, 2, [&](const LaunchTiming* tm) { return fwpkm::launch_kc(a, stream, tm); })) != hipSuccess)
       return fail(FWPKM_ERR_HIP, "sort kernel: %s", hipGetErrorString(e));
     if ((e = timed(h, 3, [&](const LaunchTiming* tm) { return fwpkm::launch_kd(a, stream, tm); })) != hipSuccess)
       return fail(FWPKM_ERR_HIP, "update kernel: %s", hipGetErrorString(e));
+    if (addr) {
+      if ((e = timed(h, 7, [&](const LaunchTiming* tm) { return fwpkm::launch_ke_apply(a, stream, tm); })) != hipSuccess)
+        return fail(FWPKM_ERR_HIP, "addressing step kernel: %s", hipGetErrorString(e));
+    }
   }
   g_err[0] = '\0';
   return FWPKM_OK;

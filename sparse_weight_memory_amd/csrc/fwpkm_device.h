@@ -68,6 +68,10 @@ struct ChunkArgs {
   int region_bits; // log2(regions)
   int pw;          // floats per row = max(d_v, d_h)
   int npr;         // Cartesian candidates (i, j) with (i+1)(j+1) <= k: sum_i floor(k/(i+1))
+  // marginal-entropy addressing loss (addr_s == nullptr: off)
+  float addr_weight;   // lambda
+  float* addr_s;       // [U, 2, T, n] ordering keys of every (token, sub-key); later dL/ds coefficients
+  float* addr_dk;      // [U, 2, n, d_h] addressing gradient of each key row
 };
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

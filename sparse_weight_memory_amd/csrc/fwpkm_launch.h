@@ -41,6 +41,13 @@ int group_regions(int units);
 size_t kc_smem_bytes(int P);
 hipError_t launch_kc(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 
+// KE: marginal-entropy addressing loss (only with addr_weight != 0):
+// softmax statistics and marginal usage per (unit, half), the key-gradient
+// contraction, and the key step after the update.
+hipError_t launch_ke_stats(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
+hipError_t launch_ke_grad(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
+hipError_t launch_ke_apply(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
+
 // KD: per segment mean gradient and in-place SGD on V, K1 and K2 rows.
 hipError_t launch_kd(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 

@@ -38,6 +38,7 @@ class Config:
     max_batch: int = 1
     eps: float = 1e-3
     score_mode: str = "idw"      # "idw" or "dot"
+    addr_weight: float = 0.0     # lambda of the marginal-entropy addressing loss (0: off)
 
     @property
     def num_slots(self) -> int:
@@ -51,7 +52,7 @@ class Config:
         mode = {"idw": _lib.SCORE_IDW, "dot": _lib.SCORE_DOT}.get(self.score_mode, -1)
         return _lib.CConfig(self.sqrt_slots, self.dim_qk, self.dim_v, self.topk,
                             self.chunk_size, self.num_heads, self.max_batch,
-                            float(self.eps), mode)
+                            float(self.eps), mode, float(self.addr_weight))
 
 
 class State(NamedTuple):

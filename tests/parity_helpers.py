@@ -64,9 +64,9 @@ def state_to_host(s, units=None):
     return out
 
 
-def oracle_units(state, q, y, lr, k, eps, mode, units, H, overrides=None, tw=None):
+def oracle_units(state, q, y, lr, k, eps, mode, units, H, overrides=None, tw=None, addr=0.0):
     """Run the oracle on the given units only (state holds those units, in order).
-    tw: token weights [B, C, H] or None.
+    tw: token weights [B, C, H] or None; addr: addressing-loss weight.
 
     Returns (retrieved {u: [C, d_v]}, new state (same unit order), results).
     """
@@ -76,7 +76,7 @@ def oracle_units(state, q, y, lr, k, eps, mode, units, H, overrides=None, tw=Non
         b, h = divmod(u, H)
         ov = overrides.get(u) if overrides else None
         r = O.unit_chunk(state["k1"][i], state["k2"][i], state["v"][i], q[b, :, h], y[b, :, h],
-                         lr, k, eps, mode, ov, None if tw is None else tw[b, :, h])
+                         lr, k, eps, mode, ov, None if tw is None else tw[b, :, h], addr)
         rets[u] = r.retrieved
         results[u] = r
         if r.updates:
@@ -142,11 +142,12 @@ def compare_chunk(mem, st_host, q, y, lr, units=None, rtol=RTOL_CHUNK, atol=ATOL
     sub = {name: a[units] for name, a in st_host.items()}
     mode = mode_name(cfg.score_mode)
     say(label, "oracle on units", units[:8], "..." if len(units) > 8 else "")
-    rets, new, results = oracle_units(sub, q, y, lr, cfg.topk, cfg.eps, mode, units, H, tw=tw)
+    addr = getattr(cfg, "addr_weight", 0.0)
+    rets, new, results = oracle_units(sub, q, y, lr, cfg.topk, cfg.eps, mode, units, H, tw=tw, addr=addr)
     overrides, ties = selection_overrides(results, slots, H, units)
     if overrides:
         rets, new, results = oracle_units(sub, q, y, lr, cfg.topk, cfg.eps, mode, units, H,
-                                          overrides, tw=tw)
+                                          overrides, tw=tw, addr=addr)
     for u in units:
         b, h = divmod(u, H)
         assert_close(f"{label} retrieved u{u}", ret[b, :, h], rets[u], rtol, atol)

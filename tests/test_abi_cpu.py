@@ -67,6 +67,8 @@ def create(lib, c):
     (dict(eps=0.0), _lib.ERR_INVALID_ARG),
     (dict(eps=float("nan")), _lib.ERR_INVALID_ARG),
     (dict(score_mode=7), _lib.ERR_INVALID_ARG),
+    (dict(addr_weight=float("nan")), _lib.ERR_INVALID_ARG),
+    (dict(addr_weight=float("inf")), _lib.ERR_INVALID_ARG),
     (dict(sqrt_slots=5000, topk=4), _lib.ERR_UNSUPPORTED),
     (dict(dim_qk=66), _lib.ERR_UNSUPPORTED),                  # d_h = 33
     (dict(dim_v=66), _lib.ERR_UNSUPPORTED),
@@ -197,3 +199,12 @@ def test_weighted_entry_checks_like_the_plain_one(fwpkm_lib, handle):
     if not torch.cuda.is_available():
         assert fwd_w(L, handle, r=TW + 4 * 2 * 64) == _lib.ERR_HIP
         assert fwd_w(L, handle, tw=None) == _lib.ERR_HIP      # NULL = all weights 1
+
+
+def test_addressing_workspace_only_when_enabled(fwpkm_lib):
+    """The [units, 2, tokens, n] score buffer and the key gradients are
+    allocated only with a non-zero addressing weight."""
+    off = fwpkm_lib.fwpkm_workspace_bytes(ctypes.byref(cfg()))
+    on = fwpkm_lib.fwpkm_workspace_bytes(ctypes.byref(cfg(addr_weight=0.1)))
+    units, tokens, n, half = 2, 64, 32, 32
+    assert on - off >= 4 * units * 2 * (tokens * n + n * half)
