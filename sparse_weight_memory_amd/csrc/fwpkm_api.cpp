@@ -34,7 +34,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 // Byte sizes of the workspace regions for `units` units of `tokens` tokens.
 struct WsLayout {
   size_t half_o, half_i, qnorm, sel_w, g, keys, coef, pay, long_rec, short_rec, kinds;
-  size_t addr_s, addr_dk, total;
+  size_t addr_s, addr_dk, addr_tok, addr_ell, total;
 };
 
 WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
@@ -59,8 +59,11 @@ WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
   // every sub-key (then its dL/ds coefficient), and the key gradient
   const bool addr = c.addr_weight != 0.0f;
   const int64_t n = c.sqrt_slots, half = c.dim_qk / 2;
-  L.addr_s = take(addr ? sizeof(float) * units * 2 * tokens * n : 0);
+  const int64_t np = (n + fwpkm::kAddrPad - 1) / fwpkm::kAddrPad * fwpkm::kAddrPad;
+  L.addr_s = take(addr ? sizeof(float) * units * 2 * tokens * np : 0);
   L.addr_dk = take(addr ? sizeof(float) * units * 2 * n * half : 0);
+  L.addr_tok = take(addr ? sizeof(float) * units * 2 * tokens * 2 : 0);
+  L.addr_ell = take(addr ? sizeof(float) * units * 2 * n : 0);
   L.total = off;
   return L;
 }
@@ -406,7 +409,10 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
   const bool addr = write && c.addr_weight != 0.0f;
   a.addr_weight = c.addr_weight;
   a.addr_s = addr ? reinterpret_cast<float*>(ws + L.addr_s) : nullptr;
+  a.addr_np = (n + fwpkm::kAddrPad - 1) / fwpkm::kAddrPad * fwpkm::kAddrPad;
   a.addr_dk = reinterpret_cast<float*>(ws + L.addr_dk);
+  a.addr_tok = reinterpret_cast<float*>(ws + L.addr_tok);
+  a.addr_ell = reinterpret_cast<float*>(ws + L.addr_ell);
 
   using fwpkm::LaunchTiming;
   if ((e = timed(h, 0, [&](const LaunchTiming* tm) { return fwpkm::launch_ka(a, stream, tm); })) != hipSuccess)

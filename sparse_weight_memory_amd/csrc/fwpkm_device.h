@@ -10,6 +10,7 @@ namespace fwpkm {
 constexpr int kWave = 64;
 constexpr int kKeyBlock = 64;       // smallest key block of the score kernel
 constexpr int kTokTile = 16;        // tokens per score workgroup (MFMA N)
+constexpr int kAddrPad = 256;   // score-row pitch multiple of the addressing loss (4 loads per lane)
 constexpr int kGroupWaves = 8;      // waves of one grouping workgroup
 constexpr int kSortMaxPairs = 8192; // C*k limit of the in-LDS sort
 constexpr int kShortSeg = 16;       // longest segment one update wave sums alone
@@ -70,8 +71,11 @@ struct ChunkArgs {
   int npr;         // Cartesian candidates (i, j) with (i+1)(j+1) <= k: sum_i floor(k/(i+1))
   // marginal-entropy addressing loss (addr_s == nullptr: off)
   float addr_weight;   // lambda
-  float* addr_s;       // [U, 2, T, n] ordering keys of every (token, sub-key); later dL/ds coefficients
+  float* addr_s;       // [U, 2, T, addr_np] ordering keys of every (token, sub-key); later dL/ds coefficients
+  int addr_np;         // row pitch of addr_s: n rounded up to kAddrPad (pad columns hold no data)
   float* addr_dk;      // [U, 2, n, d_h] addressing gradient of each key row
+  float* addr_tok;     // [U, 2, T, 2] per token: softmax shift m (dot) and 1 / softmax sum
+  float* addr_ell;     // [U, 2, n] log marginal usage of each sub-key
 };
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -42,8 +42,9 @@ size_t kc_smem_bytes(int P);
 hipError_t launch_kc(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 
 // KE: marginal-entropy addressing loss (only with addr_weight != 0):
-// softmax statistics and marginal usage per (unit, half), the key-gradient
-// contraction, and the key step after the update.
+// softmax statistics, marginal usage and dL/ds coefficients per (unit,
+// half) (three kernels, timed as one span), the key-gradient contraction,
+// and the key step after the update.
 hipError_t launch_ke_stats(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 hipError_t launch_ke_grad(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 hipError_t launch_ke_apply(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);

@@ -302,10 +302,10 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   // ---- addressing loss: every ordering key of the tile goes to the
   // workspace (the softmax over all sub-keys needs them, not only the best k)
   if (a.addr_s) {
-    float* dst = a.addr_s + ((int64_t)(u * 2 + h) * a.T + t0) * a.n + kb * blk;
+    float* dst = a.addr_s + ((int64_t)(u * 2 + h) * a.T + t0) * a.addr_np + kb * blk;
     for (int e = tid; e < kTokTile * blk; e += kScoreWaves * kWave) {
       const int r = e / blk, c = e - r * blk;
-      if (t0 + r < a.T && kb * blk + c < a.n) dst[(int64_t)r * a.n + c] = sc[r * ppitch + c];
+      if (t0 + r < a.T && kb * blk + c < a.n) dst[(int64_t)r * a.addr_np + c] = sc[r * ppitch + c];
     }
   }
 

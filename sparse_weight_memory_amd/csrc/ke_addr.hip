@@ -11,9 +11,16 @@
 //   dL/ds[t, j] = lambda/T * P[t, j] (l_j - sum_i P[t, i] l_i),  l = log p
 //   dL/dK[j]    = sum_t dL/ds[t, j] * ds[t, j]/dK[j], with
 //                 IDW 2 (q_t - K[j]) / (eps + d[t, j]),  dot q_t.
-// The score kernel leaves every ordering key in addr_s; ke_stats turns them
-// into the coefficients c[t, j] = dL/ds * (IDW: 2 / (eps + d)) in place;
-// ke_grad contracts them with the queries on the matrix cores,
+// The score kernel leaves every ordering key o in addr_s (IDW: the squared
+// distance is qnorm + o; dot: the score is -o).  For IDW the softmax of
+// -log(eps + d) is u / sum u with u = 1 / (eps + d), so no exp or log is taken
+// there; dot scores take the usual max-shifted softmax.
+//   ke_tokstats  per token: shift m (dot) and 1 / softmax sum
+//   ke_usage     per sub-key: p = mean_t P[t, :] and l = log p, summed over
+//                tokens in a fixed order (deterministic)
+//   ke_coef      per token: sum_i P l_i, then c[t, j] = dL/ds * (IDW:
+//                2 / (eps + d)) written over the scores in place
+// ke_grad contracts c with the queries on the matrix cores,
 //   dK[j] = sum_t c[t, j] q_t  (- (sum_t c[t, j]) K[j] for IDW),
 // at the chunk's starting keys; ke_apply subtracts lr * dK from every key row
 // after the update kernel has taken the MSE step.
@@ -25,9 +32,7 @@ namespace fwpkm {
 
 namespace {
 
-constexpr int kStatThreads = 1024;
-constexpr int kMaxTokens = 1024;     // chunk-size limit of the API
-constexpr int kMaxSubKeys = 4096;    // sqrt_slots limit of the API
+constexpr int kStatWaves = 16;       // one token (or 64 sub-keys) per wave
 constexpr float kMinUsage = 1e-30f;  // floor of p before the log (p > 0 in exact arithmetic)
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -40,63 +45,165 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// One token's view of its score row: turns an ordering key into the
+// unnormalised softmax term and the IDW factor 1 / (eps + d).  The score mode
+// is a template argument so that no branch sits between a row's loads.
+template <bool kIdw>
+struct TokenRow {
+  float eps, qn, m;
+  __device__ __forceinline__ float inv_dist(float o) const {
+    const float d = qn + o;
+    return 1.0f / (eps + (d > 0.f ? d : 0.f));
+  }
+  // exp(s - m): IDW u = 1 / (eps + d) (m = 0), dot exp(-o - m)
+  __device__ __forceinline__ float term(float o) const { return kIdw ? inv_dist(o) : expf(-o - m); }
+};
+
+template <bool kIdw>
+__device__ __forceinline__ TokenRow<kIdw> token_row(const ChunkArgs& a, int u, int h, int t, float m) {
+  TokenRow<kIdw> r;
+  r.eps = a.eps;
+  r.qn = kIdw ? a.qnorm[((int64_t)u * a.T + t) * 2 + h] : 0.f;
+  r.m = m;
+  return r;
+}
+
 }  // namespace
 
-// One workgroup per (unit, half).
-__global__ __launch_bounds__(kStatThreads) void ke_stats(ChunkArgs a) {
-  __shared__ float s_max[kMaxTokens];
-  __shared__ float s_inv[kMaxTokens];    // 1 / softmax sum
-  __shared__ float s_ell[kMaxSubKeys];   // log marginal usage
-  const int uh = blockIdx.x;
-  const int u = uh >> 1, h = uh & 1;
-  const int T = a.T, n = a.n;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  constexpr int kWaves = kStatThreads / kWave;
-  float* S = a.addr_s + (int64_t)uh * T * n;
-  const bool idw = a.mode == 0;
-  auto dist = [&](float o, int t) {   // squared distance from the ordering key
-    const float d = a.qnorm[((int64_t)u * T + t) * 2 + h] + o;
-    return d > 0.f ? d : 0.f;
-  };
-  auto score = [&](float o, int t) { return idw ? -logf(a.eps + dist(o, t)) : -o; };
+// Loads of a score row run kRowLoads at a time across the padded pitch (every
+// load in range, none behind a branch); values past n are masked to zero in
+// sums by AND-ing their bits, so no load is ever made conditional.
+constexpr int kRowLoads = kAddrPad / kWave;
+static_assert(kRowLoads * kWave == kAddrPad, "row pitch is a whole number of load batches");
 
-  // per token: max score and softmax sum
-  for (int t = wave; t < T; t += kWaves) {
-    const float* row = S + (int64_t)t * n;
-    float m = -__builtin_inff();
-    for (int i = lane; i < n; i += kWave) m = fmaxf(m, score(row[i], t));
-    m = wave_max(m);
-    float z = 0.f;
-    for (int i = lane; i < n; i += kWave) z += expf(score(row[i], t) - m);
-    z = wave_sum(z);
-    if (lane == 0) {
-      s_max[t] = m;
-      s_inv[t] = 1.0f / z;
+// The mask goes through an empty asm so the compiler cannot rewrite the AND
+// as a select and then move the load behind a branch (which would wait for
+// every load on its own).
+__device__ __forceinline__ float keep_if(float x, bool ok) {
+  unsigned int m = ok ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(m));
+  return __uint_as_float(__float_as_uint(x) & m);
+}
+
+// grid (2U, ceil(T / 16)): one wave per token.
+template <bool kIdw>
+__global__ __launch_bounds__(kStatWaves * kWave) void ke_tokstats(ChunkArgs a) {
+  const int uh = blockIdx.x, u = uh >> 1, h = uh & 1;
+  const int t = blockIdx.y * kStatWaves + (int)(threadIdx.x / kWave);
+  const int lane = lane_id(), n = a.n, np = a.addr_np;
+  if (t >= a.T) return;
+  const float* row = a.addr_s + ((int64_t)uh * a.T + t) * np;
+  float m = 0.f;
+  if (!kIdw) {                // dot: m = max_i s_i = max_i (-o_i); past n reread column n-1
+    float hi = -__builtin_inff();
+    for (int i0 = 0; i0 < np; i0 += kAddrPad) {
+      float x[kRowLoads];
+#pragma unroll
+      for (int j = 0; j < kRowLoads; ++j) {
+        const int i = i0 + j * kWave + lane;
+        x[j] = row[i < n ? i : n - 1];
+      }
+#pragma unroll
+      for (int j = 0; j < kRowLoads; ++j) hi = fmaxf(hi, -x[j]);
     }
+    m = wave_max(hi);
   }
+  const TokenRow<kIdw> tr = token_row<kIdw>(a, u, h, t, m);
+  float z = 0.f;
+  for (int i0 = 0; i0 < np; i0 += kAddrPad) {
+    float x[kRowLoads];
+#pragma unroll
+    for (int j = 0; j < kRowLoads; ++j) x[j] = row[i0 + j * kWave + lane];
+#pragma unroll
+    for (int j = 0; j < kRowLoads; ++j) z += keep_if(tr.term(x[j]), i0 + j * kWave + lane < n);
+  }
+  z = wave_sum(z);
+  if (lane == 0) {
+    float* st = a.addr_tok + ((int64_t)uh * a.T + t) * 2;
+    st[0] = m;
+    st[1] = 1.0f / z;
+  }
+}
+
+// grid (2U, ceil(n / 64)): lane = sub-key, waves stride over tokens; the 16
+// partial sums of a sub-key are added in wave order.
+template <bool kIdw>
+__global__ __launch_bounds__(kStatWaves * kWave) void ke_usage(ChunkArgs a) {
+  constexpr int kTokLoads = 8;            // tokens of one wave in flight
+  __shared__ float part[kStatWaves][kWave];
+  const int uh = blockIdx.x, u = uh >> 1, h = uh & 1;
+  const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
+  const int i = blockIdx.y * kWave + lane;          // < addr_np: the load is in range
+  const int n = a.n, T = a.T, np = a.addr_np;
+  const float* S = a.addr_s + (int64_t)uh * T * np;
+  const float* st = a.addr_tok + (int64_t)uh * T * 2;
+  float acc = 0.f;
+  for (int t0 = wave; t0 < T; t0 += kStatWaves * kTokLoads) {
+    float x[kTokLoads], zi[kTokLoads];
+    TokenRow<kIdw> tr[kTokLoads];
+#pragma unroll
+    for (int j = 0; j < kTokLoads; ++j) {
+      const int t = t0 + j * kStatWaves;
+      const int tc = t < T ? t : T - 1;
+      x[j] = S[(int64_t)tc * np + i];
+      tr[j] = token_row<kIdw>(a, u, h, tc, kIdw ? 0.f : st[2 * tc]);
+      zi[j] = st[2 * tc + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kTokLoads; ++j)
+      acc += keep_if(tr[j].term(x[j]) * zi[j], t0 + j * kStatWaves < T);
+  }
+  part[wave][lane] = acc;
   __syncthreads();
-  // per sub-key: marginal usage and its log
-  const float inv_T = 1.0f / (float)T;
-  for (int i = tid; i < n; i += kStatThreads) {
+  if (wave == 0 && i < n) {
     float p = 0.f;
-    for (int t = 0; t < T; ++t) p += expf(score(S[(int64_t)t * n + i], t) - s_max[t]) * s_inv[t];
-    s_ell[i] = logf(fmaxf(p * inv_T, kMinUsage));
+#pragma unroll
+    for (int w = 0; w < kStatWaves; ++w) p += part[w][lane];
+    a.addr_ell[(int64_t)uh * n + i] = logf(fmaxf(p / (float)T, kMinUsage));
   }
-  __syncthreads();
-  // per token: sum_i P l_i, then the coefficients in place
-  const float lam_T = a.addr_weight * inv_T;
-  for (int t = wave; t < T; t += kWaves) {
-    float* row = S + (int64_t)t * n;
-    const float m = s_max[t], zi = s_inv[t];
-    float acc = 0.f;
-    for (int i = lane; i < n; i += kWave) acc += expf(score(row[i], t) - m) * zi * s_ell[i];
-    const float pl = wave_sum(acc);
-    for (int i = lane; i < n; i += kWave) {
-      const float o = row[i];
-      const float P = expf(score(o, t) - m) * zi;
-      float c = lam_T * P * (s_ell[i] - pl);
-      if (idw) c *= 2.0f / (a.eps + dist(o, t));
-      row[i] = c;
+}
+
+// grid (2U, ceil(T / 16)): one wave per token; scores become coefficients
+// (pad columns receive values that no reader uses).
+template <bool kIdw>
+__global__ __launch_bounds__(kStatWaves * kWave) void ke_coef(ChunkArgs a) {
+  const int uh = blockIdx.x, u = uh >> 1, h = uh & 1;
+  const int t = blockIdx.y * kStatWaves + (int)(threadIdx.x / kWave);
+  const int lane = lane_id(), n = a.n, np = a.addr_np;
+  if (t >= a.T) return;
+  float* row = a.addr_s + ((int64_t)uh * a.T + t) * np;
+  const float* ell = a.addr_ell + (int64_t)uh * n;
+  const float* st = a.addr_tok + ((int64_t)uh * a.T + t) * 2;
+  const TokenRow<kIdw> tr = token_row<kIdw>(a, u, h, t, st[0]);
+  const float zi = st[1];
+  float acc = 0.f;
+  for (int i0 = 0; i0 < np; i0 += kAddrPad) {
+    float x[kRowLoads], l[kRowLoads];
+#pragma unroll
+    for (int j = 0; j < kRowLoads; ++j) {
+      const int i = i0 + j * kWave + lane;
+      x[j] = row[i];
+      l[j] = ell[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kRowLoads; ++j)
+      acc += keep_if(tr.term(x[j]) * zi * l[j], i0 + j * kWave + lane < n);
+  }
+  const float pl = wave_sum(acc);
+  const float lam_T = a.addr_weight / (float)a.T;
+  for (int i0 = 0; i0 < np; i0 += kAddrPad) {
+    float x[kRowLoads], l[kRowLoads];
+#pragma unroll
+    for (int j = 0; j < kRowLoads; ++j) {
+      const int i = i0 + j * kWave + lane;
+      x[j] = row[i];
+      l[j] = ell[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kRowLoads; ++j) {
+      float c = lam_T * (tr.term(x[j]) * zi) * (l[j] - pl);
+      if (kIdw) c *= 2.0f * tr.inv_dist(x[j]);
+      row[i0 + j * kWave + lane] = c;
     }
   }
 }
@@ -105,13 +212,16 @@ namespace {
 
 constexpr int kGradWaves = 16;
 constexpr int kGradTile = 64;     // keys and dims of one workgroup's output block
-constexpr int kTokChunk = 32;     // tokens staged in LDS at a time
+constexpr int kTokChunk = 64;     // tokens staged in LDS at a time
 constexpr int kGradPitch = kGradTile + 4;
+constexpr int kRowsPerPass = kGradWaves;                  // one staged row per wave per load
+constexpr int kLoadsPerThread = 2 * kTokChunk / kRowsPerPass;   // coefficient and query rows
 
 }  // namespace
 
 // dK for a 64-key x 64-dim block of one (unit, half); 16 waves, one 16x16
-// output tile each.
+// output tile each.  The next 64-token slice of coefficients and queries is
+// loaded into registers while the current one feeds the matrix cores.
 __global__ __launch_bounds__(kGradWaves * kWave) void ke_grad(ChunkArgs a) {
   __shared__ float cs[kTokChunk][kGradPitch];   // coefficients [token][key]
   __shared__ float qs[kTokChunk][kGradPitch];   // queries [token][dim]
@@ -120,30 +230,53 @@ __global__ __launch_bounds__(kGradWaves * kWave) void ke_grad(ChunkArgs a) {
   const int b = u / a.H, hh = u - b * a.H;
   const int key0 = blockIdx.y * kGradTile, dim0 = blockIdx.z * kGradTile;
   const int T = a.T, n = a.n, half = a.half;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
   const int kt = wave & 3, dt = wave >> 2;        // 16x16 tile of the block
   const int row = lane & 15, quad = lane >> 4;
-  const float* S = a.addr_s + (int64_t)uh * T * n;
+  const int np = a.addr_np;
+  const float* S = a.addr_s + (int64_t)uh * T * np;
+  const float* Q = a.q + (int64_t)b * T * a.H * a.dqk + (int64_t)hh * a.dqk + h * half;
+  const int64_t q_tok = (int64_t)a.H * a.dqk;     // query stride between tokens
+  // this lane's column in the staged rows: key columns past n fall in the
+  // row pitch's pad, dims past d_h are clamped; both are masked to zero
+  const bool key_ok = key0 + lane < n, dim_ok = dim0 + lane < half;
+  const int key_c = key0 + lane, dim_c = dim_ok ? dim0 + lane : half - 1;
+  float pre[kLoadsPerThread];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < kLoadsPerThread; ++j) {
+      const int r = wave + kRowsPerPass * (j % (kLoadsPerThread / 2));
+      const int t = t0 + r;
+      const int tc = t < T ? t : T - 1;
+      pre[j] = j < kLoadsPerThread / 2 ? S[(int64_t)tc * np + key_c] : Q[tc * q_tok + dim_c];
+    }
+  };
+  // the starting key rows of this lane's four outputs (IDW term), loaded
+  // up front with clamped indices so that they land during the loop
+  const bool idw = a.mode == 0;
+  const float* Kt = (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k + (int64_t)hh * n * half;
+  const int out_dim = dim0 + dt * 16 + row;
+  float kv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int key = key0 + kt * 16 + 4 * quad + r;
+    kv[r] = Kt[(int64_t)(key < n ? key : n - 1) * half + (out_dim < half ? out_dim : half - 1)];
+  }
   typedef float v4f __attribute__((ext_vector_type(4)));
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
   float csum = 0.f;                               // sum_t c[t, key0 + kt*16 + row] (lanes of quad 0..3)
+  fetch(0);
   for (int t0 = 0; t0 < T; t0 += kTokChunk) {
-    // stage: 2 * 32 * 64 floats, two per thread
-    for (int e = tid; e < 2 * kTokChunk * kGradTile; e += kGradWaves * kWave) {
-      const int which = e / (kTokChunk * kGradTile);
-      const int r = (e / kGradTile) % kTokChunk, c = e % kGradTile;
-      const int t = t0 + r;
-      float x = 0.f;
-      if (which == 0) {
-        if (t < T && key0 + c < n) x = S[(int64_t)t * n + key0 + c];
-        cs[r][c] = x;
-      } else {
-        if (t < T && dim0 + c < half)
-          x = a.q[((int64_t)(b * T + t) * a.H + hh) * a.dqk + h * half + dim0 + c];
-        qs[r][c] = x;
-      }
+#pragma unroll
+    for (int j = 0; j < kLoadsPerThread; ++j) {
+      // masked here, after the loads have landed: rows past T, key columns
+      // in the pitch's pad and clamped dims stage as zero
+      const int r = wave + kRowsPerPass * (j % (kLoadsPerThread / 2));
+      if (j < kLoadsPerThread / 2) cs[r][lane] = keep_if(pre[j], t0 + r < T && key_ok);
+      else qs[r][lane] = keep_if(pre[j], t0 + r < T && dim_ok);
     }
     __syncthreads();
+    fetch(t0 + kTokChunk);                        // past the end: clamped, masked, unused
 #pragma unroll
     for (int s = 0; s < kTokChunk / 4; ++s) {
       const float av = cs[4 * s + quad][kt * 16 + row];   // A[key][token]
@@ -156,17 +289,15 @@ __global__ __launch_bounds__(kGradWaves * kWave) void ke_grad(ChunkArgs a) {
   // coefficient sums per key: lanes row, row+16, row+32, row+48 hold parts
   csum += xor_lane<16>(csum);
   csum += xor_lane<32>(csum);
-  const bool idw = a.mode == 0;
-  const float* Kt = (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k + (int64_t)hh * n * half;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int kl = 4 * quad + r;                  // key of this accumulator inside the tile
     const float ck = __shfl(csum, kl, kWave);
-    const int key = key0 + kt * 16 + kl, dim = dim0 + dt * 16 + row;
-    if (key < n && dim < half) {
+    const int key = key0 + kt * 16 + kl;
+    if (key < n && out_dim < half) {
       float g = acc[r];
-      if (idw) g -= ck * Kt[(int64_t)key * half + dim];
-      a.addr_dk[((int64_t)uh * n + key) * half + dim] = g;
+      if (idw) g -= ck * kv[r];
+      a.addr_dk[((int64_t)uh * n + key) * half + out_dim] = g;
     }
   }
 }
@@ -186,7 +317,25 @@ __global__ __launch_bounds__(256) void ke_apply(ChunkArgs a) {
 }
 
 hipError_t launch_ke_stats(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
-  return fw_launch(ke_stats, dim3(2 * a.U), dim3(kStatThreads), 0, s, tm, a);
+  // one timed span: the first launch stamps the start, the last the end
+  LaunchTiming first, last;
+  if (tm) {
+    first.beg = tm->beg;
+    last.end = tm->end;
+  }
+  const dim3 tok_grid(2 * a.U, (a.T + kStatWaves - 1) / kStatWaves);
+  const dim3 key_grid(2 * a.U, (a.n + kWave - 1) / kWave);
+  const dim3 block(kStatWaves * kWave);
+  const bool idw = a.mode == 0;
+  hipError_t e = idw ? fw_launch(ke_tokstats<true>, tok_grid, block, 0, s, tm ? &first : nullptr, a)
+                     : fw_launch(ke_tokstats<false>, tok_grid, block, 0, s, tm ? &first : nullptr, a);
+  if (e == hipSuccess)
+    e = idw ? fw_launch(ke_usage<true>, key_grid, block, 0, s, nullptr, a)
+            : fw_launch(ke_usage<false>, key_grid, block, 0, s, nullptr, a);
+  if (e == hipSuccess)
+    e = idw ? fw_launch(ke_coef<true>, tok_grid, block, 0, s, tm ? &last : nullptr, a)
+            : fw_launch(ke_coef<false>, tok_grid, block, 0, s, tm ? &last : nullptr, a);
+  return e;
 }
 
 hipError_t launch_ke_grad(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
