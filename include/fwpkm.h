@@ -183,6 +183,63 @@ int fwpkm_forward_chunk_weighted(fwpkm_handle* h,
                                  float* retrieved, int32_t* out_slots, float* out_weights,
                                  hipStream_t stream);
 
+/* ---- sequence-level layer ------------------------------------------------
+ * Whole token sequences through the memory [PyPI page
+ * "fast-weight-product-key-memory", Usage: model-width tokens in, memories
+ * chained from call to call; gist.science "Fast-weight Product Key Memory",
+ * section 2: Core Architecture (gated residual output) and Key Technical
+ * Choices (lookahead targets)].  With D = num_heads * dim_v the model width
+ * and, per token t of a sequence of S tokens:
+ *
+ *   [q_t | v_t] = w_in x_t               fp32 projection (queries of head
+ *                                         0..H-1, then values of head 0..H-1)
+ *   target of q_t = v_{t+1}              the last token has none: it reads
+ *                                         but does not write (weight 0)
+ *   chunks of chunk_size tokens (the last may be shorter), each read with
+ *   the tables left by the chunks before it, then written
+ *   (fwpkm_forward_chunk_weighted's step, addr_weight included)
+ *   g = sigmoid(w_gate[h] . x_t + b_gate[h])
+ *   out_t[h*dim_v .. (h+1)*dim_v) = g * r_t[h] + (1 - g) * x_t[same slice]
+ *
+ * The gate's and the projections' forms are readings: the pages name the
+ * gate and the lookahead pairing but give no formula for either. */
+
+/* Bytes of workspace fwpkm_forward_sequence needs for (batch, seq); 0 on
+ * an invalid configuration or size (see fwpkm_last_error). */
+size_t fwpkm_sequence_workspace_bytes(const fwpkm_config* cfg, int32_t batch, int32_t seq);
+
+/* Arguments (device pointers unless noted; all row-major fp32):
+ *   x          [batch, seq, D] tokens
+ *   w_in       [H*dim_qk + H*dim_v, D] projection rows
+ *   w_gate     [H, D] gate weights;  b_gate  nullable [H] gate biases (0)
+ *   batch      1 .. max_batch;  seq  >= 1 (batch * seq <= 2^30)
+ *   lr         learning rate of every chunk's step (0: read only)
+ *   past_state, next_state  as for fwpkm_forward_chunk: the first chunk
+ *              reads past_state (copied into next_state when they differ),
+ *              later chunks update next_state in place
+ *   out        [batch, seq, D] written: the gated output
+ *   out_slots, out_weights  nullable [batch, seq, H, k]: every token's
+ *              selection, as fwpkm_forward_chunk reports it
+ *   workspace  caller-owned device memory of at least
+ *              fwpkm_sequence_workspace_bytes(cfg, batch, seq) bytes (its
+ *              contents need no initialisation and are scratch afterwards)
+ *   stream     HIP stream to enqueue on
+ * Aliasing: out, out_slots, out_weights, the workspace and next_state must
+ * not overlap x, w_in, w_gate or b_gate; outputs must not overlap the
+ * workspace or the state; the workspace must not overlap the state
+ * (FWPKM_ERR_ALIAS).  Every size and pointer is checked before anything is
+ * enqueued; a HIP error during enqueueing leaves out and next_state
+ * unspecified.  The handle's own workspace is used by each chunk, as for
+ * fwpkm_forward_chunk: calls on one handle must be ordered. */
+int fwpkm_forward_sequence(fwpkm_handle* h,
+                           const float* x, const float* w_in,
+                           const float* w_gate, const float* b_gate,
+                           int32_t batch, int32_t seq, float lr,
+                           const fwpkm_state* past_state, const fwpkm_state* next_state,
+                           float* out, int32_t* out_slots, float* out_weights,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* Release the handle and its workspace (synchronises the device before the
  * workspace is freed).  NULL-safe. */
 void fwpkm_destroy(fwpkm_handle* h);
@@ -202,8 +259,10 @@ const char* fwpkm_last_error(void);
  *   4 copy   (past -> next state copy, copy mode only)
  *   5 addr_stats   (addressing loss: softmax statistics and marginal usage)
  *   6 addr_grad    (addressing loss: key gradient contraction)
- *   7 addr_apply   (addressing loss: key step)                              */
-#define FWPKM_NUM_TIMED 8
+ *   7 addr_apply   (addressing loss: key step)
+ *   8 project  (sequence layer: query/value projection and last-token prep)
+ *   9 gate     (sequence layer: gated output)                             */
+#define FWPKM_NUM_TIMED 10
 
 /* enable != 0: clear the totals and start recording; 0: stop recording. */
 int fwpkm_profile_enable(fwpkm_handle* h, int32_t enable);

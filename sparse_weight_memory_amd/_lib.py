@@ -34,6 +34,8 @@ EXPORTS = (
     "fwpkm_workspace_bytes",
     "fwpkm_forward_chunk",
     "fwpkm_forward_chunk_weighted",
+    "fwpkm_sequence_workspace_bytes",
+    "fwpkm_forward_sequence",
     "fwpkm_destroy",
     "fwpkm_last_error",
     "fwpkm_profile_enable",
@@ -41,8 +43,9 @@ EXPORTS = (
     "fwpkm_kernel_name",
 )
 
-NUM_TIMED = 8
-KERNEL_NAMES = ("score", "read", "sort", "update", "copy", "addr_stats", "addr_grad", "addr_apply")
+NUM_TIMED = 10
+KERNEL_NAMES = ("score", "read", "sort", "update", "copy", "addr_stats", "addr_grad", "addr_apply",
+                "project", "gate")
 
 
 class CConfig(ctypes.Structure):
@@ -110,6 +113,22 @@ def load() -> ctypes.CDLL:
         ctypes.c_void_p,                       # stream
     ]
     lib.fwpkm_forward_chunk_weighted.restype = ctypes.c_int
+    lib.fwpkm_sequence_workspace_bytes.argtypes = [ctypes.POINTER(CConfig), ctypes.c_int32,
+                                                   ctypes.c_int32]
+    lib.fwpkm_sequence_workspace_bytes.restype = ctypes.c_size_t
+    lib.fwpkm_forward_sequence.argtypes = [
+        ctypes.c_void_p,                       # handle
+        ctypes.c_void_p, ctypes.c_void_p,      # x, w_in
+        ctypes.c_void_p, ctypes.c_void_p,      # w_gate, b_gate (nullable)
+        ctypes.c_int32, ctypes.c_int32,        # batch, seq
+        ctypes.c_float,                        # lr
+        ctypes.POINTER(CState), ctypes.POINTER(CState),
+        ctypes.c_void_p,                       # out
+        ctypes.c_void_p, ctypes.c_void_p,      # out_slots, out_weights
+        ctypes.c_void_p, ctypes.c_size_t,      # workspace, workspace_bytes
+        ctypes.c_void_p,                       # stream
+    ]
+    lib.fwpkm_forward_sequence.restype = ctypes.c_int
     lib.fwpkm_destroy.argtypes = [ctypes.c_void_p]
     lib.fwpkm_destroy.restype = None
     lib.fwpkm_last_error.argtypes = []

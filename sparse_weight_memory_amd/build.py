@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfwpkm.so")
 
 SOURCES = ["ka_score.hip", "kb_read.hip", "kc_sort.hip", "kd_update.hip", "ke_addr.hip",
-           "fwpkm_api.cpp"]
+           "kf_sequence.hip", "fwpkm_api.cpp"]
 ARCH = "gfx950"
 
 

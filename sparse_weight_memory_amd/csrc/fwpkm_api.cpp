@@ -68,6 +68,23 @@ WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
   return L;
 }
 
+// Byte offsets of the sequence call's caller-provided workspace.
+struct SeqLayout {
+  size_t q, y, tw, total;
+};
+
+SeqLayout seq_layout(const fwpkm_config& c, int64_t batch, int64_t seq) {
+  SeqLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
+  const int64_t H = c.num_heads;
+  L.q = take(sizeof(float) * batch * seq * H * c.dim_qk);     // chunk-major queries
+  L.y = take(sizeof(float) * batch * seq * H * c.dim_v);      // chunk-major lookahead targets
+  L.tw = take(sizeof(float) * batch * std::min<int64_t>(seq, c.chunk_size) * H);   // last chunk's weights
+  L.total = off;
+  return L;
+}
+
 int check_config(const fwpkm_config* c) {
   if (!c) return fail(FWPKM_ERR_INVALID_ARG, "config is NULL");
   if (c->sqrt_slots < 1) return fail(FWPKM_ERR_INVALID_ARG, "sqrt_slots must be >= 1 (got %d)", c->sqrt_slots);
@@ -155,7 +172,8 @@ hipError_t timed(fwpkm_handle* h, int kernel, F&& fn) {
 }
 
 const char* const kKernelNames[FWPKM_NUM_TIMED] = {"score", "read", "sort", "update", "copy",
-                                                   "addr_stats", "addr_grad", "addr_apply"};
+                                                   "addr_stats", "addr_grad", "addr_apply",
+                                                   "project", "gate"};
 
 }  // namespace
 
@@ -186,7 +204,7 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
                         const float* token_weights, int32_t batch, int32_t tokens, float lr,
                         const fwpkm_state* past, const fwpkm_state* next,
                         float* retrieved, int32_t* out_slots, float* out_weights,
-                        hipStream_t stream);
+                        int64_t out_rows_b, hipStream_t stream, bool dry_run = false);
 
 int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targets,
                         int32_t batch, int32_t tokens, float lr,
@@ -194,7 +212,7 @@ int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targ
                         float* retrieved, int32_t* out_slots, float* out_weights,
                         hipStream_t stream) {
   return forward_impl(h, queries, targets, nullptr, batch, tokens, lr, past, next, retrieved,
-                      out_slots, out_weights, stream);
+                      out_slots, out_weights, 0, stream);
 }
 
 int fwpkm_forward_chunk_weighted(fwpkm_handle* h, const float* queries, const float* targets,
@@ -203,7 +221,117 @@ int fwpkm_forward_chunk_weighted(fwpkm_handle* h, const float* queries, const fl
                                  float* retrieved, int32_t* out_slots, float* out_weights,
                                  hipStream_t stream) {
   return forward_impl(h, queries, targets, token_weights, batch, tokens, lr, past, next, retrieved,
-                      out_slots, out_weights, stream);
+                      out_slots, out_weights, 0, stream);
+}
+
+size_t fwpkm_sequence_workspace_bytes(const fwpkm_config* cfg, int32_t batch, int32_t seq) {
+  if (check_config(cfg) != FWPKM_OK) return 0;
+  if (batch < 1 || seq < 1) {
+    fail(FWPKM_ERR_INVALID_ARG, "batch and seq must be >= 1 (got %d, %d)", batch, seq);
+    return 0;
+  }
+  return seq_layout(*cfg, batch, seq).total;
+}
+
+int fwpkm_forward_sequence(fwpkm_handle* h, const float* x, const float* w_in,
+                           const float* w_gate, const float* b_gate, int32_t batch, int32_t seq,
+                           float lr, const fwpkm_state* past, const fwpkm_state* next, float* out,
+                           int32_t* out_slots, float* out_weights, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  // ---------------------------------------------------------- validation
+  if (!h) return fail(FWPKM_ERR_INVALID_ARG, "handle is NULL");
+  const fwpkm_config& c = h->cfg;
+  if (!x || !w_in || !w_gate || !out) return fail(FWPKM_ERR_INVALID_ARG, "x, w_in, w_gate and out must be non-NULL");
+  if (!workspace) return fail(FWPKM_ERR_INVALID_ARG, "workspace is NULL");
+  if (!past || !next) return fail(FWPKM_ERR_INVALID_ARG, "past_state and next_state must be non-NULL");
+  if (batch < 1 || batch > c.max_batch) return fail(FWPKM_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, c.max_batch);
+  if (seq < 1) return fail(FWPKM_ERR_INVALID_ARG, "seq must be >= 1 (got %d)", seq);
+  const int H = c.num_heads, C = c.chunk_size, k = c.topk;
+  const int64_t D = (int64_t)H * c.dim_v, M = (int64_t)batch * seq;
+  const int64_t Nrows = (int64_t)H * (c.dim_qk + c.dim_v);
+  if (M > ((int64_t)1 << 30))
+    return fail(FWPKM_ERR_UNSUPPORTED, "batch * seq = %lld tokens is more than 2^30", (long long)M);
+  const SeqLayout L = seq_layout(c, batch, seq);
+  if (workspace_bytes < L.total)
+    return fail(FWPKM_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+
+  char* ws = static_cast<char*>(workspace);
+  float* q_all = reinterpret_cast<float*>(ws + L.q);
+  float* y_all = reinterpret_cast<float*>(ws + L.y);
+  float* tw_last = reinterpret_cast<float*>(ws + L.tw);
+  auto rng = [](const void* p, int64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, p ? a + (uintptr_t)bytes : a};
+  };
+  const Range rx = rng(x, 4 * M * D), rwi = rng(w_in, 4 * Nrows * D), rwg = rng(w_gate, 4 * (int64_t)H * D);
+  const Range rbg = rng(b_gate, 4 * (int64_t)H), rout = rng(out, 4 * M * D), rws = rng(workspace, (int64_t)L.total);
+  const Range rsl = rng(out_slots, 4 * M * H * k), rwt = rng(out_weights, 4 * M * H * k);
+  const int n = c.sqrt_slots, half = c.dim_qk / 2;
+  const int64_t sk = (int64_t)H * n * half, sv = (int64_t)H * n * n * c.dim_v;
+  const Range tables[6] = {table_range(past->k1, past->batch_stride_k, sk, batch),
+                           table_range(past->k2, past->batch_stride_k, sk, batch),
+                           table_range(past->v, past->batch_stride_v, sv, batch),
+                           table_range(next->k1, next->batch_stride_k, sk, batch),
+                           table_range(next->k2, next->batch_stride_k, sk, batch),
+                           table_range(next->v, next->batch_stride_v, sv, batch)};
+  // everything the call writes (out, the selections, the workspace, next_state)
+  // must stay clear of what it reads afterwards (x, the weights, the state)
+  for (const Range& a : {rx, rwi, rwg, rbg}) {
+    if (a.lo == a.hi) continue;
+    for (const Range& b : {rout, rws, rsl, rwt, tables[3], tables[4], tables[5]})
+      if (b.lo != b.hi && overlap(a, b)) return fail(FWPKM_ERR_ALIAS, "an output or the workspace overlaps x or a weight");
+  }
+  for (const Range& b : {rout, rsl, rwt}) {
+    if (b.lo == b.hi) continue;
+    if (overlap(b, rws)) return fail(FWPKM_ERR_ALIAS, "an output overlaps the workspace");
+  }
+  for (const Range& t : tables)
+    if (overlap(t, rws)) return fail(FWPKM_ERR_ALIAS, "the workspace overlaps a state table");
+
+  const int nchunks = (seq + C - 1) / C;
+  auto chunk_call = [&](int ci, bool dry) {
+    const int c0 = ci * C, cc = std::min(C, seq - c0);
+    const int64_t rows0 = (int64_t)batch * c0 * H;     // rows of the chunks before this one
+    return forward_impl(h, q_all + rows0 * c.dim_qk, y_all + rows0 * c.dim_v,
+                        ci == nchunks - 1 ? tw_last : nullptr, batch, cc, lr,
+                        ci == 0 ? past : next, next, out + (int64_t)c0 * D,
+                        out_slots ? out_slots + (int64_t)c0 * H * k : nullptr,
+                        out_weights ? out_weights + (int64_t)c0 * H * k : nullptr,
+                        (int64_t)seq * H, stream, dry);
+  };
+  // the first and the last chunk calls cover every pointer and size the loop uses
+  int rc = chunk_call(0, true);
+  if (rc == FWPKM_OK && nchunks > 1) rc = chunk_call(nchunks - 1, true);
+  if (rc != FWPKM_OK) return rc;
+
+  // ---------------------------------------------------------- enqueue
+  fwpkm::SeqArgs sa{};
+  sa.x = x;
+  sa.w_in = w_in;
+  sa.w_gate = w_gate;
+  sa.b_gate = b_gate;
+  sa.q_all = q_all;
+  sa.y_all = y_all;
+  sa.tw_last = tw_last;
+  sa.out = out;
+  sa.B = batch;
+  sa.S = seq;
+  sa.D = (int)D;
+  sa.H = H;
+  sa.dqk = c.dim_qk;
+  sa.dv = c.dim_v;
+  sa.C = C;
+  sa.Nq = H * c.dim_qk;
+  sa.Nv = H * c.dim_v;
+  using fwpkm::LaunchTiming;
+  hipError_t e = timed(h, 8, [&](const LaunchTiming* tm) { return fwpkm::launch_kf_project(sa, stream, tm); });
+  if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "projection kernel: %s", hipGetErrorString(e));
+  for (int ci = 0; ci < nchunks; ++ci)
+    if ((rc = chunk_call(ci, false)) != FWPKM_OK) return rc;
+  e = timed(h, 9, [&](const LaunchTiming* tm) { return fwpkm::launch_kf_gate(sa, stream, tm); });
+  if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "gate kernel: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return FWPKM_OK;
 }
 
 void fwpkm_destroy(fwpkm_handle* h) {
@@ -255,11 +383,14 @@ int fwpkm_profile_read(fwpkm_handle* h, double* ms, int64_t* launches) {
   return FWPKM_OK;
 }
 
+// out_rows_b: (token, head) rows between sequences in retrieved, out_slots
+// and out_weights (0: tokens * H, the packed layout of a chunk call).
+// dry_run: validate only, enqueue nothing.
 static int forward_impl(fwpkm_handle* h, const float* queries, const float* targets,
                         const float* token_weights, int32_t batch, int32_t tokens, float lr,
                         const fwpkm_state* past, const fwpkm_state* next,
                         float* retrieved, int32_t* out_slots, float* out_weights,
-                        hipStream_t stream) {
+                        int64_t out_rows_b, hipStream_t stream, bool dry_run) {
   // ---------------------------------------------------------- validation
   if (!h) return fail(FWPKM_ERR_INVALID_ARG, "handle is NULL");
   const fwpkm_config& c = h->cfg;
@@ -302,14 +433,17 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
         if (overlap(a, b)) return fail(FWPKM_ERR_ALIAS, "next_state partially overlaps past_state");
   }
   const int64_t rows = (int64_t)batch * tokens * H;
+  if (out_rows_b == 0) out_rows_b = (int64_t)tokens * H;
+  // rows spanned by the outputs: the last sequence's rows end tokens * H past its start
+  const int64_t orows = (int64_t)(batch - 1) * out_rows_b + (int64_t)tokens * H;
   const Range rq = {reinterpret_cast<uintptr_t>(queries), reinterpret_cast<uintptr_t>(queries + rows * c.dim_qk)};
   const Range ry = {reinterpret_cast<uintptr_t>(targets), reinterpret_cast<uintptr_t>(targets + rows * c.dim_v)};
-  const Range rr = {reinterpret_cast<uintptr_t>(retrieved), reinterpret_cast<uintptr_t>(retrieved + rows * c.dim_v)};
+  const Range rr = {reinterpret_cast<uintptr_t>(retrieved), reinterpret_cast<uintptr_t>(retrieved + orows * c.dim_v)};
   const Range rw = {reinterpret_cast<uintptr_t>(token_weights),
                     reinterpret_cast<uintptr_t>(token_weights + (token_weights ? rows : 0))};
   const Range outs[3] = {rr,
-                         {reinterpret_cast<uintptr_t>(out_slots), reinterpret_cast<uintptr_t>(out_slots + (out_slots ? rows * k : 0))},
-                         {reinterpret_cast<uintptr_t>(out_weights), reinterpret_cast<uintptr_t>(out_weights + (out_weights ? rows * k : 0))}};
+                         {reinterpret_cast<uintptr_t>(out_slots), reinterpret_cast<uintptr_t>(out_slots + (out_slots ? orows * k : 0))},
+                         {reinterpret_cast<uintptr_t>(out_weights), reinterpret_cast<uintptr_t>(out_weights + (out_weights ? orows * k : 0))}};
   const Range ins[9] = {rq, ry, pk1, pk2, pv, nk1, nk2, nv, rw};
   for (int i = 0; i < 3; ++i) {
     if (outs[i].lo == outs[i].hi) continue;
@@ -321,6 +455,7 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
   for (const Range& b : {nk1, nk2, nv})
     if (overlap(b, rq) || overlap(b, ry) || (rw.lo != rw.hi && overlap(b, rw)))
       return fail(FWPKM_ERR_ALIAS, "next_state overlaps queries, targets or token weights");
+  if (dry_run) return FWPKM_OK;
 
   // ---------------------------------------------------------- workspace
   int dev = -1;
@@ -386,6 +521,7 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
   a.stride_k = next->batch_stride_k;
   a.stride_v = next->batch_stride_v;
   a.retrieved = retrieved;
+  a.out_rows_b = out_rows_b;
   a.out_slots = out_slots;
   a.out_weights = out_weights;
   a.half_o = reinterpret_cast<float*>(ws + L.half_o);

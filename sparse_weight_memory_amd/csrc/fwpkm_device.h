@@ -48,7 +48,9 @@ struct ChunkArgs {
   int64_t stride_k;   // elements between sequences
   int64_t stride_v;
   // outputs
-  float* retrieved;   // [B, T, H, dv]
+  float* retrieved;   // [B, ., H, dv]: row (b, t, h) at b * out_rows_b + t * H + h
+  int64_t out_rows_b; // (token, head) rows between sequences in retrieved / out_slots /
+                      // out_weights: T * H for a chunk call, S * H inside a sequence
   int* out_slots;     // nullable [B, T, H, k]
   float* out_weights; // nullable [B, T, H, k]
   // workspace
@@ -77,6 +79,30 @@ struct ChunkArgs {
   float* addr_tok;     // [U, 2, T, 2] per token: softmax shift m (dot) and 1 / softmax sum
   float* addr_ell;     // [U, 2, n] log marginal usage of each sub-key
 };
+
+// The sequence-level layer around the chunk step (queries/values projected
+// from model-width tokens, lookahead targets, gated output).
+struct SeqArgs {
+  const float* x;       // [B, S, D] tokens, D = H * dv
+  const float* w_in;    // [Nq + Nv, D]: query rows (head-major), then value rows
+  const float* w_gate;  // [H, D]
+  const float* b_gate;  // nullable [H]
+  float* q_all;         // chunk-major queries: chunk c holds [B, Cc, H, dqk]
+  float* y_all;         // chunk-major targets (value of the next token): [B, Cc, H, dv]
+  float* tw_last;       // [B, C_last, H] token weights of the last chunk
+  float* out;           // [B, S, D]: memory reads, then the gated output in place
+  int B, S, D, H, dqk, dv;
+  int C;                // chunk size (the last chunk may be shorter)
+  int Nq, Nv;           // H * dqk, H * dv
+};
+
+// Row of token (b, t) in the chunk-major layout: chunk c = t / C starts after
+// c full chunks of B * C rows and holds B sequences of Cc tokens each.
+__device__ __forceinline__ int64_t seq_chunk_row(const SeqArgs& s, int b, int t) {
+  const int c = t / s.C, tt = t - c * s.C;
+  const int cc = min(s.C, s.S - c * s.C);
+  return (int64_t)c * s.B * s.C + (int64_t)b * cc + tt;
+}
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

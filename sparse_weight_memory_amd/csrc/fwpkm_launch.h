@@ -49,6 +49,11 @@ hipError_t launch_ke_stats(const ChunkArgs& a, hipStream_t s, const LaunchTiming
 hipError_t launch_ke_grad(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 hipError_t launch_ke_apply(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 
+// KF: the sequence-level layer: projection GEMM with lookahead targets (and
+// the last-token prep, timed as one span), then the gated output.
+hipError_t launch_kf_project(const SeqArgs& s, hipStream_t st, const LaunchTiming* tm);
+hipError_t launch_kf_gate(const SeqArgs& s, hipStream_t st, const LaunchTiming* tm);
+
 // KD: per segment mean gradient and in-place SGD on V, K1 and K2 rows.
 hipError_t launch_kd(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 

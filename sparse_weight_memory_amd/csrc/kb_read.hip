@@ -217,15 +217,16 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   }
 
   // ---- outputs of the read
-  float4* ret = reinterpret_cast<float4*>(a.retrieved + io * a.dv);
+  const int64_t ob = (int64_t)b * a.out_rows_b + (int64_t)t * a.H + hh;   // output row
+  float4* ret = reinterpret_cast<float4*>(a.retrieved + ob * a.dv);
 #pragma unroll
   for (int j = 0; j < VR; ++j) {
     const int c = lane + 64 * j;
     if (c < dv4) ret[c] = acc[j];
   }
   if (lane < k) {
-    if (a.out_slots) a.out_slots[io * k + lane] = sel_s;
-    if (a.out_weights) a.out_weights[io * k + lane] = w;
+    if (a.out_slots) a.out_slots[ob * k + lane] = sel_s;
+    if (a.out_weights) a.out_weights[ob * k + lane] = w;
   }
   if (!WRITE) return;
 

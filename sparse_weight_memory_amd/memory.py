@@ -200,3 +200,74 @@ class Memory:
         if return_selection:
             return retrieved, next, slots, weights
         return retrieved, next
+
+    def sequence_workspace_bytes(self, batch: int, seq: int) -> int:
+        n = int(self._lib.fwpkm_sequence_workspace_bytes(ctypes.byref(self._c_cfg), int(batch), int(seq)))
+        if n == 0:
+            raise FwPKMError(_lib.ERR_INVALID_ARG, _lib.last_error())
+        return n
+
+    def forward_sequence(self, x: torch.Tensor, w_in: torch.Tensor, w_gate: torch.Tensor,
+                         b_gate: Optional[torch.Tensor], lr: float, past: State,
+                         next: Optional[State] = None, out: Optional[torch.Tensor] = None,
+                         return_selection: bool = False,
+                         workspace: Optional[torch.Tensor] = None):
+        """Whole sequences: (out [B, S, D], next state), D = H * d_v.
+
+        x [B, S, D]; w_in [H*d_qk + H*d_v, D] (query rows of every head, then
+        value rows); w_gate [H, D]; b_gate [H] or None.  Each token's target
+        is the next token's value; the last token reads without writing; the
+        sequence runs through the chunk step chunk_size tokens at a time and
+        out = g * read + (1 - g) * x per head with g = sigmoid(w_gate x + b)
+        (fwpkm_forward_sequence).  workspace: a device byte tensor of at least
+        sequence_workspace_bytes(B, S) bytes, or None to allocate one.
+        """
+        cfg = self.cfg
+        H = cfg.num_heads
+        D = H * cfg.dim_v
+        _check_tensor("x", x)
+        _check_tensor("w_in", w_in)
+        _check_tensor("w_gate", w_gate)
+        if x.dim() != 3 or x.shape[2] != D:
+            raise ValueError(f"x must be [B, S, {D}]")
+        B, S = x.shape[0], x.shape[1]
+        if tuple(w_in.shape) != (H * (cfg.dim_qk + cfg.dim_v), D):
+            raise ValueError(f"w_in must be [{H * (cfg.dim_qk + cfg.dim_v)}, {D}]")
+        if tuple(w_gate.shape) != (H, D):
+            raise ValueError(f"w_gate must be [{H}, {D}]")
+        if b_gate is not None:
+            _check_tensor("b_gate", b_gate)
+            if b_gate.numel() != H:
+                raise ValueError(f"b_gate must have {H} entries")
+        if next is None:
+            next = empty_state(cfg, B, x.device)
+        c_past = _c_state(past, cfg)
+        c_next = _c_state(next, cfg)
+        if out is None:
+            out = torch.empty((B, S, D), device=x.device)
+        else:
+            _check_tensor("out", out)
+            if tuple(out.shape) != (B, S, D):
+                raise ValueError(f"out must be [{B}, {S}, {D}]")
+        need = self.sequence_workspace_bytes(B, S)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        elif workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous device tensor of >= {need} bytes")
+        slots = weights = None
+        if return_selection:
+            slots = torch.empty((B, S, H, cfg.topk), device=x.device, dtype=torch.int32)
+            weights = torch.empty((B, S, H, cfg.topk), device=x.device)
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = self._lib.fwpkm_forward_sequence(
+            self._h, x.data_ptr(), w_in.data_ptr(), w_gate.data_ptr(),
+            b_gate.data_ptr() if b_gate is not None else None, B, S, float(lr),
+            ctypes.byref(c_past), ctypes.byref(c_next), out.data_ptr(),
+            slots.data_ptr() if slots is not None else None,
+            weights.data_ptr() if weights is not None else None,
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+        if rc != _lib.OK:
+            raise FwPKMError(rc, _lib.last_error())
+        if return_selection:
+            return out, next, slots, weights
+        return out, next

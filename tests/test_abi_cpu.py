@@ -208,3 +208,63 @@ def test_addressing_workspace_only_when_enabled(fwpkm_lib):
     on = fwpkm_lib.fwpkm_workspace_bytes(ctypes.byref(cfg(addr_weight=0.1)))
     units, tokens, n, half = 2, 64, 32, 32
     assert on - off >= 4 * units * 2 * (tokens * n + n * half)
+
+
+# ------------------------------------------------------- sequence entry
+# cfg(): n 32, d_qk 64, d_v 64, k 4, chunk 64, one head, max_batch 2: D = 64
+X, WIN, WG, BG = 0xC0_0000_0000, 0xC8_0000_0000, 0xD0_0000_0000, 0xD8_0000_0000
+OUT, WS = 0xE0_0000_0000, 0xF0_0000_0000
+
+
+def seq_ws(lib, batch=2, seq=100, **kw):
+    return lib.fwpkm_sequence_workspace_bytes(ctypes.byref(cfg(**kw)), batch, seq)
+
+
+def fwd_s(lib, h, x=X, out=OUT, ws=WS, ws_bytes=None, batch=2, seq=100, lr=1.0, nxt=None,
+          slots=None, w=None, b_gate=BG):
+    past = state(PK1, PK2, PV)
+    nxt = nxt if nxt is not None else state(PK1, PK2, PV)
+    ws_bytes = seq_ws(lib, batch if 1 <= batch <= 2 else 2, max(seq, 1)) if ws_bytes is None else ws_bytes
+    return lib.fwpkm_forward_sequence(h, x, WIN, WG, b_gate, batch, seq, lr, ctypes.byref(past),
+                                      ctypes.byref(nxt), out, slots, w, ws, ws_bytes, None)
+
+
+def test_sequence_workspace_bytes(fwpkm_lib):
+    L = fwpkm_lib
+    # queries and targets of every token, plus the last chunk's weights
+    need = seq_ws(L, 2, 100)
+    assert need >= 4 * 2 * 100 * (64 + 64) + 4 * 2 * 64
+    assert seq_ws(L, 2, 200) > need
+    assert seq_ws(L, 0, 100) == 0 and seq_ws(L, 2, 0) == 0
+    assert L.fwpkm_sequence_workspace_bytes(ctypes.byref(cfg(sqrt_slots=0)), 2, 10) == 0
+
+
+def test_sequence_argument_errors(fwpkm_lib, handle):
+    L = fwpkm_lib
+    E = _lib.ERR_INVALID_ARG
+    assert fwd_s(L, None) == E
+    assert fwd_s(L, handle, x=None) == E
+    assert fwd_s(L, handle, out=None) == E
+    assert fwd_s(L, handle, ws=None) == E
+    assert fwd_s(L, handle, batch=3) == E
+    assert fwd_s(L, handle, seq=0) == E
+    assert fwd_s(L, handle, lr=math.nan) == E
+    assert fwd_s(L, handle, ws_bytes=seq_ws(L) - 1) == E
+    assert "workspace" in L.fwpkm_last_error().decode()
+
+
+def test_sequence_alias_errors(fwpkm_lib, handle):
+    L = fwpkm_lib
+    A = _lib.ERR_ALIAS
+    assert fwd_s(L, handle, out=X + 4 * 64) == A                  # out over x
+    assert fwd_s(L, handle, out=WIN + 4) == A                     # out over the projection
+    assert fwd_s(L, handle, ws=X + 4 * 8) == A                    # workspace over x
+    assert fwd_s(L, handle, ws=PV + 4 * 1024) == A                # workspace over the state
+    assert fwd_s(L, handle, out=WS + 4 * 64) == A                 # out over the workspace
+    assert fwd_s(L, handle, nxt=state(NK1, NK2, X)) == A          # next state over x
+    assert fwd_s(L, handle, slots=BG) == A                        # selections over the gate bias
+    # everything apart: passes validation, then needs the device
+    import torch
+    if not torch.cuda.is_available():
+        assert fwd_s(L, handle) == _lib.ERR_HIP
+        assert fwd_s(L, handle, b_gate=None) == _lib.ERR_HIP

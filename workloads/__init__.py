@@ -10,11 +10,14 @@ from .configs import CONFIGS, WorkloadConfig, get_config
 from .generate import (
     ChunkInputs,
     InitialTables,
+    LayerWeights,
     chunk_inputs,
     draw_normal,
     draw_queries,
     draw_targets,
+    draw_tokens,
     initial_tables,
+    layer_weights,
 )
 
 __all__ = [
@@ -23,9 +26,12 @@ __all__ = [
     "get_config",
     "ChunkInputs",
     "InitialTables",
+    "LayerWeights",
     "chunk_inputs",
     "draw_normal",
     "draw_queries",
     "draw_targets",
+    "draw_tokens",
     "initial_tables",
+    "layer_weights",
 ]

@@ -4,7 +4,9 @@ Every array comes from numpy's PCG64 generator seeded with
 ``1000 * config.index + stream``; streams are
 
     0 = K1 sub-keys, 1 = K2 sub-keys, 2 = V, 3 = queries, 4 = targets,
-    5 = cluster centres, 6 = cluster assignment then cluster noise.
+    5 = cluster centres, 6 = cluster assignment then cluster noise,
+    7 = sequence-layer tokens (centres, then assignment and noise),
+    8 = sequence-layer projection rows, 9 = gate weights then gate biases.
 
 Values are drawn in float64 in C order, scaled in float64 and cast to fp32
 once.  Large arrays are drawn block by block from one generator, which
@@ -13,7 +15,9 @@ yields the same numbers as a single draw.
 Layouts:
   * initial tables: one set per head, shared by every sequence of the batch
     (k1, k2: [H, n, d_qk/2]; v: [H, n*n, d_v]);
-  * queries [B, T, H, d_qk], targets [B, T, H, d_v], T = tokens per pass.
+  * queries [B, T, H, d_qk], targets [B, T, H, d_v], T = tokens per pass;
+  * sequence layer: tokens [B, T, D] with D = H * d_v, projection rows
+    [H*d_qk + H*d_v, D], gate weights [H, D] and biases [H].
 Targets stand in for the lookahead value vectors (each query paired with
 the next token's value); the caller would shift them, so here they are
 simply independent N(0, 1) draws aligned with the queries.
@@ -34,6 +38,9 @@ STREAM_Q = 3
 STREAM_Y = 4
 STREAM_CENTRES = 5
 STREAM_ASSIGN = 6
+STREAM_TOKENS = 7
+STREAM_W_IN = 8
+STREAM_GATE = 9
 
 _BLOCK = 1 << 22  # elements per block when drawing large arrays
 
@@ -126,3 +133,42 @@ def expand_tables(tables: InitialTables, batch: int) -> InitialTables:
     def rep(a):
         return np.repeat(a[None], batch, axis=0).reshape((-1,) + a.shape[1:])
     return InitialTables(k1=rep(tables.k1), k2=rep(tables.k2), v=rep(tables.v))
+
+
+def draw_tokens(cfg: WorkloadConfig) -> np.ndarray:
+    """Model-width tokens for the sequence layer, [B, T, D] fp32, D = H*d_v.
+
+    Clustered workloads: unit-norm centres in D dimensions, per-coordinate
+    noise sigma/sqrt(D) (the query recipe, one level up); otherwise N(0, 1/D)
+    per coordinate (unit expected norm)."""
+    B, T, D = cfg.batch, cfg.tokens_per_pass, cfg.heads * cfg.dim_v
+    rng = make_rng(cfg, STREAM_TOKENS)
+    if cfg.query_kind != "clustered":
+        return draw_normal(rng, (B, T, D), 1.0 / np.sqrt(D))
+    centres = rng.standard_normal((cfg.clusters, D))
+    centres /= np.linalg.norm(centres, axis=1, keepdims=True)
+    assign = rng.integers(0, cfg.clusters, size=B * T)
+    out = np.empty((B * T, D), dtype=np.float32)
+    noise_std = cfg.cluster_sigma / np.sqrt(D)
+    rows_per_block = max(1, _BLOCK // D)
+    for r0 in range(0, B * T, rows_per_block):
+        r1 = min(B * T, r0 + rows_per_block)
+        out[r0:r1] = centres[assign[r0:r1]] + rng.standard_normal((r1 - r0, D)) * noise_std
+    return out.reshape(B, T, D)
+
+
+@dataclasses.dataclass
+class LayerWeights:
+    w_in: np.ndarray    # [H*d_qk + H*d_v, D] fp32, N(0, 1/D)
+    w_gate: np.ndarray  # [H, D] fp32, N(0, 1/D)
+    b_gate: np.ndarray  # [H] fp32, N(0, 1)
+
+
+def layer_weights(cfg: WorkloadConfig) -> LayerWeights:
+    """Stand-in (random, untrained) weights of the sequence layer."""
+    H, D = cfg.heads, cfg.heads * cfg.dim_v
+    w_in = draw_normal(make_rng(cfg, STREAM_W_IN), (H * (cfg.dim_qk + cfg.dim_v), D), 1.0 / np.sqrt(D))
+    grng = make_rng(cfg, STREAM_GATE)
+    w_gate = draw_normal(grng, (H, D), 1.0 / np.sqrt(D))
+    b_gate = draw_normal(grng, (H,))
+    return LayerWeights(w_in=w_in, w_gate=w_gate, b_gate=b_gate)
