@@ -88,6 +88,10 @@ def parse():
     ap.add_argument("--addr-weight", type=float, default=0.0,
                     help="weight of the marginal-entropy addressing loss on the sub-keys "
                          "(0: the plain step)")
+    ap.add_argument("--sequence", action="store_true",
+                    help="time the sequence layer instead (fwpkm_forward_sequence): model-width "
+                         "tokens projected to queries and lookahead targets, the chained chunk "
+                         "step, and the gated output, with random stand-in layer weights")
     ap.add_argument("--eager", action="store_true",
                     help="launch every chunk from Python instead of replaying a HIP graph")
     ap.add_argument("--no-profile-pass", action="store_true",
@@ -138,6 +142,15 @@ def algorithmic_cost(cfg, kernel, tokens, uniq_v, uniq_k, addr=False):
     if kernel == "addr_apply":
         # key gradients in, key tables read and written
         return 3 * keys, 0.0
+    D = cfg.heads * cfg.dim_v
+    Nf = cfg.heads * (cfg.dim_qk + cfg.dim_v)
+    if kernel == "project":
+        # tokens and projection rows in, queries and targets out; launched once
+        # per sequence call, so `tokens` is every token of the call here
+        return f * (tokens * D + Nf * D + tokens * Nf), 2.0 * tokens * D * Nf
+    if kernel == "gate":
+        # tokens and memory reads in, outputs out (gate rows stay in cache)
+        return f * 3 * tokens * D, 2.0 * tokens * D * cfg.heads
     if kernel == "read":
         # k gathered value rows + the target row read + the retrieved row written
         return f * tokens * (cfg.topk * cfg.dim_v + 2 * cfg.dim_v), 0.0
@@ -185,6 +198,35 @@ def cpu_baseline(cfg, tables, Q, Y, seconds):
                       f"{dt:.1f} s"}
 
 
+def cpu_baseline_sequence(cfg, tables, x, lw, seconds):
+    """The oracle's sequence layer, single-threaded, on sequence 0."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    from oracle import fwpkm_sequence as OS
+
+    st = {"k1": tables.k1[:1].copy(), "k2": tables.k2[:1].copy(), "v": tables.v[:1].copy()}
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    tokens = passes = 0
+    t0 = time.perf_counter()
+    try:
+        while True:
+            _, st, _ = OS.forward_sequence(st, x[:1], lw.w_in, lw.w_gate, lw.b_gate, cfg.lr,
+                                           cfg.topk, cfg.chunk, cfg.eps)
+            tokens += x.shape[1]
+            passes += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} pass(es) of sequence 0 ({x.shape[1]} tokens, 1 of {cfg.batch} "
+                      f"sequences; sequences are independent), float64 numpy, 1 thread, {dt:.1f} s"}
+
+
 def main():
     args = parse()
     if args.copy_probe_mib:
@@ -200,7 +242,8 @@ def main():
     import torch
 
     from sparse_weight_memory_amd import Config, Memory, State, _lib
-    from workloads import draw_queries, draw_targets, get_config, initial_tables
+    from workloads import (draw_queries, draw_targets, draw_tokens, get_config, initial_tables,
+                           layer_weights)
 
     key = int(args.workload) if args.workload.isdigit() else args.workload
     cfg = get_config(key)
@@ -246,6 +289,27 @@ def main():
                 out.append(r[2])
         return out
 
+    X = lw = None
+    if args.sequence:
+        # the sequence layer: model-width tokens [B, S, D] instead of ready
+        # queries and targets, random stand-in layer weights
+        X = draw_tokens(cfg)
+        lw = layer_weights(cfg)
+        xd = torch.from_numpy(X).to(dev)
+        w_in, w_gate, b_gate = (torch.from_numpy(a).to(dev) for a in (lw.w_in, lw.w_gate, lw.b_gate))
+        seq_out = torch.empty_like(xd)
+        ws = torch.empty(mem.sequence_workspace_bytes(B, cfg.tokens_per_pass), dtype=torch.uint8,
+                         device=dev)
+        del qd, yd
+
+        def step(select=False):  # noqa: F811
+            r = mem.forward_sequence(xd, w_in, w_gate, b_gate, cfg.lr, st, next=st, out=seq_out,
+                                     return_selection=select, workspace=ws)
+            if not select:
+                return []
+            slots = r[2]
+            return [slots[:, c * C:(c + 1) * C] for c in range(cfg.chunks)]
+
     print(f"[bench] warmup {args.warmup} step(s)", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -282,7 +346,8 @@ def main():
     value = tokens_per_step / (ms_step * 1e-3)
 
     result = {
-        "metric": "tokens/s for chained FwPKM read+update chunk",
+        "metric": ("tokens/s for the FwPKM sequence layer (projection, chained chunks, gate)"
+                   if args.sequence else "tokens/s for chained FwPKM read+update chunk"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -302,7 +367,10 @@ def main():
                    "parallelism": "single GPU",
                    "launch": "eager" if graph is None else "hip graph of one step",
                    "token_weights": "last token of each sequence 0, others 1" if args.weighted else None,
-                   "addr_weight": args.addr_weight},
+                   "addr_weight": args.addr_weight,
+                   "layer": ("sequence: tokens [B, S, H*d_v] -> fp32 projection to queries and "
+                             "lookahead targets -> chunks -> gated output; random stand-in "
+                             "weights") if args.sequence else None},
     }
 
     if not args.no_profile_pass:
@@ -331,7 +399,9 @@ def main():
             if n == 0:
                 continue
             avg_us = 1e3 * ms / n
-            byts, flops = algorithmic_cost(cfg, name, tokens_launch, uv, uk, args.addr_weight != 0)
+            per_call = name in ("project", "gate")      # once per sequence call
+            byts, flops = algorithmic_cost(cfg, name, B * cfg.tokens_per_pass if per_call else tokens_launch,
+                                           uv, uk, args.addr_weight != 0)
             kernels[name] = {"avg_us": avg_us, "launches": n,
                              "alg_bytes": byts, "alg_gbps": byts / (avg_us * 1e3) if byts else None,
                              "alg_tflops": flops / (avg_us * 1e6) if flops else None}
@@ -340,14 +410,14 @@ def main():
                                             "pairs": B * H * C * cfg.topk}
         dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
         kd = kernels[dom]
-        if kd["alg_tflops"] is not None and dom in ("score", "addr_grad"):
+        if kd["alg_tflops"] is not None and dom in ("score", "addr_grad", "project"):
             roof = {"bound": "mfma", "achieved": kd["alg_tflops"], "peak": FP32_MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s"}
         else:
             roof = {"bound": "hbm", "achieved": kd["alg_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] / roof["peak"]
         # the committed counters were taken on the plain step
-        plain = args.addr_weight == 0 and not args.weighted
+        plain = args.addr_weight == 0 and not args.weighted and not args.sequence
         traffic = measured_traffic(cfg.name) if plain else {}
         for name in kernels:
             kernels[name]["hbm_bytes_counted"] = traffic.get(name)
@@ -357,7 +427,8 @@ def main():
 
     if not args.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, tables, Q, Y, args.cpu_seconds)
+        result["cpu_baseline"] = (cpu_baseline_sequence(cfg, tables, X, lw, args.cpu_seconds)
+                                  if args.sequence else cpu_baseline(cfg, tables, Q, Y, args.cpu_seconds))
 
     print(json.dumps(result), flush=True)
 
