@@ -75,3 +75,21 @@ def test_zero_addressing_weight_is_the_plain_step():
     assert torch.equal(outs[0][0], outs[1][0])
     for a, b in zip(outs[0][1], outs[1][1]):
         assert torch.equal(a, b)
+
+
+def test_addressing_with_wide_sub_key_tables():
+    """n = 1024 sub-keys (four 256-wide load batches per score row), 4 heads
+    of d_h 64, top-16: the statistics kernels' row loops and the gradient
+    tiles at more than one block per dimension."""
+    need_gpu()
+    B, H, C, n, half, dv, k = 1, 4, 96, 1024, 64, 32, 16
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=C, num_heads=H,
+               max_batch=B, addr_weight=0.3)
+    rng = np.random.default_rng(86)
+    U = B * H
+    st = {"k1": (rng.standard_normal((U, n, half)) / np.sqrt(half)).astype(np.float32),
+          "k2": (rng.standard_normal((U, n, half)) / np.sqrt(half)).astype(np.float32),
+          "v": (rng.standard_normal((U, n * n, dv)) * 0.14).astype(np.float32)}
+    q = rng.standard_normal((B, C, H, 2 * half)).astype(np.float32)
+    y = rng.standard_normal((B, C, H, dv)).astype(np.float32)
+    compare_chunk(mem, st, q, y, 1.0, label="addr-n1024")

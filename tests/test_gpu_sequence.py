@@ -148,3 +148,13 @@ def test_sequence_at_the_chained_workload_shape():
         assert_close(f"chained next {name}", nxt[name][:1], o_nxt[name], RTOL_CHAIN, ATOL_CHAIN)
     # the other sequences took their own steps
     assert not np.array_equal(nxt["v"][1], st["v"][1])
+
+
+def test_sequence_with_four_heads():
+    """Four heads of d_qk 64 / d_v 32 (D = 128, 384 projection rows over
+    three column tiles), chunks of 48, 2 x 200 tokens."""
+    need_gpu()
+    B, S, H, n, dqk, dv, k, C = 2, 200, 4, 64, 64, 32, 8, 48
+    mem = _mem(sqrt_slots=n, dim_qk=dqk, dim_v=dv, topk=k, chunk_size=C, num_heads=H, max_batch=B)
+    st, x, w_in, w_gate, b_gate = _case(1130, B, S, H, n, dqk, dv)
+    compare_sequence(mem, st, x, w_in, w_gate, b_gate, 1.0, "seq-4heads")
