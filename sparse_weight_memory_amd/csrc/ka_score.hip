@@ -83,7 +83,10 @@ __host__ __device__ inline int ka_query_width(int half, int blk) {
   return (ndq - 1) * share + ka_chunks<DC, PF>(half, blk) * DC;
 }
 
-template <int kDimChunk, int kPrefetch>
+// kFull: every multiplied chunk lies inside its dim share and d_h (the
+// shares tile d_h in whole chunks, and no ring padding is multiplied), so
+// the staging loads need no mask.
+template <int kDimChunk, int kPrefetch, bool kFull>
 __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a) {
   constexpr int kKPitch = Staging<kDimChunk, kPrefetch>::kKPitch;
   constexpr int kStageF4 = Staging<kDimChunk, kPrefetch>::kStageF4;
@@ -155,6 +158,18 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     lane_off[j] = (gk < a.n ? gk : 0) * half + min(dq * share + lane_ds, half - 4);
   }
   auto stage_load = [&](float4 (&dst)[kStageF4], int c) {
+    if constexpr (kFull) {
+      // ring loads past the last chunk re-read chunk 0 (never multiplied)
+      const int cofs = c < nchunks ? c * kDimChunk : 0;
+#pragma unroll
+      for (int j = 0; j < kStageF4; ++j) {
+        // through the native vector type: a copy of the float4 struct would
+        // go through memory
+        const v4f v = *reinterpret_cast<const v4f*>(kbase + lane_off[j] + cofs);
+        dst[j] = make_float4(v.x, v.y, v.z, v.w);
+      }
+      return;
+    }
     const bool ok = c < nchunks && c * kDimChunk + lane_ds < ds_lim;
     const unsigned int m = ok ? 0xFFFFFFFFu : 0u;    // masked, so the load is never skipped
     const int cofs = ok ? c * kDimChunk : 0;
@@ -382,14 +397,24 @@ namespace {
 
 constexpr size_t kLdsBytes = 160 * 1024;
 
-template <int DC, int PF>
-hipError_t launch_ka_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
+template <int DC, int PF, bool kFull>
+hipError_t launch_ka_full(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&ka_score_topk<DC, PF>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      reinterpret_cast<const void*>(&ka_score_topk<DC, PF, kFull>), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)kLdsBytes);
   if (attr != hipSuccess) return attr;
-  return fw_launch(ka_score_topk<DC, PF>, dim3(ka_grid(a)), dim3(kScoreWaves * kWave),
+  return fw_launch(ka_score_topk<DC, PF, kFull>, dim3(ka_grid(a)), dim3(kScoreWaves * kWave),
                    (uint32_t)ka_smem_bytes<DC, PF>(a.half, a.key_block), s, tm, a);
+}
+
+template <int DC, int PF>
+hipError_t launch_ka_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
+  // the kernel's own share / chunk arithmetic, on the host
+  const int ndq = kScoreWaves / (a.key_block / 16);
+  const int share = ((a.half + 16 * ndq - 1) / (16 * ndq)) * 16;
+  const int nchunks = (share + DC - 1) / DC;
+  const bool full = share % DC == 0 && ndq * share <= a.half && ka_chunks<DC, PF>(a.half, a.key_block) == nchunks;
+  return full ? launch_ka_full<DC, PF, true>(a, s, tm) : launch_ka_full<DC, PF, false>(a, s, tm);
 }
 
 }  // namespace
