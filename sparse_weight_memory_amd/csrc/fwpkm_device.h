@@ -164,6 +164,16 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
+// All ones if ok, else zero, through an empty asm: AND-ing a loaded value
+// with it masks the value without letting the compiler turn the mask into a
+// select, and the select into a branch around the load (every such branch
+// waits for its load alone).
+__device__ __forceinline__ unsigned int opaque_mask(bool ok) {
+  unsigned int m = ok ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(m));
+  return m;
+}
+
 // Butterfly sum over the wave (every lane gets the total, in one fixed order).
 template <typename T>
 __device__ __forceinline__ T wave_sum(T x) {

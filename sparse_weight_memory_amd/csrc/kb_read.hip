@@ -54,8 +54,10 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   const int64_t io = ((int64_t)(b * a.T + t) * a.H + hh);
   const int dv4 = a.dv >> 2;
 
-  // loads that do not depend on the selection go out first
-  const float qn = (a.mode == 0) ? a.qnorm[ut * 2] + a.qnorm[ut * 2 + 1] : 0.f;
+  // loads that do not depend on the selection go out first, all together:
+  // nothing here sits behind a branch (a load inside one is waited for on
+  // its own), values a lane or mode does not use are masked afterwards
+  const float qn = (a.qnorm[ut * 2] + a.qnorm[ut * 2 + 1]) * (a.mode == 0 ? 1.f : 0.f);
   // token-importance weight of this token's loss; 0 = read only, no write
   const float lam = (WRITE && a.tw) ? a.tw[io] : 1.0f;
   float4 yv[VR];
@@ -69,25 +71,54 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   // ---- 1. per-half best-k lists (lane m < k holds the m-th best), as
   // packed (ordering key, sub-key index) keys
   skey hk[2];
+  if (a.nblk == 1) {
+    // lanes past k re-read entry 0 and are masked to the empty key
+    const int li = lane < k ? lane : 0;
+    int ix[2];
+    float ov[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t base = (ut * 2 + h) * k;
+      ix[h] = a.half_i[base + li];
+      ov[h] = a.half_o[base + li];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const unsigned int m32 = opaque_mask(lane < k && ix[h] != kNoIndex);
+      const skey m = (skey)m32 << 32 | m32;
+      hk[h] = (pack_key(order_key(ov[h]), ix[h]) & m) | (kEmptyKey & ~m);
+    }
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int64_t base = (ut * 2 + h) * a.nblk * k;
-    if (a.nblk == 1) {
-      const int ix = lane < k ? a.half_i[base + lane] : kNoIndex;
-      hk[h] = ix == kNoIndex ? kEmptyKey : pack_key(order_key(a.half_o[base + lane]), ix);
-    } else {
+    if (a.nblk != 1) {
       // merge the per-block lists: the best k so far stay in lanes 0..k-1,
       // the next 64-k candidates fill lanes k..63, and a bitonic sort brings
       // the best k of both back to lanes 0..k-1
       const int nc = a.nblk * k;
       const int fresh = kWave - k;
+      // candidate pos + lane - k of a round; indices outside [0, nc) re-read
+      // an entry in range and are masked.  The next round's pair of loads is
+      // issued before this round's sort.
+      auto fetch = [&](int pos, int& ix, float& ov) {
+        const int c = min(max(pos + lane - k, 0), nc - 1);
+        ix = a.half_i[base + c];
+        ov = a.half_o[base + c];
+      };
+      int ixn;
+      float ovn;
+      fetch(0, ixn, ovn);
       skey x = kEmptyKey;
       for (int pos = 0; pos < nc; pos += fresh) {
+        const int ix = ixn;
+        const float ov = ovn;
+        fetch(pos + fresh < nc ? pos + fresh : pos, ixn, ovn);
         const int c = pos + lane - k;
-        if (lane >= k) {
-          const int ix = c < nc ? a.half_i[base + c] : kNoIndex;
-          x = ix == kNoIndex ? kEmptyKey : pack_key(order_key(a.half_o[base + c]), ix);
-        }
+        const unsigned int m32 = opaque_mask(lane >= k && c < nc && ix != kNoIndex);
+        const skey m = (skey)m32 << 32 | m32;
+        const skey cand = (pack_key(order_key(ov), ix) & m) | (kEmptyKey & ~m);
+        x = lane >= k ? cand : x;
         sort_keys<64>(x);
       }
       hk[h] = lane < k ? x : kEmptyKey;
