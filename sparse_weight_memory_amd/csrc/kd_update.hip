@@ -68,6 +68,19 @@ __device__ void task_prefix(const int4* kinds, int L, int* pref, int* nlong, int
   __syncthreads();
 }
 
+// A table row as R float4 per lane, unguarded: columns past the row re-read
+// its last float4.  Those lanes' sums are never stored, so the values need no
+// mask, and nothing consumes the loads before the pair sums need them.
+template <int R>
+__device__ __forceinline__ void load_row(const float4* row, int width4, float4 (&out)[R]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = lane + 64 * r;
+    out[r] = row[c < width4 ? c : width4 - 1];
+  }
+}
+
 // Token of pair p = t*k + m without an integer divide: (p + 1/2) / k lies at
 // least 1/(2k) >= 1/64 away from an integer, relative 2e-6 at p < 8192, far
 // above the reciprocal's error.
@@ -76,19 +89,21 @@ __device__ __forceinline__ int token_of(int p, int k) {
 }
 
 // One wave's sum over the sorted pairs pay[0, n) of a V segment:
-// sum_p w_p g_{t_p}.  NB data rows are in flight at a time.
+// sum_p w_p g_{t_p}.  NB data rows are in flight at a time.  The row's
+// current value goes into `old`, loaded in the first round beside the pairs'
+// data (loads outstanding at a loop's head would be waited for there).
 template <int R, int NB>
 __device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const int* pay,
-                                                int n, float4 (&acc)[R]) {
+                                                int n, const float4* trow, int width4,
+                                                float4 (&old)[R], float4 (&acc)[R]) {
   const int lane = lane_id();
-  const int width4 = a.dv >> 2;
   const float* gbase = a.g + (int64_t)u * a.T * a.dv;
   const float* sw = a.sel_w + (int64_t)u * a.P;
   for (int base = 0; base < n; base += kWave) {
     const int nb = min(kWave, n - base);
     const int pl = lane < nb ? pay[base + lane] : 0;
     const int tl = token_of(pl, a.k);
-    const float wl = lane < nb ? sw[pl] : 0.f;
+    float wl = 0.f;
     for (int i = 0; i < nb; i += NB) {
       float4 gv[NB][R];
 #pragma unroll
@@ -100,6 +115,13 @@ __device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const
           const int c = lane + 64 * r;
           gv[jj][r] = (i + jj < nb && c < width4) ? gr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+      }
+      // the pairs' weights and the row's value go out behind the first
+      // round's data rows (loads outstanding at a loop's head are waited for
+      // there); lanes >= nb read pair 0's weight, never used
+      if (i == 0) {
+        wl = sw[pl];
+        if (base == 0) load_row<R>(trow, width4, old);
       }
 #pragma unroll
       for (int jj = 0; jj < NB; ++jj) {
@@ -117,12 +139,13 @@ __device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const
 }
 
 // One wave's sum over the pairs pay[0, n) of a K segment (half h):
-//   IDW sum_p c_p (q_h[t_p] - old),  dot sum_p c_p q_h[t_p].
+//   IDW sum_p c_p (q_h[t_p] - old),  dot sum_p c_p q_h[t_p];
+// `old` (the row's current value) is loaded as for value segments.
 template <int R, int NB>
 __device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, const int* pay,
-                                              int n, const float4 (&old)[R], float4 (&acc)[R]) {
+                                              int n, const float4* trow, int width4,
+                                              float4 (&old)[R], float4 (&acc)[R]) {
   const int lane = lane_id();
-  const int width4 = a.half >> 2;
   const int b = u / a.H, hh = u - b * a.H;
   const bool idw = a.mode == 0;
   const float* cf = a.coef + (int64_t)h * a.U * a.P + (int64_t)u * a.P;
@@ -130,7 +153,7 @@ __device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, 
     const int nb = min(kWave, n - base);
     const int pl = lane < nb ? pay[base + lane] : 0;
     const int tl = token_of(pl, a.k);
-    const float cl = lane < nb ? cf[pl] : 0.f;
+    float cl = 0.f;
     for (int i = 0; i < nb; i += NB) {
       float4 qv[NB][R];
 #pragma unroll
@@ -143,6 +166,11 @@ __device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, 
           const int c = lane + 64 * r;
           qv[jj][r] = (i + jj < nb && c < width4) ? qr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+      }
+      // coefficients and the row's value behind the first round's data rows
+      if (i == 0) {
+        cl = cf[pl];
+        if (base == 0) load_row<R>(trow, width4, old);
       }
 #pragma unroll
       for (int jj = 0; jj < NB; ++jj) {
@@ -236,23 +264,16 @@ __global__ __launch_bounds__(W * kWave, kd_waves_per_simd<W>()) void kd_update(C
       width4 = a.dv >> 2;
       trow = reinterpret_cast<float4*>(
           a.v + (int64_t)b * a.stride_v + ((int64_t)hh * a.n * a.n + row) * a.dv);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int c = lane + 64 * r;
-        old[r] = (finisher && c < width4) ? trow[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      sum_value_pairs<R, NB>(a, u, pay, np, acc);
+      // every wave loads the row (used by the finisher only), beside the pairs
+      if (np <= 0) load_row<R>(trow, width4, old);
+      sum_value_pairs<R, NB>(a, u, pay, np, trow, width4, old, acc);
     } else {
       const int h = list - 1;
       width4 = a.half >> 2;
       trow = reinterpret_cast<float4*>(
           (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k + ((int64_t)hh * a.n + row) * a.half);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int c = lane + 64 * r;
-        old[r] = c < width4 ? trow[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      sum_key_pairs<R, NB>(a, u, h, pay, np, old, acc);
+      if (np <= 0) load_row<R>(trow, width4, old);
+      sum_key_pairs<R, NB>(a, u, h, pay, np, trow, width4, old, acc);
     }
 
     if (is_long) {
@@ -329,7 +350,7 @@ hipError_t launch_kd(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) 
   if (r <= 1) return launch_kd_as<1, 16, 4>(a, s, tm);
   if (r <= 2) return launch_kd_as<2, 8, 8>(a, s, tm);
   if (r <= 4) return launch_kd_as<4, 4, 4>(a, s, tm);
-  return launch_kd_as<8, 4, 4>(a, s, tm);
+  return launch_kd_as<8, 4, 2>(a, s, tm);
 }
 
 }  // namespace fwpkm
