@@ -83,11 +83,68 @@ __host__ __device__ inline int ka_query_width(int half, int blk) {
   return (ndq - 1) * share + ka_chunks<DC, PF>(half, blk) * DC;
 }
 
+// Key staging straight from global memory into LDS (kDma, only with kFull):
+// each wave owns a ring of kPrefetch slots of 16 rows x kDimChunk dims.  One
+// global_load_lds_dwordx4 fills 64 consecutive 16-byte LDS slots, so a slot's
+// layout is row-major in load order; lane l of a load takes key row
+// r = l / (kDimChunk / 4) (+ rows of earlier loads) and the dim group
+// (l % (kDimChunk / 4)) ^ swz(r), which puts the 16 rows of a matrix-operand
+// read in 16 different 16-byte bank groups.
+template <int kDimChunk>
+__device__ __forceinline__ int dma_swizzle(int r) {
+  constexpr int kCols = kDimChunk / 4;          // float4 per staged row
+  return (r / (16 / kCols)) % kCols;
+}
+
+// Byte offset of an LDS location (the pointer points into __shared__ memory).
+__device__ __forceinline__ unsigned int lds_offset(const float* p) {
+  return (unsigned int)(uintptr_t)(__attribute__((address_space(3))) const float*)p;
+}
+
+// 2 S 16-byte LDS reads (S key operands, S query operands) issued together,
+// with the wait for all of them inside the same asm block, so no result is
+// visible before it has arrived.
+template <int S>
+__device__ __forceinline__ void lds_read_wait(v4f (&ka)[S], v4f (&qa)[S], const unsigned int (&ka_at)[S],
+                                              const unsigned int (&qa_at)[S]) {
+#if __HIP_DEVICE_COMPILE__
+  static_assert(S == 2 || S == 4, "two or four steps per chunk");
+  if constexpr (S == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(ka[0]), "=&v"(ka[1]), "=&v"(ka[2]), "=&v"(ka[3]),
+          "=&v"(qa[0]), "=&v"(qa[1]), "=&v"(qa[2]), "=&v"(qa[3])
+        : "v"(ka_at[0]), "v"(ka_at[1]), "v"(ka_at[2]), "v"(ka_at[3]),
+          "v"(qa_at[0]), "v"(qa_at[1]), "v"(qa_at[2]), "v"(qa_at[3]));
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(ka[0]), "=&v"(ka[1]), "=&v"(qa[0]), "=&v"(qa[1])
+        : "v"(ka_at[0]), "v"(ka_at[1]), "v"(qa_at[0]), "v"(qa_at[1]));
+  }
+#else
+  (void)ka; (void)qa; (void)ka_at; (void)qa_at;
+#endif
+}
+
+// s_waitcnt that waits until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left alone).
+template <int n>
+__device__ __forceinline__ void wait_vm_at_most() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // kFull: every multiplied chunk lies inside its dim share and d_h (the
 // shares tile d_h in whole chunks, and no ring padding is multiplied), so
-// the staging loads need no mask.
-template <int kDimChunk, int kPrefetch, bool kFull>
+// the staging loads need no mask.  kDma: stage keys with direct LDS loads
+// (see dma_swizzle); kPrefetch is then the number of LDS slots per wave.
+template <int kDimChunk, int kPrefetch, bool kFull, bool kDma>
 __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a) {
+  static_assert(!kDma || kFull, "direct LDS staging cannot mask");
   constexpr int kKPitch = Staging<kDimChunk, kPrefetch>::kKPitch;
   constexpr int kStageF4 = Staging<kDimChunk, kPrefetch>::kStageF4;
   constexpr int kLanesPerRow = Staging<kDimChunk, kPrefetch>::kLanesPerRow;
@@ -100,12 +157,17 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   const int qwidth = ka_query_width<kDimChunk, kPrefetch>(half, blk);
   const int qpitch = qwidth + 4;
   float* qs = smem;                                      // [16][qpitch]
-  float* kst = qs + kTokTile * qpitch;                   // [16 waves][2][16][kKPitch] staged keys
-  double* knp = reinterpret_cast<double*>(kst + 2 * kStageRows * kKPitch);  // [ndq][blk]
+  float* kst = qs + kTokTile * qpitch;                   // staged keys (register ring: [16 waves][2][16][kKPitch];
+                                                         // direct: [16 waves][kPrefetch][16][kDimChunk])
+  constexpr int kStageFloats = kDma ? kScoreWaves * kPrefetch * 16 * kDimChunk : 2 * kStageRows * kKPitch;
+  double* knp = reinterpret_cast<double*>(kst + kStageFloats);  // [ndq][blk]
   // after the contraction the staging buffers are free:
   float* part = kst;                                     // [ndq][16][blk + 1]
   float* sc = part;                                      // [16][blk + 1], reuses part[0]
-  skey* surv = reinterpret_cast<skey*>(kst + kStageRows * kKPitch);   // [16][blk] survivors
+  constexpr int kSurvOffset = kDma ? 4 * kTokTile * (64 + 1) : kStageRows * kKPitch;
+  static_assert(kSurvOffset * sizeof(float) + sizeof(skey) * kTokTile * kMaxBlk <= kStageFloats * sizeof(float),
+                "survivors fit the staging area");
+  skey* surv = reinterpret_cast<skey*>(kst + kSurvOffset);   // [16][blk] survivors
 
   const int ntt = (a.T + kTokTile - 1) / kTokTile;
   const int total = a.U * 2 * a.nblk * ntt;
@@ -188,8 +250,39 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
       *reinterpret_cast<float4*>(&buf[r * kKPitch + (lane % kLanesPerRow) * 4]) = src[j];
     }
   };
+  // direct staging: this wave's ring and the per-lane source offsets of a
+  // chunk's loads (chunk c adds c * kDimChunk)
+  float* wring = kst + wave * kPrefetch * 16 * kDimChunk;
+  int dma_off[kStageF4];
+  auto dma_issue = [&](int c) {
+    // chunks past the end re-read chunk 0 into a slot nobody reads again
+    const int cofs = c < nchunks ? c * kDimChunk : 0;
+    float* dst = wring + (c % kPrefetch) * 16 * kDimChunk;
+#if __HIP_DEVICE_COMPILE__   // a device builtin: the host pass only needs the kernel's stub
 #pragma unroll
-  for (int i = 0; i < kPrefetch; ++i) stage_load(stg[i], i);   // in flight while queries are staged
+    for (int j = 0; j < kStageF4; ++j)
+      __builtin_amdgcn_global_load_lds(kbase + dma_off[j] + cofs,
+                                       (__attribute__((address_space(3))) void*)(dst + j * kRowsPerLoad * kDimChunk),
+                                       16, 0, 0);
+#else
+    (void)cofs;
+    (void)dst;
+#endif
+  };
+  if constexpr (kDma) {
+#pragma unroll
+    for (int j = 0; j < kStageF4; ++j) {
+      const int r = j * kRowsPerLoad + lane / kLanesPerRow;
+      const int gk = kb * blk + kt * 16 + r;
+      const int col = (lane % kLanesPerRow) ^ dma_swizzle<kDimChunk>(r);
+      dma_off[j] = (gk < a.n ? gk : 0) * half + dq * share + col * 4;
+    }
+#pragma unroll
+    for (int i = 0; i + 1 < kPrefetch; ++i) dma_issue(i);    // in flight while queries are staged
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) stage_load(stg[i], i);   // in flight while queries are staged
+  }
 
   // ---- stage the 16-token query tile (this half) in LDS
   const int half4 = half >> 2;
@@ -204,20 +297,27 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     }
     *reinterpret_cast<float4*>(&qs[r * qpitch + c4 * 4]) = x;
   }
-  stage_store(stg[0], 0);
-  stage_load(stg[0], kPrefetch);
+  if constexpr (!kDma) {
+    stage_store(stg[0], 0);
+    stage_load(stg[0], kPrefetch);
+  }
   __syncthreads();
 
-  // ---- query norms (fp64 sums), once per token and half; wave w <-> token w
-  if (kb == 0 && t0 + wave < a.T) {
-    double s = 0.0;
-    for (int d = lane; d < half; d += kWave) {
-      const double x = qs[wave * qpitch + d];
-      s += x * x;
+  // ---- query norms (fp64 sums), once per token and half; wave w <-> token w.
+  // With direct staging they are stored after the contraction, so that only
+  // key loads are outstanding while the loop counts them.
+  auto query_norms = [&]() {
+    if (kb == 0 && t0 + wave < a.T) {
+      double s = 0.0;
+      for (int d = lane; d < half; d += kWave) {
+        const double x = qs[wave * qpitch + d];
+        s += x * x;
+      }
+      s = wave_sum_d(s);
+      if (lane == 0) a.qnorm[((int64_t)u * a.T + t0 + wave) * 2 + h] = (float)s;
     }
-    s = wave_sum_d(s);
-    if (lane == 0) a.qnorm[((int64_t)u * a.T + t0 + wave) * 2 + h] = (float)s;
-  }
+  };
+  if constexpr (!kDma) query_norms();
 
   // ---- scores.  Two independent accumulator chains (x,y and z,w components
   // of each step); one barrier per staged chunk.
@@ -241,17 +341,57 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
       acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.w, bq.w, acc1, 0, 0, 0);
     }
   };
-  // chunk c lives in ring slot c % kPrefetch until it is copied to the
-  // wave's LDS buffer c & 1 (during chunk c - 1); the slot is then refilled
-  // with chunk c + kPrefetch.  A wave's LDS operations complete in order, so
-  // buffer c & 1 is rewritten only after chunk c - 2's reads of it.
-  for (int c0 = 0; c0 < nchunks_p; c0 += kPrefetch) {
+  if constexpr (kDma) {
+    // chunk c sits in slot c % kPrefetch; the loads of chunk c + kPrefetch - 1
+    // refill the slot chunk c - 1 was read from (those reads fed the matrix
+    // core already), then the wave waits until at most the newer chunks'
+    // loads are outstanding: loads complete in order, so chunk c is in LDS
+    for (int c = 0; c < nchunks_p; ++c) {
+      dma_issue(c + kPrefetch - 1);
+      wait_vm_at_most<(kPrefetch - 1) * kStageF4>();
+      const float* slot = wring + (c % kPrefetch) * 16 * kDimChunk + row * kDimChunk;
+      const int sw = dma_swizzle<kDimChunk>(row);
+      // the chunk's operands in one block of LDS reads that waits for them
+      // itself: read as ordinary loads, each would first wait for every
+      // outstanding direct load (the compiler cannot tell the slots apart)
+      constexpr int kSteps = kDimChunk / 16;
+      v4f akv[kSteps], bqv[kSteps];
+      {
+        unsigned int ka_at[kSteps], qa_at[kSteps];
 #pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) {
-      const int c = c0 + i;
-      mfma_chunk(c);
-      stage_store(stg[(i + 1) % kPrefetch], c + 1);
-      stage_load(stg[(i + 1) % kPrefetch], c + 1 + kPrefetch);
+        for (int j = 0; j < kSteps; ++j) {
+          ka_at[j] = lds_offset(&slot[((4 * j + quad) ^ sw) * 4]);
+          qa_at[j] = lds_offset(&arow_base[(c * kSteps + j) * 16 + quad * 4]);
+        }
+        lds_read_wait<kSteps>(akv, bqv, ka_at, qa_at);
+      }
+#pragma unroll
+      for (int j = 0; j < kDimChunk / 16; ++j) {
+        const v4f ak = akv[j];
+        const v4f bq = bqv[j];
+        ksq = fmaf(ak.x, ak.x, ksq); ksq = fmaf(ak.y, ak.y, ksq);
+        ksq = fmaf(ak.z, ak.z, ksq); ksq = fmaf(ak.w, ak.w, ksq);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.x, bq.x, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.z, bq.z, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.y, bq.y, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.w, bq.w, acc1, 0, 0, 0);
+      }
+    }
+    wait_vm_at_most<0>();   // the overrun loads land before the area is reused
+    query_norms();
+  } else {
+    // chunk c lives in ring slot c % kPrefetch until it is copied to the
+    // wave's LDS buffer c & 1 (during chunk c - 1); the slot is then refilled
+    // with chunk c + kPrefetch.  A wave's LDS operations complete in order, so
+    // buffer c & 1 is rewritten only after chunk c - 2's reads of it.
+    for (int c0 = 0; c0 < nchunks_p; c0 += kPrefetch) {
+#pragma unroll
+      for (int i = 0; i < kPrefetch; ++i) {
+        const int c = c0 + i;
+        mfma_chunk(c);
+        stage_store(stg[(i + 1) % kPrefetch], c + 1);
+        stage_load(stg[(i + 1) % kPrefetch], c + 1 + kPrefetch);
+      }
     }
   }
   __syncthreads();     // the score buffers below reuse every wave's staging slice
@@ -374,7 +514,7 @@ int score_key_block(int units, int tokens, int n) {
   return blk;
 }
 
-template <int kDimChunk, int kPrefetch>
+template <int kDimChunk, int kPrefetch, bool kDma = false>
 size_t ka_smem_bytes(int half, int blk) {
   constexpr int kKPitch = kDimChunk + 4;
   const int ndq = kScoreWaves / (blk / 16);
@@ -382,8 +522,10 @@ size_t ka_smem_bytes(int half, int blk) {
   // staging buffers once the contraction is done
   static_assert(sizeof(float) * 4 * kTokTile * (64 + 1) <= sizeof(float) * kStageRows * kKPitch, "partials");
   static_assert(sizeof(skey) * kTokTile * kMaxBlk <= sizeof(float) * kStageRows * kKPitch, "survivors");
+  const size_t staging = kDma ? sizeof(float) * kScoreWaves * kPrefetch * 16 * kDimChunk   // direct rings
+                              : 2 * sizeof(float) * kStageRows * kKPitch;                 // double buffer
   return sizeof(float) * kTokTile * (ka_query_width<kDimChunk, kPrefetch>(half, blk) + 4)   // queries
-         + 2 * sizeof(float) * kStageRows * kKPitch                  // staged keys (double buffer)
+         + staging                                                   // staged keys
          + sizeof(double) * ndq * blk;                               // key-norm partials
 }
 
@@ -397,14 +539,14 @@ namespace {
 
 constexpr size_t kLdsBytes = 160 * 1024;
 
-template <int DC, int PF, bool kFull>
+template <int DC, int PF, bool kFull, bool kDma = false>
 hipError_t launch_ka_full(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&ka_score_topk<DC, PF, kFull>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)kLdsBytes);
+      reinterpret_cast<const void*>(&ka_score_topk<DC, PF, kFull, kDma>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
   if (attr != hipSuccess) return attr;
-  return fw_launch(ka_score_topk<DC, PF, kFull>, dim3(ka_grid(a)), dim3(kScoreWaves * kWave),
-                   (uint32_t)ka_smem_bytes<DC, PF>(a.half, a.key_block), s, tm, a);
+  return fw_launch(ka_score_topk<DC, PF, kFull, kDma>, dim3(ka_grid(a)), dim3(kScoreWaves * kWave),
+                   (uint32_t)ka_smem_bytes<DC, PF, kDma>(a.half, a.key_block), s, tm, a);
 }
 
 template <int DC, int PF>
@@ -420,6 +562,15 @@ hipError_t launch_ka_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* t
 }  // namespace
 
 hipError_t launch_ka(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
+  {
+    // full shapes (every 32-dim chunk of a share inside d_h, four per slot
+    // ring turn) stage keys straight into LDS when the rings fit
+    const int ndq = kScoreWaves / (a.key_block / 16);
+    const int share = ((a.half + 16 * ndq - 1) / (16 * ndq)) * 16;
+    const bool full32 = share % 32 == 0 && ndq * share <= a.half && (share / 32) % 4 == 0;
+    if (full32 && ka_smem_bytes<32, 4, true>(a.half, a.key_block) <= kLdsBytes)
+      return launch_ka_full<32, 4, true, true>(a, s, tm);
+  }
   // wider chunks halve the barriers per contraction; they fit for d_h <= 256.
   // A ring deeper than the chunk count would only multiply zeros.
   if (ka_smem_bytes<64, 2>(a.half, a.key_block) <= kLdsBytes) {

@@ -268,3 +268,11 @@ def test_sequence_alias_errors(fwpkm_lib, handle):
     if not torch.cuda.is_available():
         assert fwd_s(L, handle) == _lib.ERR_HIP
         assert fwd_s(L, handle, b_gate=None) == _lib.ERR_HIP
+
+
+def test_library_leaves_no_kernel_symbol_undefined():
+    """Every kernel the launchers reference is defined in the library (a shared
+    object links with undefined symbols and would only fail when loaded)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    assert "fwpkm" not in out, out

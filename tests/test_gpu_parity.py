@@ -100,6 +100,10 @@ EDGE = [
     ("k32-max", 1, 1, 32, 32, 40, 4, 600, 32, "idw"),
     ("dot-small", 2, 1, 64, 64, 16, 8, 12, 4, "dot"),
     ("dot-k16", 1, 2, 64, 50, 64, 16, 32, 16, "dot"),
+    # keys staged straight into LDS: 128-key blocks (two dim shares), and
+    # 256-key blocks with a ragged last block and token tile
+    ("direct-staging-blk128", 4, 1, 256, 256, 256, 256, 64, 8, "idw"),
+    ("direct-staging-ragged-dot", 8, 1, 256, 200, 300, 128, 32, 8, "dot"),
 ]
 
 
