@@ -17,26 +17,30 @@
 // in LDS.  The key block (64, 128 or 256 keys) is chosen per launch so that
 // small chunks still spread over the whole chip: wave w multiplies key tile
 // (w mod blk/16) over its share of the dims; dim shares are summed in LDS.
-// Each wave stages its own 16 key rows through a private LDS slice, 64 (or,
-// for d_h > 256, 32) dims at a time, loaded with whole lines (a wave-wide
-// load of matrix operands straight from memory would touch 16 key rows at
-// once, which the load path serves at a fraction of its rate); two (four)
-// chunks are in flight in registers, two in LDS.  With no barrier inside the
-// contraction, the waves of a SIMD drift apart and one's LDS traffic overlaps
-// another's matrix work.
+// Each wave stages its own 16 key rows through a private LDS slice (a
+// wave-wide load of matrix operands straight from memory would touch 16 key
+// rows at once, which the load path serves at a fraction of its rate).
+// When every chunk of the wave's dims is full, whole-line direct loads
+// (global_load_lds_dwordx4) fill a ring of four 32-dim slots; otherwise
+// chunks of 64 (or, for d_h > 256, 32) dims travel through registers into
+// two LDS buffers.  With no barrier inside the contraction, the waves of a
+// SIMD drift apart and one's LDS traffic overlaps another's matrix work.
 // Key norms are summed in fp32 beside the contraction (on this chip fp32
 // matrix instructions share the vector issue, so every extra instruction in
 // that loop costs time): their rounding, ~1e-7 of ||K||^2, stays well below
 // the dot product's and the 1e-6 relative gap at which candidates count as
 // tied.
 //
-// Selection, one wave per token, on packed 64-bit (value, index) keys: a
-// bitonic sort of the first 64 candidates gives a threshold (the k-th best);
-// the remaining candidates are filtered against it with one ballot per 64,
-// the few that pass are compacted into LDS, and a bitonic sort of the k best
-// plus the survivors (over 16, 32 or 64 lanes, whichever holds them) gives
-// the block's top-k.  Every step orders by (value, index), which is unique,
-// so the result is deterministic.
+// Selection, one wave per token, on packed 64-bit (value, index) keys.  For
+// blocks of 128 or 256 keys each lane first takes the smallest value of its
+// candidates; the k-th smallest of those 64 values (a 32-bit bitonic sort)
+// bounds the answer, only the candidates at or below it are compacted into
+// LDS, and a 64-bit bitonic sort over 16, 32 or 64 lanes orders them.  Where
+// more than 64 pass (mass ties) and for 64-key blocks: a bitonic sort of the
+// first 64 candidates gives a threshold (the k-th best), the remaining ones
+// are filtered against it with one ballot per 64, and a bitonic sort of the
+// k best plus the survivors gives the top-k.  Every step orders by (value,
+// index), which is unique, so both give the same, deterministic result.
 // Work items are laid out so that the token tiles sharing one key block run
 // on one XCD (workgroup i is dispatched to XCD i % 8), which keeps the block's
 // keys in that XCD's L2.
@@ -49,6 +53,25 @@
 namespace fwpkm {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Ascending bitonic sort of one 32-bit word per lane over the whole wave.
+template <int S>
+__device__ __forceinline__ void cas_u32(unsigned int& x, bool ascending) {
+  const unsigned int o = (unsigned int)xor_lane<S>((int)x);
+  const bool keep_min = ((lane_id() & S) == 0) == ascending;
+  x = keep_min ? min(x, o) : max(x, o);
+}
+template <int SIZE, int S>
+__device__ __forceinline__ void u32_merge_steps(unsigned int& x) {
+  cas_u32<S>(x, SIZE == kWave || (lane_id() & SIZE) == 0);
+  if constexpr (S > 1) u32_merge_steps<SIZE, S / 2>(x);
+}
+template <int SIZE>
+__device__ __forceinline__ void u32_stages(unsigned int& x) {
+  if constexpr (SIZE > 2) u32_stages<SIZE / 2>(x);
+  u32_merge_steps<SIZE, SIZE / 2>(x);
+}
+__device__ __forceinline__ void sort_u32(unsigned int& x) { u32_stages<kWave>(x); }
 
 constexpr int kScoreWaves = 16;
 constexpr int kMaxBlk = 256;       // largest key block
@@ -473,7 +496,45 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     const int gkey = kb * blk + c;
     return gkey < a.n ? pack_key(srow[c], gkey) : kEmptyKey;
   };
-  skey x = cand(lane);
+  skey x;
+  bool picked = false;
+  if (blk > kWave) {
+    // Each lane's best candidate value bounds the answer: the k-th smallest
+    // of those 64 values (compared on the value bits alone, a 32-bit sort)
+    // is >= the k-th best key, so only candidates whose value bits do not
+    // exceed it can be among the k best.  Those few get the exact 64-bit
+    // sort.  When more than a wave's worth pass (mass ties, or fewer than k
+    // real keys in the block) the general path below runs instead.
+    constexpr int kR = kMaxBlk / kWave;
+    const int nr = blk / kWave;
+    skey cr[kR];
+    unsigned int lo_hi = 0xFFFFFFFFu;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      cr[r] = r < nr ? cand(lane + r * kWave) : kEmptyKey;
+      lo_hi = min(lo_hi, (unsigned int)(cr[r] >> 32));
+    }
+    sort_u32(lo_hi);
+    const unsigned int th = (unsigned int)__builtin_amdgcn_readlane((int)lo_hi, k - 1);
+    skey* sv = surv + wave * blk;
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const bool pass = r < nr && (unsigned int)(cr[r] >> 32) <= th;
+      const unsigned long long m = __ballot(pass);
+      if (pass) sv[n + __popcll(m & ((1ull << lane) - 1ull))] = cr[r];
+      n += __popcll(m);
+    }
+    if (n <= kWave) {
+      x = lane < n ? sv[lane] : kEmptyKey;
+      if (n <= 16) sort_keys<16>(x);
+      else if (n <= 32) sort_keys<32>(x);
+      else sort_keys<64>(x);
+      picked = true;
+    }
+  }
+  if (!picked) {
+  x = cand(lane);
   sort_keys<64>(x);                               // the first 64, best first
   if (blk > kWave) {
     const skey th = readlane_k(x, k - 1);         // k-th best so far
@@ -499,6 +560,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
       else if (cnt <= 32) sort_keys<32>(x);
       else sort_keys<64>(x);
     }
+  }
   }
   if (lane < k) {
     const int64_t base = ((((int64_t)u * a.T + tw) * 2 + h) * a.nblk + kb) * k;
