@@ -6,10 +6,14 @@
 // in their original order (dropping those the read kernel marked as merged
 // away: K rows a token already listed, key n; V key n*n = no slot) and counts
 // the entries of lower regions, which fixes where its output goes.  Then it
-// sorts its entries by row with a stable LSD radix sort held entirely in LDS
-// (8-bit digits; as many passes as its largest row needs).  Stability keeps
-// every row's pairs in ascending (token, rank) order, so each row's gradient
-// is summed in one fixed order and no float atomics are used.
+// sorts its entries by row, stably, in LDS.  A region of at most 64 entries,
+// or of at most 256 whose rows span more than 8 bits, packs each (row,
+// position in list order) into one 32-bit word and places every entry at the
+// count of words below its own (one pass, every entry against every other);
+// other regions use an LSD radix sort (8-bit digits; as many passes as the
+// largest row needs).  Stability keeps every row's
+// pairs in ascending (token, rank) order, so each row's gradient is summed in
+// one fixed order and no float atomics are used.
 // [gist.science "Fast-weight Product Key Memory", section 2, Key Technical
 // Choices: gradients of slots accessed several times in a chunk are
 // aggregated (averaged)]
@@ -18,7 +22,7 @@
 // compute units; a row lands in exactly one region, so segments never cross
 // regions and the result does not depend on the region count.
 //
-// Ranking inside a wave uses ballots: the lanes holding the same digit are
+// Radix ranking inside a wave uses ballots: the lanes holding the same digit are
 // found with one ballot per digit bit, a lane's rank among them is the
 // population count of the lower such lanes.  Each wave owns a contiguous run
 // of 64-entry tiles and one counter per digit, so the scatter base of a
@@ -44,6 +48,23 @@ constexpr int kBits = 8;
 constexpr int kDigits = 1 << kBits;
 constexpr int kGroupThreads = kGroupWaves * kWave;
 constexpr int kScanTiles = kSortMaxPairs / (kWave * kGroupWaves);   // key tiles per wave, at most
+// Rank sort limits: positions in kRankPosBits bits, rows below
+// 2^(32 - kRankPosBits).  Its all-pairs compares cost M^2 / 64 vector
+// instructions per workgroup; past ~256 entries two radix passes are cheaper.
+constexpr int kRankPosBits = 8;
+constexpr int kRankMax = 1 << kRankPosBits;
+constexpr int kRankBatch = 32;   // words compared per round, eight 16-byte reads in flight
+constexpr int kRankPartOffset = 1024;   // partial counts after the packed words, in the counters' space
+static_assert(kRankMax <= kGroupThreads, "one ranked entry per thread");
+static_assert(kRankMax + kRankBatch - 1 <= kRankPartOffset, "packed words before the partial counts");
+static_assert(kRankPartOffset + (kGroupWaves - 1) * kWave <= kGroupWaves * kDigits,
+              "partial counts fit the counters' space");
+
+// r + (w < me): the compare's carry feeds the add (two instructions).
+__device__ __forceinline__ unsigned int add_if_below(unsigned int r, unsigned int w, unsigned int me) {
+  asm("v_cmp_lt_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, 0, %0, vcc" : "+v"(r) : "v"(w), "v"(me) : "vcc");
+  return r;
+}
 
 // Region of a row: multiplicative (Fibonacci) hashing, so rows that many
 // tokens share spread over the regions.
@@ -155,6 +176,13 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
     if (tid == 0) *kinds = make_int4(0, 0, off, 0);
     return;
   }
+  // regions of at most kRankMax entries whose rows need two or more radix
+  // passes, and regions of at most 64 entries, are sorted by ranking (below);
+  // their packed (row, position) words use the radix counters' space
+  // (against one radix pass, ranking pays only for the smallest regions)
+  const bool by_rank = kmax < (1 << (32 - kRankPosBits)) &&
+                       (M <= kWave || (M <= kRankMax && kmax >= kDigits));
+  unsigned int* packed = reinterpret_cast<unsigned int*>(cnt);
 #pragma unroll
   for (int j = 0; j < kScanTiles; ++j) {
     if (j >= tpw) break;
@@ -165,22 +193,74 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
       const int pos = base + __popcll(m & lanes_below());
       key0[pos] = key;
       idx0[pos] = (wave * tpw + j) * kWave + lane;
+      if (by_rank) packed[pos] = ((unsigned int)key << kRankPosBits) | (unsigned int)pos;
     }
     base += __popcll(m);
   }
   int* mycnt = cnt + wave * kDigits;   // only this wave counts into / scatters from it
-  for (int i = lane; i < kDigits; i += kWave) mycnt[i] = 0;
+  if (by_rank) {
+    if (tid < kRankBatch - 1) packed[M + tid] = 0xFFFFFFFFu;   // pad to whole batches; never below a real word
+  } else {
+    for (int i = lane; i < kDigits; i += kWave) mycnt[i] = 0;
+  }
   __syncthreads();
-  int bits = 0;
-  while (bits < 31 && (kmax >> bits) != 0) ++bits;
-  const int passes = (bits + kBits - 1) / kBits;
 
-  // ---- LSD radix passes over the M kept entries
+  // wave w owns tiles [t_lo, t_hi) of the M kept entries
   const int vtiles = (M + kWave - 1) / kWave;
   const int vtpw = (vtiles + kGroupWaves - 1) / kGroupWaves;
   const int t_lo = wave * vtpw;
   const int t_hi = min(vtiles, t_lo + vtpw);
   int *ks = key0, *is = idx0, *kd = key1, *id = idx1;
+  if (by_rank) {
+    // ---- rank sort: the words are distinct and ordered as (row, position),
+    // so an entry's place in the stable order is the number of words below
+    // its own.  Every wave takes one 64-entry tile and one share of the
+    // word batches (all lanes read the same words: LDS broadcast reads);
+    // with fewer tiles than waves, the shares' counts meet in LDS.
+    const int rtiles = (M + kWave - 1) / kWave;
+    const int shares = kGroupWaves / rtiles;                // >= 1
+    const int rtile = wave % rtiles, share = wave / rtiles;
+    const int i = rtile * kWave + lane;
+    const int nb = (M + kRankBatch - 1) / kRankBatch;
+    // wave-uniform bounds (scalar loop)
+    const int b_lo = __builtin_amdgcn_readfirstlane(share * nb / shares);
+    const int b_hi = __builtin_amdgcn_readfirstlane((share + 1) * nb / shares);
+    int* part = cnt + kRankPartOffset;                      // [shares][M] partial counts
+    int rank = 0;
+    if (share < shares) {
+      const unsigned int me = i < M ? packed[i] : 0u;
+      const uint4* p4 = reinterpret_cast<const uint4*>(packed);
+      unsigned int r[kRankBatch / 4] = {};
+      for (int bb = b_lo; bb < b_hi; ++bb) {
+        uint4 v[kRankBatch / 4];
+#pragma unroll
+        for (int q = 0; q < kRankBatch / 4; ++q) v[q] = p4[bb * (kRankBatch / 4) + q];   // all in flight
+#pragma unroll
+        for (int q = 0; q < kRankBatch / 4; ++q) {
+          r[q] = add_if_below(r[q], v[q].x, me);
+          r[q] = add_if_below(r[q], v[q].y, me);
+          r[q] = add_if_below(r[q], v[q].z, me);
+          r[q] = add_if_below(r[q], v[q].w, me);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kRankBatch / 4; ++q) rank += (int)r[q];
+      if (shares > 1 && share > 0 && i < M) part[(share - 1) * M + i] = rank;
+    }
+    if (shares > 1) __syncthreads();                        // block-uniform
+    if (share == 0 && i < M) {
+      for (int sh = 1; sh < shares; ++sh) rank += part[(sh - 1) * M + i];
+      key1[rank] = key0[i];
+      idx1[rank] = idx0[i];
+    }
+    __syncthreads();
+    ks = key1; is = idx1; kd = key0; id = idx0;
+  } else {
+  int bits = 0;
+  while (bits < 31 && (kmax >> bits) != 0) ++bits;
+  const int passes = (bits + kBits - 1) / kBits;
+
+  // ---- LSD radix passes over the M kept entries
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * kBits;
     for (int tile = t_lo; tile < t_hi; ++tile) {
@@ -231,6 +311,7 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
     int* t;
     t = ks; ks = kd; kd = t;
     t = is; is = id; id = t;
+  }
   }
 
   // ---- segments: heads of runs of equal rows.  The pong buffers are free
