@@ -31,6 +31,9 @@ constexpr int kPThreads = 256;       // 4 waves, 2 x 2 of 64 x 64
 constexpr int kPLoads = kPM * kPK / 4 / kPThreads;   // float4 per thread per operand
 static_assert(kPM == kPN, "one loader mapping serves both operands");
 static_assert(kPLoads * 4 * kPThreads == kPM * kPK, "whole float4 loads");
+constexpr int kPStage = (kPM + kPN) * kPPitch;                       // floats per stage
+constexpr size_t kPLdsBytes = sizeof(float) * 2 * kPStage;           // two stages
+static_assert(2 * kPLdsBytes <= 160 * 1024, "two workgroups per compute unit");
 
 // Native 4-vectors for the staged tiles (plain registers; copies of the
 // HIP float4 struct through memory would keep them in scratch).
@@ -56,8 +59,9 @@ __device__ __forceinline__ f4 keep_if4(f4 v, bool ok) {
 // operands, so the sum is unchanged), which lets each lane read its 8 values
 // as two 16-byte LDS loads.
 __global__ __launch_bounds__(kPThreads, 2) void kf_project(SeqArgs s) {
-  __shared__ float As[kPM * kPPitch];
-  __shared__ float Bs[kPN * kPPitch];
+  // two stages of both operand tiles: step k reads stage k % 2 while the
+  // tiles of step k + 1 are written to the other one
+  extern __shared__ float kf_lds[];
   const int M = s.B * s.S, N = s.Nq + s.Nv, D = s.D;
   const int mtiles = (M + kPM - 1) / kPM, ntiles = (N + kPN - 1) / kPN;
   const int total = mtiles * ntiles;
@@ -105,18 +109,27 @@ __global__ __launch_bounds__(kPThreads, 2) void kf_project(SeqArgs s) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  fetch(0);
-  for (int k0 = 0; k0 < D; k0 += kPK) {
+  auto stage = [&](int k0, int buf) __attribute__((always_inline)) {
+    float* As = kf_lds + buf * kPStage;
+    float* Bs = As + kPM * kPPitch;
 #pragma unroll
     for (int i = 0; i < kPLoads; ++i) {
       const int col = ((tid + i * kPThreads) & 7) * 4;
       *reinterpret_cast<f4*>(&As[lds_off[i]]) = keep_if4(pa[i], k0 + col < D);
       *reinterpret_cast<f4*>(&Bs[lds_off[i]]) = pb[i];
     }
-    __syncthreads();
-    fetch(k0 + kPK < D ? k0 + kPK : k0);          // the last round reloads (unused)
+  };
+  fetch(0);
+  stage(0, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < D; k0 += kPK, buf ^= 1) {
+    const bool more = k0 + kPK < D;
+    fetch(more ? k0 + kPK : k0);                 // the last step reloads (unused): no branch around loads
     // keep the next tile's loads ahead of this tile's matrix work
     __builtin_amdgcn_sched_barrier(0);
+    const float* As = kf_lds + buf * kPStage;
+    const float* Bs = As + kPM * kPPitch;
     float a[4][8], b[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -136,6 +149,9 @@ __global__ __launch_bounds__(kPThreads, 2) void kf_project(SeqArgs s) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][st], b[j][st], acc[i][j], 0, 0, 0);
+    // the other stage was last read in the previous step, before the barrier
+    // that ended it
+    if (more) stage(k0 + kPK, buf ^ 1);
     __syncthreads();
   }
 
@@ -210,7 +226,11 @@ hipError_t launch_kf_project(const SeqArgs& s, hipStream_t st, const LaunchTimin
     first.beg = tm->beg;
     last.end = tm->end;
   }
-  hipError_t e = fw_launch(kf_project, dim3((unsigned)tiles), dim3(kPThreads), 0, st, tm ? &first : nullptr, s);
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&kf_project),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPLdsBytes);
+  if (attr != hipSuccess) return attr;
+  hipError_t e = fw_launch(kf_project, dim3((unsigned)tiles), dim3(kPThreads), (uint32_t)kPLdsBytes, st,
+                           tm ? &first : nullptr, s);
   if (e == hipSuccess) e = fw_launch(kf_prep, dim3(s.B), dim3(256), 0, st, tm ? &last : nullptr, s);
   return e;
 }
