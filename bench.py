@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=str(DEFAULT_WORKLOAD))
+    ap.add_argument("--batch", type=int, default=0,
+                    help="run the workload's per-unit shape with this many sequences "
+                         "(the workload name records it); 0 keeps the workload's own")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time spent timing the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -247,6 +250,11 @@ def main():
 
     key = int(args.workload) if args.workload.isdigit() else args.workload
     cfg = get_config(key)
+    if args.batch:
+        import dataclasses
+        import re
+        cfg = dataclasses.replace(cfg, batch=args.batch,
+                                  name=re.sub(r"-\d+x", f"-{args.batch}x", cfg.name, count=1))
     if not os.path.exists(_lib.LIB_PATH):
         from sparse_weight_memory_amd import build as _build
         _build.build()
