@@ -118,6 +118,18 @@ def test_edge_shapes(case):
         st, _, _ = compare_chunk(mem, st, q, y, lr, label=f"{label} step{c}")
 
 
+@pytest.mark.parametrize("C", [32, 33])
+def test_grouping_at_the_rank_sort_limit(C):
+    """48 units leave one hash region per list, so every unit's V list holds
+    exactly C*k entries: 256 (the largest region sorted by ranking) or 264
+    (the radix sort); the K lists hold fewer entries, with 5-bit rows."""
+    need_gpu()
+    B, H, n, half, dv, k = 48, 1, 32, 8, 16, 8
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=C, num_heads=H, max_batch=B)
+    st, q, y = _random_case(900 + C, B, H, C, n, half, dv)
+    compare_chunk(mem, st, q, y, 1.0, units=[0, 11, 30, 47], label=f"rank-limit C{C}")
+
+
 @pytest.mark.parametrize("mode", ["idw", "dot"])
 def test_long_segments_split_into_pieces(mode):
     """Every token asks the same few queries, so each touched row is hit by
