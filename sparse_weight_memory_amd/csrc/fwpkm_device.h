@@ -106,6 +106,20 @@ __device__ __forceinline__ int64_t seq_chunk_row(const SeqArgs& s, int b, int t)
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Units and XCDs.  Workgroup i of every launch runs on XCD i % 8 (the
+// dispatcher deals workgroups to the eight XCDs in turn), each XCD has its
+// own L2, and that L2 keeps what one kernel wrote for the next.  When the
+// unit count is a multiple of 8, the score kernel's layout runs unit u on XCD
+// u / (U / 8); kernels whose work items are unit-major follow it, so a unit's
+// candidate lists, pair lists and g rows are read back from the L2 that
+// holds them.  Returns the work item of workgroup `wg` for a grid of exactly
+// units * per_unit workgroups (the identity when units % 8 != 0).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int unit_affine_item(int wg, int units, int per_unit) {
+  if (units % kXcds != 0) return wg;
+  return (wg % kXcds) * (units / kXcds) * per_unit + wg / kXcds;
+}
+
 // ---- cross-lane exchange with lane ^ S, without the LDS permute unit:
 // DPP quad permutes for S = 1, 2; row shifts for S = 4; a row rotation for
 // S = 8; the gfx950 half-swap instructions for S = 16, 32.  All lanes of the

@@ -43,8 +43,10 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   constexpr bool KEEP = KMAX * VR <= 32;
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  const int u = blockIdx.y;
-  const int t = blockIdx.x * 4 + wave;
+  const int nbx = (a.T + 3) >> 2;                      // 4 tokens per workgroup
+  const int item = unit_affine_item(blockIdx.x, a.U, nbx);
+  const int u = item / nbx;
+  const int t = (item - u * nbx) * 4 + wave;
   if (t >= a.T) return;
   const int k = a.k;
   const int n = a.n;
@@ -343,7 +345,7 @@ namespace {
 
 template <int KMAX, int VR>
 hipError_t launch_kb_t(const ChunkArgs& a, bool write, hipStream_t s, const LaunchTiming* tm) {
-  dim3 grid((a.T + 3) / 4, a.U);
+  dim3 grid((unsigned)(((a.T + 3) / 4) * a.U));       // unit-major, see unit_affine_item
   if (write) return fw_launch(kb_read<KMAX, VR, true>, grid, dim3(256), 0, s, tm, a);
   return fw_launch(kb_read<KMAX, VR, false>, grid, dim3(256), 0, s, tm, a);
 }

@@ -109,9 +109,11 @@ __device__ __forceinline__ unsigned long long lanes_below() {
 
 __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   extern __shared__ int lds[];
-  const int region = blockIdx.x;
-  const int list = blockIdx.y;   // 0 = V slots, 1 = K1 rows, 2 = K2 rows
-  const int u = blockIdx.z;
+  const int per_unit = 3 * a.regions;
+  const int item = unit_affine_item(blockIdx.x, a.U, per_unit);
+  const int u = item / per_unit;
+  const int list = (item - u * per_unit) / a.regions;   // 0 = V slots, 1 = K1 rows, 2 = K2 rows
+  const int region = item - u * per_unit - list * a.regions;
   const int P = a.P;
   int* key0 = lds;                        // [P] rows (ping)
   int* idx0 = key0 + P;                   // [P] pair indices (ping)
@@ -406,7 +408,8 @@ hipError_t launch_kc(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) 
       reinterpret_cast<const void*>(&kc_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)kc_smem_bytes(kSortMaxPairs));
   if (attr != hipSuccess) return attr;
-  return fw_launch(kc_sort, dim3(a.regions, 3, a.U), dim3(kGroupThreads), (uint32_t)smem, s, tm, a);
+  // unit-major (region fastest), see unit_affine_item
+  return fw_launch(kc_sort, dim3((unsigned)(a.regions * 3 * a.U)), dim3(kGroupThreads), (uint32_t)smem, s, tm, a);
 }
 
 }  // namespace fwpkm

@@ -33,11 +33,28 @@ namespace fwpkm {
 namespace {
 
 
-// pref[i] = tasks of regions [0, i) for i in [0, L]; nlong / nshort / offs
-// receive the regions' counts.  All threads of the block take part.
+// Regions in XCD-affine order (unit count a multiple of 8): position r =
+// ((x * 3 + list) * (U / 8) + ul) * regions + rg holds region
+// (list * U + x * (U / 8) + ul) * regions + rg, so the regions of the units
+// XCD x runs (see unit_affine_item) are positions [x L / 8, (x + 1) L / 8).
+// The identity otherwise.
+__device__ __forceinline__ int region_at(int r, int units, int regions) {
+  if (units % kXcds != 0) return r;
+  const int upx = units / kXcds;
+  const int rg = r % regions;
+  int rest = r / regions;
+  const int ul = rest % upx;
+  rest /= upx;
+  const int list = rest % 3, x = rest / 3;
+  return (list * units + x * upx + ul) * regions + rg;
+}
+
+// pref[i] = tasks of the regions at positions [0, i) (region_at order) for i
+// in [0, L]; nlong / nshort / offs receive the regions' counts, by position.
+// All threads of the block take part.
 template <int W>
-__device__ void task_prefix(const int4* kinds, int L, int* pref, int* nlong, int* nshort,
-                            int* offs, int* wtot) {
+__device__ void task_prefix(const int4* kinds, int L, int units, int regions, int* pref, int* nlong,
+                            int* nshort, int* offs, int* wtot) {
   constexpr int NT = W * kWave;
   const int tid = threadIdx.x, wave = tid / kWave;
   const int per = (L + NT - 1) / NT;
@@ -45,7 +62,7 @@ __device__ void task_prefix(const int4* kinds, int L, int* pref, int* nlong, int
   int local = 0;
   for (int j = 0; j < per; ++j) {
     if (beg + j < L) {
-      const int4 kd = kinds[beg + j];
+      const int4 kd = kinds[region_at(beg + j, units, regions)];
       nlong[beg + j] = kd.x;
       nshort[beg + j] = kd.y;
       offs[beg + j] = kd.z;
@@ -214,22 +231,32 @@ __global__ __launch_bounds__(W * kWave, kd_waves_per_simd<W>()) void kd_update(C
   int* nshort = nlong + L;                                            // [L]
   int* offs = nshort + L;                                             // [L]
   int* wtot = offs + L;                                               // [W]
-  task_prefix<W>(a.kinds, L, pref, nlong, nshort, offs, wtot);
-  const int total = pref[L];
+  task_prefix<W>(a.kinds, L, a.U, a.regions, pref, nlong, nshort, offs, wtot);
+  // workgroups of XCD x take the tasks of that XCD's units (the grid is a
+  // multiple of 8 then); otherwise every workgroup strides over all tasks
+  int r_lo = 0, r_hi = L, t_first = blockIdx.x, t_end = pref[L], t_step = gridDim.x;
+  if (a.U % kXcds == 0) {
+    const int x = blockIdx.x % kXcds;
+    r_lo = x * (L / kXcds);
+    r_hi = r_lo + L / kXcds;
+    t_first = pref[r_lo] + blockIdx.x / kXcds;
+    t_end = pref[r_hi];
+    t_step = gridDim.x / kXcds;
+  }
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int P = a.P;
   const float lr = a.lr;
 
-  for (int task = blockIdx.x; task < total; task += gridDim.x) {
-    // region holding this task
-    int lo = 0, hi = L;
+  for (int task = t_first; task < t_end; task += t_step) {
+    // region (position) holding this task
+    int lo = r_lo, hi = r_hi;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (pref[mid] <= task) lo = mid; else hi = mid;
     }
     const int j = task - pref[lo];
-    const int lu = lo / a.regions;          // list * U + unit
+    const int lu = region_at(lo, a.U, a.regions) / a.regions;   // list * U + unit
     const int list = lu / a.U;
     const int u = lu - list * a.U;
     const int b = u / a.H, hh = u - b * a.H;
@@ -337,7 +364,8 @@ hipError_t launch_kd_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* t
   const int64_t most = (int64_t)3 * a.U * a.P / (kShortSeg + 1) +
                        (int64_t)3 * a.U * a.P / W + L;
   const int64_t resident = (int64_t)kKdResidentPerCu * device_cus();
-  const int64_t gx = most < resident ? most : resident;
+  int64_t gx = most < resident ? most : resident;
+  if (a.U % kXcds == 0) gx = (gx + kXcds - 1) / kXcds * kXcds;   // whole rounds over the XCDs
   return fw_launch(kd_update<R, W, NB>, dim3((unsigned)gx), dim3(W * kWave), (uint32_t)smem, s, tm, a);
 }
 
