@@ -85,11 +85,23 @@ __device__ __forceinline__ float keep_if(float x, bool ok) {
   return __uint_as_float(__float_as_uint(x) & m);
 }
 
-// grid (2U, ceil(T / 16)): one wave per token.
+// Work item of a unit-major flat grid with `per_half` items per (unit, half):
+// (unit * 2 + half, item within the half), XCD-affine (unit_affine_item).
+struct HalfItem {
+  int uh, i;
+};
+__device__ __forceinline__ HalfItem half_item(int units, int per_half) {
+  const int item = unit_affine_item(blockIdx.x, units, 2 * per_half);
+  const int uh = item / per_half;
+  return {uh, item - uh * per_half};
+}
+
+// grid 2U * ceil(T / 16) (unit-major): one wave per token.
 template <bool kIdw>
 __global__ __launch_bounds__(kStatWaves * kWave) void ke_tokstats(ChunkArgs a) {
-  const int uh = blockIdx.x, u = uh >> 1, h = uh & 1;
-  const int t = blockIdx.y * kStatWaves + (int)(threadIdx.x / kWave);
+  const HalfItem it = half_item(a.U, (a.T + kStatWaves - 1) / kStatWaves);
+  const int uh = it.uh, u = uh >> 1, h = uh & 1;
+  const int t = it.i * kStatWaves + (int)(threadIdx.x / kWave);
   const int lane = lane_id(), n = a.n, np = a.addr_np;
   if (t >= a.T) return;
   const float* row = a.addr_s + ((int64_t)uh * a.T + t) * np;
@@ -125,15 +137,16 @@ __global__ __launch_bounds__(kStatWaves * kWave) void ke_tokstats(ChunkArgs a) {
   }
 }
 
-// grid (2U, ceil(n / 64)): lane = sub-key, waves stride over tokens; the 16
-// partial sums of a sub-key are added in wave order.
+// grid 2U * ceil(n / 64) (unit-major): lane = sub-key, waves stride over
+// tokens; the 16 partial sums of a sub-key are added in wave order.
 template <bool kIdw>
 __global__ __launch_bounds__(kStatWaves * kWave) void ke_usage(ChunkArgs a) {
   constexpr int kTokLoads = 8;            // tokens of one wave in flight
   __shared__ float part[kStatWaves][kWave];
-  const int uh = blockIdx.x, u = uh >> 1, h = uh & 1;
+  const HalfItem it = half_item(a.U, (a.n + kWave - 1) / kWave);
+  const int uh = it.uh, u = uh >> 1, h = uh & 1;
   const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
-  const int i = blockIdx.y * kWave + lane;          // < addr_np: the load is in range
+  const int i = it.i * kWave + lane;                // < addr_np: the load is in range
   const int n = a.n, T = a.T, np = a.addr_np;
   const float* S = a.addr_s + (int64_t)uh * T * np;
   const float* st = a.addr_tok + (int64_t)uh * T * 2;
@@ -163,12 +176,13 @@ __global__ __launch_bounds__(kStatWaves * kWave) void ke_usage(ChunkArgs a) {
   }
 }
 
-// grid (2U, ceil(T / 16)): one wave per token; scores become coefficients
-// (pad columns receive values that no reader uses).
+// grid 2U * ceil(T / 16) (unit-major): one wave per token; scores become
+// coefficients (pad columns receive values that no reader uses).
 template <bool kIdw>
 __global__ __launch_bounds__(kStatWaves * kWave) void ke_coef(ChunkArgs a) {
-  const int uh = blockIdx.x, u = uh >> 1, h = uh & 1;
-  const int t = blockIdx.y * kStatWaves + (int)(threadIdx.x / kWave);
+  const HalfItem it = half_item(a.U, (a.T + kStatWaves - 1) / kStatWaves);
+  const int uh = it.uh, u = uh >> 1, h = uh & 1;
+  const int t = it.i * kStatWaves + (int)(threadIdx.x / kWave);
   const int lane = lane_id(), n = a.n, np = a.addr_np;
   if (t >= a.T) return;
   float* row = a.addr_s + ((int64_t)uh * a.T + t) * np;
@@ -225,10 +239,13 @@ constexpr int kLoadsPerThread = 2 * kTokChunk / kRowsPerPass;   // coefficient a
 __global__ __launch_bounds__(kGradWaves * kWave) void ke_grad(ChunkArgs a) {
   __shared__ float cs[kTokChunk][kGradPitch];   // coefficients [token][key]
   __shared__ float qs[kTokChunk][kGradPitch];   // queries [token][dim]
-  const int uh = blockIdx.x;
+  const int kty = (a.n + kGradTile - 1) / kGradTile, dtz = (a.half + kGradTile - 1) / kGradTile;
+  const HalfItem it = half_item(a.U, kty * dtz);     // grid 2U * kty * dtz, unit-major
+  const int uh = it.uh;
   const int u = uh >> 1, h = uh & 1;
   const int b = u / a.H, hh = u - b * a.H;
-  const int key0 = blockIdx.y * kGradTile, dim0 = blockIdx.z * kGradTile;
+  const int ky = it.i / dtz;
+  const int key0 = ky * kGradTile, dim0 = (it.i - ky * dtz) * kGradTile;
   const int T = a.T, n = a.n, half = a.half;
   const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
   const int kt = wave & 3, dt = wave >> 2;        // 16x16 tile of the block
@@ -302,12 +319,15 @@ __global__ __launch_bounds__(kGradWaves * kWave) void ke_grad(ChunkArgs a) {
   }
 }
 
-// K -= lr * dK for every key row of every unit and half.
-__global__ __launch_bounds__(256) void ke_apply(ChunkArgs a) {
+// K -= lr * dK for every key row of every unit and half; grid U * bpu
+// (unit-major): the bpu workgroups of a unit stride over its 2 n d_h entries.
+__global__ __launch_bounds__(256) void ke_apply(ChunkArgs a, int bpu) {
   const int64_t per = (int64_t)a.n * a.half;
-  const int64_t total = (int64_t)a.U * 2 * per;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
+  const int item = unit_affine_item(blockIdx.x, a.U, bpu);
+  const int unit = item / bpu, w = item - unit * bpu;
+  const int64_t e_end = ((int64_t)unit + 1) * 2 * per;
+  for (int64_t e = (int64_t)unit * 2 * per + (int64_t)w * blockDim.x + threadIdx.x; e < e_end;
+       e += (int64_t)bpu * blockDim.x) {
     const int64_t uh = e / per, r = e - uh * per;
     const int u = (int)(uh >> 1), h = (int)(uh & 1);
     const int b = u / a.H, hh = u - b * a.H;
@@ -323,8 +343,8 @@ hipError_t launch_ke_stats(const ChunkArgs& a, hipStream_t s, const LaunchTiming
     first.beg = tm->beg;
     last.end = tm->end;
   }
-  const dim3 tok_grid(2 * a.U, (a.T + kStatWaves - 1) / kStatWaves);
-  const dim3 key_grid(2 * a.U, (a.n + kWave - 1) / kWave);
+  const dim3 tok_grid((unsigned)(2 * a.U * ((a.T + kStatWaves - 1) / kStatWaves)));   // unit-major
+  const dim3 key_grid((unsigned)(2 * a.U * ((a.n + kWave - 1) / kWave)));
   const dim3 block(kStatWaves * kWave);
   const bool idw = a.mode == 0;
   hipError_t e = idw ? fw_launch(ke_tokstats<true>, tok_grid, block, 0, s, tm ? &first : nullptr, a)
@@ -339,14 +359,17 @@ hipError_t launch_ke_stats(const ChunkArgs& a, hipStream_t s, const LaunchTiming
 }
 
 hipError_t launch_ke_grad(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
-  const dim3 grid(2 * a.U, (a.n + kGradTile - 1) / kGradTile, (a.half + kGradTile - 1) / kGradTile);
+  const dim3 grid((unsigned)(2 * a.U * ((a.n + kGradTile - 1) / kGradTile) *
+                             ((a.half + kGradTile - 1) / kGradTile)));   // unit-major
   return fw_launch(ke_grad, grid, dim3(kGradWaves * kWave), 0, s, tm, a);
 }
 
 hipError_t launch_ke_apply(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
-  const int64_t total = (int64_t)a.U * 2 * a.n * a.half;
-  const int64_t blocks = (total + 255) / 256;
-  return fw_launch(ke_apply, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, tm, a);
+  const int64_t per_unit = (int64_t)2 * a.n * a.half;
+  int64_t bpu = (per_unit + 255) / 256;                 // workgroups per unit, about 4096 in all
+  const int64_t cap = 4096 / a.U > 0 ? 4096 / a.U : 1;
+  if (bpu > cap) bpu = cap;
+  return fw_launch(ke_apply, dim3((unsigned)(a.U * bpu)), dim3(256), 0, s, tm, a, (int)bpu);
 }
 
 }  // namespace fwpkm
