@@ -269,10 +269,10 @@ __device__ __forceinline__ skey min_lanes(skey x) {
 }
 
 // Bitonic sort of one packed key per lane within every aligned group of
-// GROUP lanes (16, 32 or 64), ascending in each group.  All lanes active.
+// GROUP lanes (8, 16, 32 or 64), ascending in each group.  All lanes active.
 template <int GROUP>
 __device__ __forceinline__ void sort_keys(skey& x) {
-  static_assert(GROUP == 16 || GROUP == 32 || GROUP == 64, "group");
+  static_assert(GROUP == 8 || GROUP == 16 || GROUP == 32 || GROUP == 64, "group");
   key_stages<GROUP, GROUP>(x);
 }
 

@@ -35,7 +35,7 @@
 // blocks of 128 or 256 keys each lane first takes the smallest value of its
 // candidates; the k-th smallest of those 64 values (a 32-bit bitonic sort)
 // bounds the answer, only the candidates at or below it are compacted into
-// LDS, and a 64-bit bitonic sort over 16, 32 or 64 lanes orders them.  Where
+// LDS, and a 64-bit bitonic sort over 8, 16, 32 or 64 lanes orders them.  Where
 // more than 64 pass (mass ties) and for 64-key blocks: a bitonic sort of the
 // first 64 candidates gives a threshold (the k-th best), the remaining ones
 // are filtered against it with one ballot per 64, and a bitonic sort of the
@@ -527,7 +527,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     }
     if (n <= kWave) {
       x = lane < n ? sv[lane] : kEmptyKey;
-      if (n <= 16) sort_keys<16>(x);
+      if (n <= 8) sort_keys<8>(x);
+      else if (n <= 16) sort_keys<16>(x);
       else if (n <= 32) sort_keys<32>(x);
       else sort_keys<64>(x);
       picked = true;
