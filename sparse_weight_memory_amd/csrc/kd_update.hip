@@ -49,19 +49,19 @@ __device__ __forceinline__ int region_at(int r, int units, int regions) {
   return (list * units + x * upx + ul) * regions + rg;
 }
 
-// pref[i] = tasks of the regions at positions [0, i) (region_at order) for i
-// in [0, L]; nlong / nshort / offs receive the regions' counts, by position.
-// All threads of the block take part.
+// pref[i] = tasks of the regions at positions [r0, i) (region_at order) for
+// i in [r0, r1]; nlong / nshort / offs receive those regions' counts, by
+// position.  All threads of the block take part.
 template <int W>
-__device__ void task_prefix(const int4* kinds, int L, int units, int regions, int* pref, int* nlong,
-                            int* nshort, int* offs, int* wtot) {
+__device__ void task_prefix(const int4* kinds, int r0, int r1, int units, int regions, int* pref,
+                            int* nlong, int* nshort, int* offs, int* wtot) {
   constexpr int NT = W * kWave;
   const int tid = threadIdx.x, wave = tid / kWave;
-  const int per = (L + NT - 1) / NT;
-  const int beg = tid * per;
+  const int per = (r1 - r0 + NT - 1) / NT;
+  const int beg = r0 + tid * per;
   int local = 0;
   for (int j = 0; j < per; ++j) {
-    if (beg + j < L) {
+    if (beg + j < r1) {
       const int4 kd = kinds[region_at(beg + j, units, regions)];
       nlong[beg + j] = kd.x;
       nshort[beg + j] = kd.y;
@@ -76,13 +76,30 @@ __device__ void task_prefix(const int4* kinds, int L, int units, int regions, in
   for (int w = 0; w < wave; ++w) base += wtot[w];
   int run = base + incl - local;
   for (int j = 0; j < per; ++j) {
-    if (beg + j < L) {
+    if (beg + j < r1) {
       pref[beg + j] = run;
       run += nlong[beg + j] + (nshort[beg + j] + W - 1) / W;
     }
   }
-  if (tid == NT - 1) pref[L] = run;
+  if (tid == NT - 1) pref[r1] = run;
   __syncthreads();
+}
+
+// The position in [r0, r1) of the region holding `task`: the largest r with
+// pref[r] <= task (pref is nondecreasing and pref[r0] <= task < pref[r1]).
+// A 64-way search per round: lane l tests position lo + l * step, and the
+// lanes that pass are a prefix of the wave.
+__device__ __forceinline__ int find_region(const int* pref, int r0, int r1, int task) {
+  int lo = r0, span = r1 - r0;
+  while (span > 1) {
+    const int step = (span + kWave - 1) / kWave;
+    const int at = lo + lane_id() * step;
+    const bool ok = at < lo + span && pref[at] <= task;
+    const int c = __popcll(__ballot(ok));        // >= 1: position lo passes
+    lo += (c - 1) * step;
+    span = min(step, r0 + (r1 - r0) - lo);
+  }
+  return lo;
 }
 
 // A table row as R float4 per lane, unguarded: columns past the row re-read
@@ -231,30 +248,25 @@ __global__ __launch_bounds__(W * kWave, kd_waves_per_simd<W>()) void kd_update(C
   int* nshort = nlong + L;                                            // [L]
   int* offs = nshort + L;                                             // [L]
   int* wtot = offs + L;                                               // [W]
-  task_prefix<W>(a.kinds, L, a.U, a.regions, pref, nlong, nshort, offs, wtot);
   // workgroups of XCD x take the tasks of that XCD's units (the grid is a
-  // multiple of 8 then); otherwise every workgroup strides over all tasks
-  int r_lo = 0, r_hi = L, t_first = blockIdx.x, t_end = pref[L], t_step = gridDim.x;
+  // multiple of 8 then) and count only those regions; otherwise every
+  // workgroup strides over all tasks
+  int r_lo = 0, r_hi = L, t_first = blockIdx.x, t_step = gridDim.x;
   if (a.U % kXcds == 0) {
-    const int x = blockIdx.x % kXcds;
-    r_lo = x * (L / kXcds);
+    r_lo = (blockIdx.x % kXcds) * (L / kXcds);
     r_hi = r_lo + L / kXcds;
-    t_first = pref[r_lo] + blockIdx.x / kXcds;
-    t_end = pref[r_hi];
+    t_first = blockIdx.x / kXcds;
     t_step = gridDim.x / kXcds;
   }
+  task_prefix<W>(a.kinds, r_lo, r_hi, a.U, a.regions, pref, nlong, nshort, offs, wtot);
+  const int t_end = pref[r_hi];
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int P = a.P;
   const float lr = a.lr;
 
   for (int task = t_first; task < t_end; task += t_step) {
-    // region (position) holding this task
-    int lo = r_lo, hi = r_hi;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pref[mid] <= task) lo = mid; else hi = mid;
-    }
+    const int lo = find_region(pref, r_lo, r_hi, task);   // region (position) holding this task
     const int j = task - pref[lo];
     const int lu = region_at(lo, a.U, a.regions) / a.regions;   // list * U + unit
     const int list = lu / a.U;
