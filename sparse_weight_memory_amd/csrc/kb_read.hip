@@ -58,32 +58,43 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
 
   // loads that do not depend on the selection go out first, all together:
   // nothing here sits behind a branch (a load inside one is waited for on
-  // its own), values a lane or mode does not use are masked afterwards
-  const float qn = (a.qnorm[ut * 2] + a.qnorm[ut * 2 + 1]) * (a.mode == 0 ? 1.f : 0.f);
-  // token-importance weight of this token's loss; 0 = read only, no write
-  const float lam = (WRITE && a.tw) ? a.tw[io] : 1.0f;
-  float4 yv[VR];
-#pragma unroll
-  for (int j = 0; j < VR; ++j) {
-    const int c = lane + 64 * j;
-    yv[j] = (WRITE && c < dv4) ? reinterpret_cast<const float4*>(a.y + io * a.dv)[c]
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-
-  // ---- 1. per-half best-k lists (lane m < k holds the m-th best), as
-  // packed (ordering key, sub-key index) keys
-  skey hk[2];
+  // its own), values a lane or mode does not use are masked afterwards.
+  // Loads complete in issue order, so the candidate lists (wanted first, and
+  // in this XCD's L2) go out before the target row (from HBM, wanted last).
+  int ix[2];
+  float ov[2];
   if (a.nblk == 1) {
     // lanes past k re-read entry 0 and are masked to the empty key
     const int li = lane < k ? lane : 0;
-    int ix[2];
-    float ov[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int64_t base = (ut * 2 + h) * k;
       ix[h] = a.half_i[base + li];
       ov[h] = a.half_o[base + li];
     }
+  }
+  const float qn = (a.qnorm[ut * 2] + a.qnorm[ut * 2 + 1]) * (a.mode == 0 ? 1.f : 0.f);
+  // token-importance weight of this token's loss; 0 = read only, no write.
+  // Without weights the load reads this token's query norm instead (any
+  // valid address), so that it never sits behind a branch.
+  const bool has_tw = WRITE && a.tw != nullptr;
+  const float lam_ld = *(has_tw ? a.tw + io : a.qnorm + ut * 2);
+  const float lam = has_tw ? lam_ld : 1.0f;
+  float4 yv[VR];
+#pragma unroll
+  for (int j = 0; j < VR; ++j) {
+    yv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (WRITE) {
+      // columns past the row re-read its last float4, zeroed when used
+      const int c = lane + 64 * j;
+      yv[j] = reinterpret_cast<const float4*>(a.y + io * a.dv)[c < dv4 ? c : dv4 - 1];
+    }
+  }
+
+  // ---- 1. per-half best-k lists (lane m < k holds the m-th best), as
+  // packed (ordering key, sub-key index) keys
+  skey hk[2];
+  if (a.nblk == 1) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const unsigned int m32 = opaque_mask(lane < k && ix[h] != kNoIndex);
