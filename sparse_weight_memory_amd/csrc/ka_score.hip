@@ -46,6 +46,7 @@
 // keys in that XCD's L2.
 
 #include <algorithm>
+#include <utility>
 
 #include "fwpkm_device.h"
 #include "fwpkm_launch.h"
@@ -126,31 +127,43 @@ __device__ __forceinline__ unsigned int lds_offset(const float* p) {
 
 // 2 S 16-byte LDS reads (S key operands, S query operands) issued together,
 // with the wait for all of them inside the same asm block, so no result is
-// visible before it has arrived.
-template <int S>
+// visible before it has arrived.  KOFF / QOFF are byte offsets added to every
+// key / query address as the instructions' immediate offsets.
+template <int S, int KOFF, int QOFF>
 __device__ __forceinline__ void lds_read_wait(v4f (&ka)[S], v4f (&qa)[S], const unsigned int (&ka_at)[S],
                                               const unsigned int (&qa_at)[S]) {
 #if __HIP_DEVICE_COMPILE__
   static_assert(S == 2 || S == 4, "two or four steps per chunk");
+  static_assert(KOFF >= 0 && KOFF < 65536 && QOFF >= 0 && QOFF < 65536, "16-bit LDS offsets");
   if constexpr (S == 4) {
     asm volatile(
-        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
-        "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+        "ds_read_b128 %0, %8 offset:%16\n\tds_read_b128 %1, %9 offset:%16\n\t"
+        "ds_read_b128 %2, %10 offset:%16\n\tds_read_b128 %3, %11 offset:%16\n\t"
+        "ds_read_b128 %4, %12 offset:%17\n\tds_read_b128 %5, %13 offset:%17\n\t"
+        "ds_read_b128 %6, %14 offset:%17\n\tds_read_b128 %7, %15 offset:%17\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(ka[0]), "=&v"(ka[1]), "=&v"(ka[2]), "=&v"(ka[3]),
           "=&v"(qa[0]), "=&v"(qa[1]), "=&v"(qa[2]), "=&v"(qa[3])
         : "v"(ka_at[0]), "v"(ka_at[1]), "v"(ka_at[2]), "v"(ka_at[3]),
-          "v"(qa_at[0]), "v"(qa_at[1]), "v"(qa_at[2]), "v"(qa_at[3]));
+          "v"(qa_at[0]), "v"(qa_at[1]), "v"(qa_at[2]), "v"(qa_at[3]), "i"(KOFF), "i"(QOFF));
   } else {
     asm volatile(
-        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "ds_read_b128 %0, %4 offset:%8\n\tds_read_b128 %1, %5 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%9\n\tds_read_b128 %3, %7 offset:%9\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(ka[0]), "=&v"(ka[1]), "=&v"(qa[0]), "=&v"(qa[1])
-        : "v"(ka_at[0]), "v"(ka_at[1]), "v"(qa_at[0]), "v"(qa_at[1]));
+        : "v"(ka_at[0]), "v"(ka_at[1]), "v"(qa_at[0]), "v"(qa_at[1]), "i"(KOFF), "i"(QOFF));
   }
 #else
   (void)ka; (void)qa; (void)ka_at; (void)qa_at;
 #endif
+}
+
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1 (an unrolled loop whose
+// index is a compile-time constant).
+template <class F, int... I>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
 }
 
 // s_waitcnt that waits until at most n vector-memory operations are
@@ -273,20 +286,26 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
       *reinterpret_cast<float4*>(&buf[r * kKPitch + (lane % kLanesPerRow) * 4]) = src[j];
     }
   };
-  // direct staging: this wave's ring and the per-lane source offsets of a
-  // chunk's loads (chunk c adds c * kDimChunk)
-  float* wring = kst + wave * kPrefetch * 16 * kDimChunk;
+  // direct staging: this wave's ring (a wave-uniform base, so the LDS
+  // destination is set with scalar moves) and the per-lane byte offsets of a
+  // chunk's loads; chunk c adds the scalar offset 4 c kDimChunk.  Buffer loads
+  // over this unit's half table: an address past it reads zero.
+  float* wring = kst + __builtin_amdgcn_readfirstlane(wave) * kPrefetch * 16 * kDimChunk;
   int dma_off[kStageF4];
-  auto dma_issue = [&](int c) {
+#if __HIP_DEVICE_COMPILE__
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(kbase), (short)0, a.n * half * 4, 0x00020000);
+#endif
+  auto dma_issue = [&](int c, int slot) __attribute__((always_inline)) {
     // chunks past the end re-read chunk 0 into a slot nobody reads again
-    const int cofs = c < nchunks ? c * kDimChunk : 0;
-    float* dst = wring + (c % kPrefetch) * 16 * kDimChunk;
+    const int cofs = c < nchunks ? c * kDimChunk * 4 : 0;
+    float* dst = wring + slot * 16 * kDimChunk;
 #if __HIP_DEVICE_COMPILE__   // a device builtin: the host pass only needs the kernel's stub
 #pragma unroll
     for (int j = 0; j < kStageF4; ++j)
-      __builtin_amdgcn_global_load_lds(kbase + dma_off[j] + cofs,
-                                       (__attribute__((address_space(3))) void*)(dst + j * kRowsPerLoad * kDimChunk),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krsrc, (__attribute__((address_space(3))) void*)(dst + j * kRowsPerLoad * kDimChunk), 16, dma_off[j],
+          cofs, 0, 0);
 #else
     (void)cofs;
     (void)dst;
@@ -298,10 +317,10 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
       const int r = j * kRowsPerLoad + lane / kLanesPerRow;
       const int gk = kb * blk + kt * 16 + r;
       const int col = (lane % kLanesPerRow) ^ dma_swizzle<kDimChunk>(r);
-      dma_off[j] = (gk < a.n ? gk : 0) * half + dq * share + col * 4;
+      dma_off[j] = ((gk < a.n ? gk : 0) * half + dq * share + col * 4) * 4;   // bytes
     }
 #pragma unroll
-    for (int i = 0; i + 1 < kPrefetch; ++i) dma_issue(i);    // in flight while queries are staged
+    for (int i = 0; i + 1 < kPrefetch; ++i) dma_issue(i, i);    // in flight while queries are staged
   } else {
 #pragma unroll
     for (int i = 0; i < kPrefetch; ++i) stage_load(stg[i], i);   // in flight while queries are staged
@@ -368,37 +387,46 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     // chunk c sits in slot c % kPrefetch; the loads of chunk c + kPrefetch - 1
     // refill the slot chunk c - 1 was read from (those reads fed the matrix
     // core already), then the wave waits until at most the newer chunks'
-    // loads are outstanding: loads complete in order, so chunk c is in LDS
-    for (int c = 0; c < nchunks_p; ++c) {
-      dma_issue(c + kPrefetch - 1);
-      wait_vm_at_most<(kPrefetch - 1) * kStageF4>();
-      const float* slot = wring + (c % kPrefetch) * 16 * kDimChunk + row * kDimChunk;
-      const int sw = dma_swizzle<kDimChunk>(row);
-      // the chunk's operands in one block of LDS reads that waits for them
-      // itself: read as ordinary loads, each would first wait for every
-      // outstanding direct load (the compiler cannot tell the slots apart)
-      constexpr int kSteps = kDimChunk / 16;
-      v4f akv[kSteps], bqv[kSteps];
-      {
-        unsigned int ka_at[kSteps], qa_at[kSteps];
+    // loads are outstanding: loads complete in order, so chunk c is in LDS.
+    // The loop runs whole ring turns, so a chunk's slot is a constant and its
+    // operand reads take fixed per-lane addresses plus immediate offsets.
+    constexpr int kSteps = kDimChunk / 16;
+    constexpr int kSlotBytes = 4 * 16 * kDimChunk;
+    const int sw = dma_swizzle<kDimChunk>(row);
+    unsigned int ka_at[kSteps], qa_at[kSteps];
 #pragma unroll
-        for (int j = 0; j < kSteps; ++j) {
-          ka_at[j] = lds_offset(&slot[((4 * j + quad) ^ sw) * 4]);
-          qa_at[j] = lds_offset(&arow_base[(c * kSteps + j) * 16 + quad * 4]);
-        }
-        lds_read_wait<kSteps>(akv, bqv, ka_at, qa_at);
-      }
+    for (int j = 0; j < kSteps; ++j) {
+      ka_at[j] = lds_offset(&wring[row * kDimChunk + ((4 * j + quad) ^ sw) * 4]);
+      qa_at[j] = lds_offset(&arow_base[j * 16 + quad * 4]);
+    }
+    for (int c0 = 0; c0 < nchunks_p; c0 += kPrefetch) {
+      unsigned int qa_turn[kSteps];
 #pragma unroll
-      for (int j = 0; j < kDimChunk / 16; ++j) {
-        const v4f ak = akv[j];
-        const v4f bq = bqv[j];
-        ksq = fmaf(ak.x, ak.x, ksq); ksq = fmaf(ak.y, ak.y, ksq);
-        ksq = fmaf(ak.z, ak.z, ksq); ksq = fmaf(ak.w, ak.w, ksq);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.x, bq.x, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.z, bq.z, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.y, bq.y, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.w, bq.w, acc1, 0, 0, 0);
-      }
+      for (int j = 0; j < kSteps; ++j) qa_turn[j] = qa_at[j] + c0 * kSteps * 64;
+      unroll_seq(
+          [&](auto s_c) __attribute__((always_inline)) {
+            constexpr int s = decltype(s_c)::value;
+            dma_issue(c0 + s + kPrefetch - 1, (s + kPrefetch - 1) % kPrefetch);
+            wait_vm_at_most<(kPrefetch - 1) * kStageF4>();
+            // the chunk's operands in one block of LDS reads that waits for
+            // them itself: read as ordinary loads, each would first wait for
+            // every outstanding direct load (the compiler cannot tell the
+            // slots apart)
+            v4f akv[kSteps], bqv[kSteps];
+            lds_read_wait<kSteps, s * kSlotBytes, s * kSteps * 64>(akv, bqv, ka_at, qa_turn);
+#pragma unroll
+            for (int j = 0; j < kSteps; ++j) {
+              const v4f ak = akv[j];
+              const v4f bq = bqv[j];
+              ksq = fmaf(ak.x, ak.x, ksq); ksq = fmaf(ak.y, ak.y, ksq);
+              ksq = fmaf(ak.z, ak.z, ksq); ksq = fmaf(ak.w, ak.w, ksq);
+              acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.x, bq.x, acc0, 0, 0, 0);
+              acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.z, bq.z, acc1, 0, 0, 0);
+              acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.y, bq.y, acc0, 0, 0, 0);
+              acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ak.w, bq.w, acc1, 0, 0, 0);
+            }
+          },
+          std::make_integer_sequence<int, kPrefetch>{});
     }
     wait_vm_at_most<0>();   // the overrun loads land before the area is reused
     query_norms();
