@@ -654,13 +654,16 @@ hipError_t launch_ka_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* t
 
 hipError_t launch_ka(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
   {
-    // full shapes (every 32-dim chunk of a share inside d_h, four per slot
-    // ring turn) stage keys straight into LDS when the rings fit
+    // full shapes (every 32-dim chunk of a share inside d_h, whole ring
+    // turns of four slots, else of two) stage keys straight into LDS when the
+    // rings fit
     const int ndq = kScoreWaves / (a.key_block / 16);
     const int share = ((a.half + 16 * ndq - 1) / (16 * ndq)) * 16;
-    const bool full32 = share % 32 == 0 && ndq * share <= a.half && (share / 32) % 4 == 0;
-    if (full32 && ka_smem_bytes<32, 4, true>(a.half, a.key_block) <= kLdsBytes)
+    const bool full32 = share % 32 == 0 && ndq * share <= a.half;
+    if (full32 && (share / 32) % 4 == 0 && ka_smem_bytes<32, 4, true>(a.half, a.key_block) <= kLdsBytes)
       return launch_ka_full<32, 4, true, true>(a, s, tm);
+    if (full32 && (share / 32) % 2 == 0 && ka_smem_bytes<32, 2, true>(a.half, a.key_block) <= kLdsBytes)
+      return launch_ka_full<32, 2, true, true>(a, s, tm);
   }
   // wider chunks halve the barriers per contraction; they fit for d_h <= 256.
   // A ring deeper than the chunk count would only multiply zeros.
