@@ -21,6 +21,29 @@ constexpr int kUpdMaxLists = 3072;  // 3 * units the update kernel can index
 constexpr int kNoIndex = 0x7fffffff;
 
 // Everything a chunk's kernels need, passed by value.
+// Division by a divisor d >= 1 fixed for a launch, for dividends 0 <= x < 2^31:
+// x / d = (umulhi(x, m) + x) >> l with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1 (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994).  The host derives (m, l)
+// once; in a kernel the quotient costs three scalar instructions where a
+// runtime integer division costs about thirty, and the scalar unit is shared
+// by every wave of a compute unit.
+struct FastDiv {
+  unsigned int m;
+  int l;
+};
+
+inline FastDiv make_fastdiv(int d) {
+  int l = 0;
+  while ((1ll << l) < (long long)d) ++l;
+  const unsigned long long m = ((1ull << 32) * ((1ull << l) - (unsigned long long)d)) / (unsigned long long)d + 1;
+  return FastDiv{(unsigned int)m, l};
+}
+
+__device__ __forceinline__ int fast_div(int x, FastDiv f) {
+  return (int)((__umulhi((unsigned int)x, f.m) + (unsigned int)x) >> f.l);
+}
+
 struct ChunkArgs {
   // sizes
   int n;          // sub-keys per half
@@ -78,6 +101,13 @@ struct ChunkArgs {
   float* addr_dk;      // [U, 2, n, d_h] addressing gradient of each key row
   float* addr_tok;     // [U, 2, T, 2] per token: softmax shift m (dot) and 1 / softmax sum
   float* addr_ell;     // [U, 2, n] log marginal usage of each sub-key
+  // score-kernel geometry, derived on the host by its launcher
+  int ka_ntt;          // 16-token tiles = ceil(T / 16)
+  int ka_nkt_log2;     // log2(key_block / 16): key tiles per block
+  int ka_share;        // dims of d_h per dim share of a wave
+  FastDiv ka_div_ntt;  // x / ka_ntt
+  FastDiv ka_div_nblk; // x / nblk
+  FastDiv ka_div_H;    // x / H
 };
 
 // The sequence-level layer around the chunk step (queries/values projected

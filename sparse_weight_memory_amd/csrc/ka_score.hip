@@ -91,20 +91,32 @@ struct Staging {
 // Chunks of DC dims per dim share, rounded up to a multiple of the ring
 // depth PF (the extra chunks hold zero keys).
 template <int DC, int PF>
-__host__ __device__ inline int ka_chunks(int half, int blk) {
+__host__ __device__ inline int ka_chunks_of(int share) {
+  const unsigned int nchunks = ((unsigned int)share + DC - 1) / DC;
+  return (int)((nchunks + PF - 1) / PF * PF);
+}
+
+// dims of d_h per dim share of a wave
+inline int ka_share(int half, int blk) {
   const int ndq = kScoreWaves / (blk / 16);
-  const int share = ((half + 16 * ndq - 1) / (16 * ndq)) * 16;
-  const int nchunks = (share + DC - 1) / DC;
-  return (nchunks + PF - 1) / PF * PF;
+  return ((half + 16 * ndq - 1) / (16 * ndq)) * 16;
+}
+
+template <int DC, int PF>
+inline int ka_chunks(int half, int blk) {
+  return ka_chunks_of<DC, PF>(ka_share(half, blk));
 }
 
 // Width of a staged query row: every dim a chunk of any dim share may touch
 // (columns past d_h are zero), so operand reads need no bounds test.
 template <int DC, int PF>
-__host__ __device__ inline int ka_query_width(int half, int blk) {
-  const int ndq = kScoreWaves / (blk / 16);
-  const int share = ((half + 16 * ndq - 1) / (16 * ndq)) * 16;
-  return (ndq - 1) * share + ka_chunks<DC, PF>(half, blk) * DC;
+__host__ __device__ inline int ka_query_width_of(int share, int ndq) {
+  return (ndq - 1) * share + ka_chunks_of<DC, PF>(share) * DC;
+}
+
+template <int DC, int PF>
+inline int ka_query_width(int half, int blk) {
+  return ka_query_width_of<DC, PF>(ka_share(half, blk), kScoreWaves / (blk / 16));
 }
 
 // Key staging straight from global memory into LDS (kDma, only with kFull):
@@ -187,10 +199,14 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   constexpr int kRowsPerLoad = Staging<kDimChunk, kPrefetch>::kRowsPerLoad;
   extern __shared__ float smem[];
   const int half = a.half;
+  // launch geometry from the host (shifts and multiply-shift divisions:
+  // the prologue's scalar work is issued once per wave of the workgroup)
   const int blk = a.key_block;             // 64, 128 or 256
-  const int nkt = blk / 16;                // key tiles per block
-  const int ndq = kScoreWaves / nkt;       // dim shares per key tile
-  const int qwidth = ka_query_width<kDimChunk, kPrefetch>(half, blk);
+  const int blk_log2 = a.ka_nkt_log2 + 4;
+  const int nkt = 1 << a.ka_nkt_log2;      // key tiles per block
+  const int ndq = kScoreWaves >> a.ka_nkt_log2;   // dim shares per key tile
+  const int share = a.ka_share;            // dims per share
+  const int qwidth = ka_query_width_of<kDimChunk, kPrefetch>(share, ndq);
   const int qpitch = qwidth + 4;
   float* qs = smem;                                      // [16][qpitch]
   float* kst = qs + kTokTile * qpitch;                   // staged keys (register ring: [16 waves][2][16][kKPitch];
@@ -205,32 +221,31 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
                 "survivors fit the staging area");
   skey* surv = reinterpret_cast<skey*>(kst + kSurvOffset);   // [16][blk] survivors
 
-  const int ntt = (a.T + kTokTile - 1) / kTokTile;
+  const int ntt = a.ka_ntt;
   const int total = a.U * 2 * a.nblk * ntt;
-  const int per_xcd = (total + 7) / 8;
+  const int per_xcd = (int)(((unsigned int)total + 7) / 8);
   const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (L >= total) return;
-  const int tt = L % ntt;
-  int rest = L / ntt;
-  const int kb = rest % a.nblk;
-  rest /= a.nblk;
-  const int h = rest % 2;
-  const int u = rest / 2;
-  const int b = u / a.H, hh = u % a.H;
+  const int r1 = fast_div(L, a.ka_div_ntt);
+  const int tt = L - r1 * ntt;
+  const int r2 = fast_div(r1, a.ka_div_nblk);
+  const int kb = r1 - r2 * a.nblk;
+  const int h = r2 & 1;
+  const int u = r2 >> 1;
+  const int b = fast_div(u, a.ka_div_H), hh = u - b * a.H;
   const int t0 = tt * kTokTile;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = lane_id();
 
   // ---- geometry: wave (kt, dq) = key tile kt over dim share dq
-  const int kt = wave % nkt;
-  const int dq = wave / nkt;
+  const int kt = wave & (nkt - 1);
+  const int dq = wave >> a.ka_nkt_log2;
   const int row = lane & 15;          // A row (key) / B column (token)
   const int quad = lane >> 4;         // 4-dim group inside a 16-dim step
-  const int share = ((half + 16 * ndq - 1) / (16 * ndq)) * 16;   // dims per share
-  const int steps = share / 16;
-  const int nchunks = (share + kDimChunk - 1) / kDimChunk;      // chunks holding data
-  const int nchunks_p = ka_chunks<kDimChunk, kPrefetch>(half, blk); // chunks multiplied
+  const int steps = (int)((unsigned int)share / 16);
+  const int nchunks = (int)(((unsigned int)share + kDimChunk - 1) / kDimChunk);   // chunks holding data
+  const int nchunks_p = ka_chunks_of<kDimChunk, kPrefetch>(share);            // chunks multiplied
   const float* kbase = (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k + (int64_t)hh * a.n * half;
 
   // ---- key staging, private to each wave: chunk c holds the wave's 16 key
@@ -311,6 +326,13 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     (void)dst;
 #endif
   };
+  const int half4 = half >> 2;
+  const int qw4 = qwidth >> 2;
+  // direct staging of the query tile too, when a row is whole 64-lane loads
+  // (every staged column then lies inside d_h): wave w loads token t0 + w
+  // into row w of the tile; rows past the chunk's last token lie past the
+  // buffer's end and read zero
+  const bool q_direct = kDma && qw4 % kWave == 0;
   if constexpr (kDma) {
 #pragma unroll
     for (int j = 0; j < kStageF4; ++j) {
@@ -318,6 +340,21 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
       const int gk = kb * blk + kt * 16 + r;
       const int col = (lane % kLanesPerRow) ^ dma_swizzle<kDimChunk>(r);
       dma_off[j] = ((gk < a.n ? gk : 0) * half + dq * share + col * 4) * 4;   // bytes
+    }
+    if (q_direct) {
+      // issued ahead of the ring's chunks: loads retire in order, so the
+      // tile is complete while the chunks are still in flight
+#if __HIP_DEVICE_COMPILE__
+      const int64_t qrow = (int64_t)a.H * a.dqk;               // floats between tokens
+      const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.q + ((int64_t)(b * a.T + t0) * a.H + hh) * a.dqk + h * half), (short)0,
+          (int)(((a.T - 1 - t0) * qrow + half) * 4), 0x00020000);
+      float* qdst = qs + __builtin_amdgcn_readfirstlane(wave) * qpitch;
+      const int qoff = (int)(__builtin_amdgcn_readfirstlane(wave) * qrow * 4);
+      for (int m = 0; m < qw4 / kWave; ++m)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (__attribute__((address_space(3))) void*)(qdst + m * 4 * kWave),
+                                                 16, lane * 16 + m * 16 * kWave, qoff, 0, 0);
+#endif
     }
 #pragma unroll
     for (int i = 0; i + 1 < kPrefetch; ++i) dma_issue(i, i);    // in flight while queries are staged
@@ -327,23 +364,28 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   }
 
   // ---- stage the 16-token query tile (this half) in LDS
-  const int half4 = half >> 2;
-  const int qw4 = qwidth >> 2;
-  for (int e = tid; e < kTokTile * qw4; e += kScoreWaves * kWave) {
-    const int r = e / qw4, c4 = e - r * qw4;
-    const int t = t0 + r;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < a.T && c4 < half4) {
-      const float* qrow = a.q + ((int64_t)(b * a.T + t) * a.H + hh) * a.dqk + h * half;
-      x = reinterpret_cast<const float4*>(qrow)[c4];
+  if (!q_direct) {
+    for (int e = tid; e < kTokTile * qw4; e += kScoreWaves * kWave) {
+      const int r = e / qw4, c4 = e - r * qw4;
+      const int t = t0 + r;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < a.T && c4 < half4) {
+        const float* qrow = a.q + ((int64_t)(b * a.T + t) * a.H + hh) * a.dqk + h * half;
+        x = reinterpret_cast<const float4*>(qrow)[c4];
+      }
+      *reinterpret_cast<float4*>(&qs[r * qpitch + c4 * 4]) = x;
     }
-    *reinterpret_cast<float4*>(&qs[r * qpitch + c4 * 4]) = x;
   }
   if constexpr (!kDma) {
     stage_store(stg[0], 0);
     stage_load(stg[0], kPrefetch);
+    __syncthreads();
+  } else {
+    // this wave's query row has landed (only the ring's chunks may still be
+    // in flight); __syncthreads() would also wait for those (vmcnt(0))
+    if (q_direct) wait_vm_at_most<(kPrefetch - 1) * kStageF4>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  __syncthreads();
 
   // ---- query norms (fp64 sums), once per token and half; wave w <-> token w.
   // With direct staging they are stored after the contraction, so that only
@@ -480,7 +522,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
       const int e = tid + i * kScoreWaves * kWave;
       float o = __builtin_inff();
       if (e < nent) {
-        const int tok = e / blk, kk = e - tok * blk;
+        const int tok = e >> blk_log2, kk = e - (tok << blk_log2);
         const int gkey = kb * blk + kk;
         if (gkey < a.n && t0 + tok < a.T) {
           double dot = 0.0, kn = 0.0;
@@ -498,7 +540,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     for (int i = 0; i < kMaxBlk * kTokTile / (kScoreWaves * kWave); ++i) {
       const int e = tid + i * kScoreWaves * kWave;
       if (e < nent) {
-        const int tok = e / blk, kk = e - tok * blk;
+        const int tok = e >> blk_log2, kk = e - (tok << blk_log2);
         sc[tok * ppitch + kk] = oval[i];
       }
     }
@@ -510,7 +552,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   if (a.addr_s) {
     float* dst = a.addr_s + ((int64_t)(u * 2 + h) * a.T + t0) * a.addr_np + kb * blk;
     for (int e = tid; e < kTokTile * blk; e += kScoreWaves * kWave) {
-      const int r = e / blk, c = e - r * blk;
+      const int r = e >> blk_log2, c = e - (r << blk_log2);
       if (t0 + r < a.T && kb * blk + c < a.n) dst[(int64_t)r * a.addr_np + c] = sc[r * ppitch + c];
     }
   }
@@ -534,7 +576,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     // sort.  When more than a wave's worth pass (mass ties, or fewer than k
     // real keys in the block) the general path below runs instead.
     constexpr int kR = kMaxBlk / kWave;
-    const int nr = blk / kWave;
+    const int nr = blk >> 6;
     skey cr[kR];
     unsigned int lo_hi = 0xFFFFFFFFu;
 #pragma unroll
@@ -652,7 +694,16 @@ hipError_t launch_ka_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* t
 
 }  // namespace
 
-hipError_t launch_ka(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
+hipError_t launch_ka(const ChunkArgs& args, hipStream_t s, const LaunchTiming* tm) {
+  // the launch geometry the kernel takes ready-made
+  ChunkArgs a = args;
+  a.ka_ntt = (a.T + kTokTile - 1) / kTokTile;
+  a.ka_nkt_log2 = 0;
+  while ((16 << a.ka_nkt_log2) < a.key_block) ++a.ka_nkt_log2;   // key_block = 16 << log2, a power of two
+  a.ka_share = ka_share(a.half, a.key_block);
+  a.ka_div_ntt = make_fastdiv(std::max(1, a.ka_ntt));
+  a.ka_div_nblk = make_fastdiv(std::max(1, a.nblk));
+  a.ka_div_H = make_fastdiv(std::max(1, a.H));
   {
     // full shapes (every 32-dim chunk of a share inside d_h, whole ring
     // turns of four slots, else of two) stage keys straight into LDS when the
