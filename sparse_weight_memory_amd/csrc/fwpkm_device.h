@@ -107,8 +107,23 @@ struct ChunkArgs {
   int ka_share;        // dims of d_h per dim share of a wave
   FastDiv ka_div_ntt;  // x / ka_ntt
   FastDiv ka_div_nblk; // x / nblk
-  FastDiv ka_div_H;    // x / H
+  // divisors of the work-item decompositions, derived on the host by every
+  // launcher that uses them (with_divisors)
+  FastDiv div_H;       // x / H
+  FastDiv div_U;       // x / U
+  FastDiv div_upx;     // x / (U / 8): units per XCD
+  FastDiv div_nbx;     // x / ceil(T / 4): read workgroups per unit
 };
+
+// `a` with the decomposition divisors filled in
+inline ChunkArgs with_divisors(const ChunkArgs& a) {
+  ChunkArgs g = a;
+  g.div_H = make_fastdiv(a.H > 1 ? a.H : 1);
+  g.div_U = make_fastdiv(a.U > 1 ? a.U : 1);
+  g.div_upx = make_fastdiv(a.U / 8 > 1 ? a.U / 8 : 1);
+  g.div_nbx = make_fastdiv((a.T + 3) / 4 > 1 ? (a.T + 3) / 4 : 1);
+  return g;
+}
 
 // The sequence-level layer around the chunk step (queries/values projected
 // from model-width tokens, lookahead targets, gated output).

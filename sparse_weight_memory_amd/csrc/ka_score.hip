@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   const int kb = r1 - r2 * a.nblk;
   const int h = r2 & 1;
   const int u = r2 >> 1;
-  const int b = fast_div(u, a.ka_div_H), hh = u - b * a.H;
+  const int b = fast_div(u, a.div_H), hh = u - b * a.H;
   const int t0 = tt * kTokTile;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -696,14 +696,13 @@ hipError_t launch_ka_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* t
 
 hipError_t launch_ka(const ChunkArgs& args, hipStream_t s, const LaunchTiming* tm) {
   // the launch geometry the kernel takes ready-made
-  ChunkArgs a = args;
+  ChunkArgs a = with_divisors(args);
   a.ka_ntt = (a.T + kTokTile - 1) / kTokTile;
   a.ka_nkt_log2 = 0;
   while ((16 << a.ka_nkt_log2) < a.key_block) ++a.ka_nkt_log2;   // key_block = 16 << log2, a power of two
   a.ka_share = ka_share(a.half, a.key_block);
   a.ka_div_ntt = make_fastdiv(std::max(1, a.ka_ntt));
   a.ka_div_nblk = make_fastdiv(std::max(1, a.nblk));
-  a.ka_div_H = make_fastdiv(std::max(1, a.H));
   {
     // full shapes (every 32-dim chunk of a share inside d_h, whole ring
     // turns of four slots, else of two) stage keys straight into LDS when the

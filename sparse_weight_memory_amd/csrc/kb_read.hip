@@ -45,12 +45,12 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   const int lane = lane_id();
   const int nbx = (a.T + 3) >> 2;                      // 4 tokens per workgroup
   const int item = unit_affine_item(blockIdx.x, a.U, nbx);
-  const int u = item / nbx;
+  const int u = fast_div(item, a.div_nbx);
   const int t = (item - u * nbx) * 4 + wave;
   if (t >= a.T) return;
   const int k = a.k;
   const int n = a.n;
-  const int b = u / a.H, hh = u % a.H;
+  const int b = fast_div(u, a.div_H), hh = u - b * a.H;
   const int64_t ut = (int64_t)u * a.T + t;
   const float inf = __builtin_inff();
   const int64_t io = ((int64_t)(b * a.T + t) * a.H + hh);
@@ -372,7 +372,8 @@ hipError_t launch_kb_k(const ChunkArgs& a, bool write, hipStream_t s, const Laun
 
 }  // namespace
 
-hipError_t launch_kb(const ChunkArgs& a, bool write, hipStream_t s, const LaunchTiming* tm) {
+hipError_t launch_kb(const ChunkArgs& args, bool write, hipStream_t s, const LaunchTiming* tm) {
+  const ChunkArgs a = with_divisors(args);
   if (a.k <= 4) return launch_kb_k<4>(a, write, s, tm);
   if (a.k <= 8) return launch_kb_k<8>(a, write, s, tm);
   if (a.k <= 16) return launch_kb_k<16>(a, write, s, tm);

@@ -111,9 +111,10 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   extern __shared__ int lds[];
   const int per_unit = 3 * a.regions;
   const int item = unit_affine_item(blockIdx.x, a.U, per_unit);
-  const int u = item / per_unit;
-  const int list = (item - u * per_unit) / a.regions;   // 0 = V slots, 1 = K1 rows, 2 = K2 rows
-  const int region = item - u * per_unit - list * a.regions;
+  const int lr = item >> a.region_bits;   // u * 3 + list (regions is a power of two)
+  const int u = lr / 3;
+  const int list = lr - 3 * u;            // 0 = V slots, 1 = K1 rows, 2 = K2 rows
+  const int region = item & (a.regions - 1);
   const int P = a.P;
   int* key0 = lds;                        // [P] rows (ping)
   int* idx0 = key0 + P;                   // [P] pair indices (ping)

@@ -38,22 +38,23 @@ namespace {
 // (list * U + x * (U / 8) + ul) * regions + rg, so the regions of the units
 // XCD x runs (see unit_affine_item) are positions [x L / 8, (x + 1) L / 8).
 // The identity otherwise.
-__device__ __forceinline__ int region_at(int r, int units, int regions) {
+__device__ __forceinline__ int region_at(int r, const ChunkArgs& a) {
+  const int units = a.U;
   if (units % kXcds != 0) return r;
   const int upx = units / kXcds;
-  const int rg = r % regions;
-  int rest = r / regions;
-  const int ul = rest % upx;
-  rest /= upx;
-  const int list = rest % 3, x = rest / 3;
-  return (list * units + x * upx + ul) * regions + rg;
+  const int rg = r & (a.regions - 1);           // regions is a power of two
+  const int rest = r >> a.region_bits;
+  const int lx = fast_div(rest, a.div_upx);     // x * 3 + list
+  const int ul = rest - lx * upx;
+  const int x = lx / 3, list = lx - 3 * x;
+  return (((list * units + x * upx + ul) << a.region_bits) | rg);
 }
 
 // pref[i] = tasks of the regions at positions [r0, i) (region_at order) for
 // i in [r0, r1]; nlong / nshort / offs receive those regions' counts, by
 // position.  All threads of the block take part.
 template <int W>
-__device__ void task_prefix(const int4* kinds, int r0, int r1, int units, int regions, int* pref,
+__device__ void task_prefix(const ChunkArgs& a, int r0, int r1, int* pref,
                             int* nlong, int* nshort, int* offs, int* wtot) {
   constexpr int NT = W * kWave;
   const int tid = threadIdx.x, wave = tid / kWave;
@@ -62,7 +63,7 @@ __device__ void task_prefix(const int4* kinds, int r0, int r1, int units, int re
   int local = 0;
   for (int j = 0; j < per; ++j) {
     if (beg + j < r1) {
-      const int4 kd = kinds[region_at(beg + j, units, regions)];
+      const int4 kd = a.kinds[region_at(beg + j, a)];
       nlong[beg + j] = kd.x;
       nshort[beg + j] = kd.y;
       offs[beg + j] = kd.z;
@@ -180,7 +181,7 @@ __device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, 
                                               int n, const float4* trow, int width4,
                                               float4 (&old)[R], float4 (&acc)[R]) {
   const int lane = lane_id();
-  const int b = u / a.H, hh = u - b * a.H;
+  const int b = fast_div(u, a.div_H), hh = u - b * a.H;
   const bool idw = a.mode == 0;
   const float* cf = a.coef + (int64_t)h * a.U * a.P + (int64_t)u * a.P;
   for (int base = 0; base < n; base += kWave) {
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(W * kWave, kd_waves_per_simd<W>()) void kd_update(C
     t_first = blockIdx.x / kXcds;
     t_step = gridDim.x / kXcds;
   }
-  task_prefix<W>(a.kinds, r_lo, r_hi, a.U, a.regions, pref, nlong, nshort, offs, wtot);
+  task_prefix<W>(a, r_lo, r_hi, pref, nlong, nshort, offs, wtot);
   const int t_end = pref[r_hi];
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -268,10 +269,10 @@ __global__ __launch_bounds__(W * kWave, kd_waves_per_simd<W>()) void kd_update(C
   for (int task = t_first; task < t_end; task += t_step) {
     const int lo = find_region(pref, r_lo, r_hi, task);   // region (position) holding this task
     const int j = task - pref[lo];
-    const int lu = region_at(lo, a.U, a.regions) / a.regions;   // list * U + unit
-    const int list = lu / a.U;
+    const int lu = region_at(lo, a) >> a.region_bits;   // list * U + unit
+    const int list = fast_div(lu, a.div_U);
     const int u = lu - list * a.U;
-    const int b = u / a.H, hh = u - b * a.H;
+    const int b = fast_div(u, a.div_H), hh = u - b * a.H;
     const int64_t lbase = (int64_t)lu * P;
     const int nl = nlong[lo];
     const bool is_long = j < nl;
@@ -383,7 +384,8 @@ hipError_t launch_kd_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* t
 
 }  // namespace
 
-hipError_t launch_kd(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
+hipError_t launch_kd(const ChunkArgs& args, hipStream_t s, const LaunchTiming* tm) {
+  const ChunkArgs a = with_divisors(args);
   const int r = (a.pw / 4 + 63) / 64;
   // (float4 per lane per row, waves, rows in flight): the largest of each
   // that keeps two workgroups per compute unit without register spills
