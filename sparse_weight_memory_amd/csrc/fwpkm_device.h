@@ -40,8 +40,13 @@ inline FastDiv make_fastdiv(int d) {
   return FastDiv{(unsigned int)m, l};
 }
 
-__device__ __forceinline__ int fast_div(int x, FastDiv f) {
-  return (int)((__umulhi((unsigned int)x, f.m) + (unsigned int)x) >> f.l);
+__host__ __device__ __forceinline__ int fast_div(int x, FastDiv f) {
+#if __HIP_DEVICE_COMPILE__
+  const unsigned int hi = __umulhi((unsigned int)x, f.m);
+#else
+  const unsigned int hi = (unsigned int)(((unsigned long long)(unsigned int)x * f.m) >> 32);
+#endif
+  return (int)((hi + (unsigned int)x) >> f.l);
 }
 
 struct ChunkArgs {
