@@ -104,6 +104,13 @@ EDGE = [
     # 256-key blocks with a ragged last block and token tile
     ("direct-staging-blk128", 4, 1, 256, 256, 256, 256, 64, 8, "idw"),
     ("direct-staging-ragged-dot", 8, 1, 256, 200, 300, 128, 32, 8, "dot"),
+    # work-item decompositions by divisors that are not powers of two: three
+    # heads over 24 units (3 units per XCD, ragged token tiles and read
+    # workgroups), two key blocks of a 100-key half, and five heads over 5
+    # units (the plain unit order)
+    ("heads3-units24", 8, 3, 64, 37, 64, 16, 32, 4, "idw"),
+    ("heads3-two-blocks-dot", 8, 3, 64, 50, 100, 8, 16, 8, "dot"),
+    ("heads5-units5", 1, 5, 80, 70, 40, 8, 24, 6, "idw"),
 ]
 
 
