@@ -55,24 +55,26 @@ namespace fwpkm {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Ascending bitonic sort of one 32-bit word per lane over the whole wave.
+// Ascending bitonic sort of one 32-bit word per lane within every aligned
+// group of GROUP lanes (32 or the whole wave).
 template <int S>
 __device__ __forceinline__ void cas_u32(unsigned int& x, bool ascending) {
   const unsigned int o = (unsigned int)xor_lane<S>((int)x);
   const bool keep_min = ((lane_id() & S) == 0) == ascending;
   x = keep_min ? min(x, o) : max(x, o);
 }
-template <int SIZE, int S>
+template <int SIZE, int GROUP, int S>
 __device__ __forceinline__ void u32_merge_steps(unsigned int& x) {
-  cas_u32<S>(x, SIZE == kWave || (lane_id() & SIZE) == 0);
-  if constexpr (S > 1) u32_merge_steps<SIZE, S / 2>(x);
+  cas_u32<S>(x, SIZE == GROUP || (lane_id() & SIZE) == 0);
+  if constexpr (S > 1) u32_merge_steps<SIZE, GROUP, S / 2>(x);
 }
-template <int SIZE>
+template <int SIZE, int GROUP>
 __device__ __forceinline__ void u32_stages(unsigned int& x) {
-  if constexpr (SIZE > 2) u32_stages<SIZE / 2>(x);
-  u32_merge_steps<SIZE, SIZE / 2>(x);
+  if constexpr (SIZE > 2) u32_stages<SIZE / 2, GROUP>(x);
+  u32_merge_steps<SIZE, GROUP, SIZE / 2>(x);
 }
-__device__ __forceinline__ void sort_u32(unsigned int& x) { u32_stages<kWave>(x); }
+template <int GROUP = kWave>
+__device__ __forceinline__ void sort_u32(unsigned int& x) { u32_stages<GROUP, GROUP>(x); }
 
 constexpr int kScoreWaves = 16;
 constexpr int kMaxBlk = 256;       // largest key block
@@ -190,6 +192,9 @@ __device__ __forceinline__ void wait_vm_at_most() {
 // shares tile d_h in whole chunks, and no ring padding is multiplied), so
 // the staging loads need no mask.  kDma: stage keys with direct LDS loads
 // (see dma_swizzle); kPrefetch is then the number of LDS slots per wave.
+// Largest k whose selection takes two tokens per wave (32 lanes each).
+constexpr int kPairMaxK = 16;
+
 template <int kDimChunk, int kPrefetch, bool kFull, bool kDma>
 __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a) {
   static_assert(!kDma || kFull, "direct LDS staging cannot mask");
@@ -557,87 +562,145 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     }
   }
 
-  // ---- per token (wave w <-> token w): the k best of the block
-  const int tw = t0 + wave;
-  if (tw >= a.T) return;
+  // ---- the k best of the block, per token
   const int k = a.k;
-  const float* srow = sc + wave * ppitch;
-  auto cand = [&](int c) -> skey {
-    const int gkey = kb * blk + c;
-    return gkey < a.n ? pack_key(srow[c], gkey) : kEmptyKey;
+  // one token on the whole wave: a filter on the lanes' best values and a
+  // sort of the survivors, or the general path (mass ties, 64-key blocks)
+  auto select_token = [&](int tl) __attribute__((always_inline)) {
+    const int tw = t0 + tl;
+    const float* srow = sc + tl * ppitch;
+    auto cand = [&](int c) -> skey {
+      const int gkey = kb * blk + c;
+      return gkey < a.n ? pack_key(srow[c], gkey) : kEmptyKey;
+    };
+    skey x;
+    bool picked = false;
+    if (blk > kWave) {
+      // Each lane's best candidate value bounds the answer: the k-th smallest
+      // of those 64 values (compared on the value bits alone, a 32-bit sort)
+      // is >= the k-th best key, so only candidates whose value bits do not
+      // exceed it can be among the k best.  Those few get the exact 64-bit
+      // sort.  When more than a wave's worth pass (mass ties, or fewer than k
+      // real keys in the block) the general path below runs instead.
+      constexpr int kR = kMaxBlk / kWave;
+      const int nr = blk >> 6;
+      skey cr[kR];
+      unsigned int lo_hi = 0xFFFFFFFFu;
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        cr[r] = r < nr ? cand(lane + r * kWave) : kEmptyKey;
+        lo_hi = min(lo_hi, (unsigned int)(cr[r] >> 32));
+      }
+      sort_u32(lo_hi);
+      const unsigned int th = (unsigned int)__builtin_amdgcn_readlane((int)lo_hi, k - 1);
+      skey* sv = surv + tl * blk;
+      int n = 0;
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const bool pass = r < nr && (unsigned int)(cr[r] >> 32) <= th;
+        const unsigned long long m = __ballot(pass);
+        if (pass) sv[n + __popcll(m & ((1ull << lane) - 1ull))] = cr[r];
+        n += __popcll(m);
+      }
+      if (n <= kWave) {
+        x = lane < n ? sv[lane] : kEmptyKey;
+        if (n <= 8) sort_keys<8>(x);
+        else if (n <= 16) sort_keys<16>(x);
+        else if (n <= 32) sort_keys<32>(x);
+        else sort_keys<64>(x);
+        picked = true;
+      }
+    }
+    if (!picked) {
+    x = cand(lane);
+    sort_keys<64>(x);                               // the first 64, best first
+    if (blk > kWave) {
+      const skey th = readlane_k(x, k - 1);         // k-th best so far
+      skey* sv = surv + tl * blk;
+      int nsurv = 0;
+      for (int c0 = kWave; c0 < blk; c0 += kWave) {
+        const skey cx = cand(c0 + lane);
+        const bool pass = cx < th;
+        const unsigned long long m = __ballot(pass);
+        if (pass) sv[nsurv + __popcll(m & ((1ull << lane) - 1ull))] = cx;
+        nsurv += __popcll(m);
+      }
+      // the k best stay in lanes 0..k-1; survivors fill lanes k.. in batches,
+      // and only the lane group that holds them is sorted
+      const int fresh = kWave - k;
+      for (int pos = 0; pos < nsurv; pos += fresh) {
+        if (lane >= k) {
+          const int c = pos + lane - k;
+          x = c < nsurv ? sv[c] : kEmptyKey;
+        }
+        const int cnt = k + min(fresh, nsurv - pos);
+        if (cnt <= 16) sort_keys<16>(x);
+        else if (cnt <= 32) sort_keys<32>(x);
+        else sort_keys<64>(x);
+      }
+    }
+    }
+    if (lane < k) {
+      const int64_t base = ((((int64_t)u * a.T + tw) * 2 + h) * a.nblk + kb) * k;
+      a.half_o[base + lane] = key_value(x);
+      a.half_i[base + lane] = key_index(x);
+    }
   };
-  skey x;
-  bool picked = false;
-  if (blk > kWave) {
-    // Each lane's best candidate value bounds the answer: the k-th smallest
-    // of those 64 values (compared on the value bits alone, a 32-bit sort)
-    // is >= the k-th best key, so only candidates whose value bits do not
-    // exceed it can be among the k best.  Those few get the exact 64-bit
-    // sort.  When more than a wave's worth pass (mass ties, or fewer than k
-    // real keys in the block) the general path below runs instead.
-    constexpr int kR = kMaxBlk / kWave;
-    const int nr = blk >> 6;
-    skey cr[kR];
+
+  if (blk > kWave && k <= kPairMaxK) {
+    // Blocks of 128 or 256 keys: waves 0..7 take two tokens each, lanes
+    // 32 g + l serving token 2 w + g, so half the waves sort half as many
+    // lanes (the selection's cross-lane work shares each SIMD among fewer
+    // waves).  Same bound as the one-token filter: the k-th smallest of the
+    // 32 lanes' best value bits is >= the value bits of the k-th best key,
+    // so every one of the k best passes; the survivors get the exact sort.
+    if (wave >= kTokTile / 2 || t0 + 2 * wave >= a.T) return;   // wave-uniform
+    const int g = lane >> 5, l = lane & 31;
+    const int tl = 2 * wave + g;
+    const float* srow = sc + tl * ppitch;
+    constexpr int kR2 = kMaxBlk / 32;
+    const int nr = blk >> 5;
+    skey cr[kR2];
     unsigned int lo_hi = 0xFFFFFFFFu;
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      cr[r] = r < nr ? cand(lane + r * kWave) : kEmptyKey;
+    for (int r = 0; r < kR2; ++r) {
+      const int c = l + 32 * r;
+      const int gkey = kb * blk + c;
+      cr[r] = (r < nr && gkey < a.n) ? pack_key(srow[c], gkey) : kEmptyKey;
       lo_hi = min(lo_hi, (unsigned int)(cr[r] >> 32));
     }
-    sort_u32(lo_hi);
-    const unsigned int th = (unsigned int)__builtin_amdgcn_readlane((int)lo_hi, k - 1);
-    skey* sv = surv + wave * blk;
-    int n = 0;
+    sort_u32<32>(lo_hi);
+    const unsigned int th0 = (unsigned int)__builtin_amdgcn_readlane((int)lo_hi, k - 1);
+    const unsigned int th1 = (unsigned int)__builtin_amdgcn_readlane((int)lo_hi, 32 + k - 1);
+    const unsigned int th = g ? th1 : th0;
+    skey* sv = surv + tl * blk;
+    const unsigned long long half_mask = g ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull;
+    int n = 0;   // survivors of this lane's token
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
+    for (int r = 0; r < kR2; ++r) {
       const bool pass = r < nr && (unsigned int)(cr[r] >> 32) <= th;
-      const unsigned long long m = __ballot(pass);
+      const unsigned long long m = __ballot(pass) & half_mask;
       if (pass) sv[n + __popcll(m & ((1ull << lane) - 1ull))] = cr[r];
       n += __popcll(m);
     }
-    if (n <= kWave) {
-      x = lane < n ? sv[lane] : kEmptyKey;
-      if (n <= 8) sort_keys<8>(x);
-      else if (n <= 16) sort_keys<16>(x);
-      else if (n <= 32) sort_keys<32>(x);
-      else sort_keys<64>(x);
-      picked = true;
+    const int n0 = __builtin_amdgcn_readlane(n, 0), n1 = __builtin_amdgcn_readlane(n, 32);
+    const int nmax = max(n0, n1);
+    skey x = l < n ? sv[l] : kEmptyKey;
+    if (nmax <= 8) sort_keys<8>(x);
+    else if (nmax <= 16) sort_keys<16>(x);
+    else sort_keys<32>(x);
+    // a token with more than 32 survivors takes the whole-wave path instead
+    if (l < k && t0 + tl < a.T && n <= 32) {
+      const int64_t base = ((((int64_t)u * a.T + t0 + tl) * 2 + h) * a.nblk + kb) * k;
+      a.half_o[base + l] = key_value(x);
+      a.half_i[base + l] = key_index(x);
     }
+    if (n0 > 32 && t0 + 2 * wave < a.T) select_token(2 * wave);
+    if (n1 > 32 && t0 + 2 * wave + 1 < a.T) select_token(2 * wave + 1);
+    return;
   }
-  if (!picked) {
-  x = cand(lane);
-  sort_keys<64>(x);                               // the first 64, best first
-  if (blk > kWave) {
-    const skey th = readlane_k(x, k - 1);         // k-th best so far
-    skey* sv = surv + wave * blk;
-    int nsurv = 0;
-    for (int c0 = kWave; c0 < blk; c0 += kWave) {
-      const skey cx = cand(c0 + lane);
-      const bool pass = cx < th;
-      const unsigned long long m = __ballot(pass);
-      if (pass) sv[nsurv + __popcll(m & ((1ull << lane) - 1ull))] = cx;
-      nsurv += __popcll(m);
-    }
-    // the k best stay in lanes 0..k-1; survivors fill lanes k.. in batches,
-    // and only the lane group that holds them is sorted
-    const int fresh = kWave - k;
-    for (int pos = 0; pos < nsurv; pos += fresh) {
-      if (lane >= k) {
-        const int c = pos + lane - k;
-        x = c < nsurv ? sv[c] : kEmptyKey;
-      }
-      const int cnt = k + min(fresh, nsurv - pos);
-      if (cnt <= 16) sort_keys<16>(x);
-      else if (cnt <= 32) sort_keys<32>(x);
-      else sort_keys<64>(x);
-    }
-  }
-  }
-  if (lane < k) {
-    const int64_t base = ((((int64_t)u * a.T + tw) * 2 + h) * a.nblk + kb) * k;
-    a.half_o[base + lane] = key_value(x);
-    a.half_i[base + lane] = key_index(x);
-  }
+  if (t0 + wave >= a.T) return;
+  select_token(wave);
 }
 
 int score_key_block(int units, int tokens, int n) {
