@@ -125,6 +125,24 @@ def test_edge_shapes(case):
         st, _, _ = compare_chunk(mem, st, q, y, lr, label=f"{label} step{c}")
 
 
+@pytest.mark.parametrize("k", [8, 16])
+def test_two_token_selection_odd_tail_and_mass_ties(k):
+    """256-key blocks select two tokens per wave.  249 tokens leave a last
+    tile of 9, so one wave serves a real token and one past the chunk.  With
+    the first sub-key table made of 4 distinct rows repeated 64 times, each
+    lane's candidates are copies of one row, the best values tie across 64
+    keys, and a token's survivors (64 or 128) overflow the 32 lanes: it takes
+    the whole-wave path, ties resolved by index on both sides."""
+    need_gpu()
+    B, H, T, n, half, dv = 8, 1, 249, 256, 16, 16
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=256, num_heads=H, max_batch=B)
+    st, q, y = _random_case(4242 + k, B, H, T, n, half, dv)
+    compare_chunk(mem, st, q, y, 1.0, units=[0, 7], label=f"odd tail k{k}")
+    st, q, y = _random_case(4343 + k, B, H, T, n, half, dv)
+    st["k1"] = np.ascontiguousarray(np.tile(st["k1"][:, :4], (1, n // 4, 1)))
+    compare_chunk(mem, st, q, y, 1.0, units=[0, 3, 7], label=f"mass ties k{k}")
+
+
 @pytest.mark.parametrize("C", [32, 33])
 def test_grouping_at_the_rank_sort_limit(C):
     """48 units leave one hash region per list, so every unit's V list holds
