@@ -203,6 +203,13 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   constexpr int kLanesPerRow = Staging<kDimChunk, kPrefetch>::kLanesPerRow;
   constexpr int kRowsPerLoad = Staging<kDimChunk, kPrefetch>::kRowsPerLoad;
   extern __shared__ float smem[];
+  // every launch argument the prologue needs, as scalar operands of an empty
+  // statement: they are fetched in one batch with one wait (left to itself
+  // the compiler fetches them in three dependent rounds)
+  asm volatile("" :: "s"(a.T), "s"(a.U), "s"(a.nblk), "s"(a.ka_ntt), "s"(a.H), "s"(a.half), "s"(a.key_block),
+               "s"(a.ka_nkt_log2), "s"(a.ka_share), "s"(a.n), "s"(a.ka_div_ntt.m), "s"(a.ka_div_ntt.l),
+               "s"(a.ka_div_nblk.m), "s"(a.ka_div_nblk.l), "s"(a.div_H.m), "s"(a.div_H.l), "s"(a.k1), "s"(a.k2),
+               "s"(a.q), "s"(a.stride_k), "s"(a.dqk));
   const int half = a.half;
   // launch geometry from the host (shifts and multiply-shift divisions:
   // the prologue's scalar work is issued once per wave of the workgroup)

@@ -41,6 +41,11 @@ namespace fwpkm {
 template <int KMAX, int VR, bool WRITE>
 __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   constexpr bool KEEP = KMAX * VR <= 32;
+  // the launch arguments the first loads need, fetched in one batch with one
+  // wait (left to itself the compiler fetches them in dependent rounds)
+  asm volatile("" :: "s"(a.T), "s"(a.U), "s"(a.div_nbx.m), "s"(a.div_nbx.l), "s"(a.k), "s"(a.n),
+               "s"(a.div_H.m), "s"(a.div_H.l), "s"(a.H), "s"(a.nblk), "s"(a.half_i), "s"(a.half_o),
+               "s"(a.qnorm), "s"(a.tw), "s"(a.y), "s"(a.dv), "s"(a.mode));
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   const int nbx = (a.T + 3) >> 2;                      // 4 tokens per workgroup
