@@ -187,6 +187,8 @@ class UnitChunkResult:
     near_tie: np.ndarray         # [C] bool
     overridden: np.ndarray       # [C] bool: selection taken from the caller
     updates: Optional[dict]      # {"k1"|"k2"|"v": (rows, new fp32 rows)} or None
+    half_values: Optional[tuple] = None   # R2 values (d1 [C, n], d2 [C, n]) or dot scores
+    mode: str = IDW
 
 
 def _weighted_rows(w: np.ndarray, vsel: np.ndarray) -> np.ndarray:
@@ -228,6 +230,11 @@ def read_unit(k1, k2, v, q, k, eps, mode=IDW, override: Optional[Dict[int, Seque
     if override:
         for t, chosen in override.items():
             chosen = np.asarray(sorted(int(s) for s in chosen), dtype=np.int64)
+            # an imposed selection is still k distinct slots of the memory
+            if (chosen.size != k or np.unique(chosen).size != k
+                    or chosen.min() < 0 or chosen.max() >= N):
+                raise ValueError(f"override of token {t} is not {k} distinct slots in [0, {N}): "
+                                 f"{chosen.tolist()}")
             a, b = chosen // n, chosen % n
             cv = v1[t, a] + v2[t, b]
             order = np.lexsort((chosen, _order_key(cv, mode)))
@@ -236,7 +243,8 @@ def read_unit(k1, k2, v, q, k, eps, mode=IDW, override: Optional[Dict[int, Seque
             overridden[t] = True
     w = score_weights(vals, eps, mode)
     out = _weighted_rows(w, np.asarray(v, np.float64)[slots])
-    return out, slots, vals, w, dict(value_k1=vk1, near_tie=tie, overridden=overridden)
+    return out, slots, vals, w, dict(value_k1=vk1, near_tie=tie, overridden=overridden,
+                                     half_values=(v1, v2))
 
 
 # -------------------------------------------------------------------- write
@@ -344,7 +352,8 @@ def unit_chunk(k1, k2, v, q, y, lr, k, eps=1e-3, mode=IDW, override=None,
     out, slots, vals, w, ex = read_unit(k1, k2, v, q, k, eps, mode, override)
     res = UnitChunkResult(retrieved=out, slots=slots, values=vals, weights=w,
                           value_k1=ex["value_k1"], near_tie=ex["near_tie"],
-                          overridden=ex["overridden"], updates=None)
+                          overridden=ex["overridden"], updates=None,
+                          half_values=ex["half_values"], mode=mode)
     if lr == 0.0:
         return res
     grads = chunk_gradients(k1, k2, v, q, y, slots, vals, w, eps, mode, token_weights)

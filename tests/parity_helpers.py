@@ -84,14 +84,82 @@ def oracle_units(state, q, y, lr, k, eps, mode, units, H, overrides=None, tw=Non
     return rets, new, results
 
 
-def selection_overrides(results, gpu_slots, H, units):
+def _tie_window(x, y):
+    """Z17's near-tie width around two values (relative 1e-6, floor 1)."""
+    return O.NEAR_TIE_REL * max(abs(x), abs(y), 1.0)
+
+
+# Exact-tie enumeration gives up beyond this many candidate slots per token
+# (then only the symmetric difference is checked for exact ties).
+_MAX_WINDOW_SLOTS = 1 << 20
+
+
+def validate_adopted_selection(r, t, chosen, n):
+    """Check that `chosen`, a selection the GPU made for token t where it
+    differs from the oracle's, is one an fp32 ranking may legitimately make.
+
+    r is the oracle's (non-overridden) UnitChunkResult of the unit.  Raises
+    AssertionError unless
+      * chosen holds k distinct slots in [0, n*n);
+      * every slot in the symmetric difference with the oracle's set has an
+        oracle value within the near-tie window of the k-th best value (a
+        slot the GPU dropped was not clearly better, one it took was not
+        clearly worse);
+      * where float64 values tie exactly, the lower slot was taken: no chosen
+        slot has a left-out slot of exactly its value and a lower index
+        (ties by lower slot, as both sides order candidates).
+    """
+    k = r.slots.shape[1]
+    N = n * n
+    chosen = [int(s) for s in chosen]
+    assert len(chosen) == k and len(set(chosen)) == k, (
+        f"token {t}: GPU selection {chosen} is not {k} distinct slots")
+    assert all(0 <= s < N for s in chosen), f"token {t}: GPU selection {chosen} leaves [0, {N})"
+    v1, v2 = r.half_values
+    sign = 1.0 if r.mode == O.IDW else -1.0          # order key: ascending is best first
+
+    def value(s):
+        return float(v1[t, s // n] + v2[t, s % n])
+
+    d_k = float(r.values[t, k - 1])                  # the oracle's k-th best value
+    mine, theirs = set(chosen), set(int(s) for s in r.slots[t])
+    for s in sorted(mine ^ theirs):
+        d = value(s)
+        assert abs(d - d_k) <= _tie_window(d, d_k), (
+            f"token {t}: slot {s} ({'taken' if s in mine else 'dropped'} by the GPU) has value "
+            f"{d!r}, outside the near-tie window of the k-th best {d_k!r}")
+    # slots whose value could lie within the window: per half, the sub-keys
+    # that can still reach it with the other half's best value
+    o1, o2 = sign * v1[t], sign * v2[t]
+    lim = sign * d_k + _tie_window(d_k, d_k) * 1.000001
+    A = np.flatnonzero(o1 + o2.min() <= lim)
+    B = np.flatnonzero(o2 + o1.min() <= lim)
+    if A.size * B.size <= _MAX_WINDOW_SLOTS:
+        cand = (A[:, None] * n + B[None, :]).reshape(-1)
+        cval = (v1[t, A][:, None] + v2[t, B][None, :]).reshape(-1)
+    else:
+        cand = np.asarray(sorted(mine ^ theirs), dtype=np.int64)
+        cval = np.asarray([value(s) for s in cand])
+    left_out = ~np.isin(cand, np.asarray(chosen))
+    for s in chosen:
+        d = value(s)
+        lower = cand[left_out & (cval == d) & (cand < s)]
+        assert lower.size == 0, (
+            f"token {t}: GPU took slot {s} over slot {int(lower[0])} of exactly the same value "
+            f"{d!r} (ties go to the lower slot)")
+
+
+def selection_overrides(results, gpu_slots, H, units, n=None):
     """Compare slot sets; returns ({u: {t: gpu set}}, near-tie count).
 
-    Fails if a set differs where the oracle sees no near-tie."""
+    A set may differ from the oracle's only at a near-tie (k-th and (k+1)-th
+    best within 1e-6 relative), and then only as validate_adopted_selection
+    allows; the oracle then adopts the GPU's set for that token."""
     overrides, ties = {}, 0
     for u in units:
         b, h = divmod(u, H)
         r = results[u]
+        nn = n if n is not None else r.half_values[0].shape[1]
         g = gpu_slots[b, :, h]
         for t in range(g.shape[0]):
             gs = sorted(int(s) for s in g[t])
@@ -100,6 +168,7 @@ def selection_overrides(results, gpu_slots, H, units):
                 assert r.near_tie[t], (
                     f"unit {u} token {t}: GPU slots {gs} != oracle {os_} without a near-tie "
                     f"(k-th {r.values[t, -1]!r}, (k+1)-th {r.value_k1[t]!r})")
+                validate_adopted_selection(r, t, gs, nn)
                 overrides.setdefault(u, {})[t] = gs
                 ties += 1
     return overrides, ties

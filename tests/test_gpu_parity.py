@@ -132,7 +132,9 @@ def test_two_token_selection_odd_tail_and_mass_ties(k):
     the first sub-key table made of 4 distinct rows repeated 64 times, each
     lane's candidates are copies of one row, the best values tie across 64
     keys, and a token's survivors (64 or 128) overflow the 32 lanes: it takes
-    the whole-wave path, ties resolved by index on both sides."""
+    the whole-wave path.  Every token is then an exact float64 tie at the
+    k-th place, and the checker accepts only the lower-slot choice among
+    exactly tied candidates, so the path's selection is checked bit for bit."""
     need_gpu()
     B, H, T, n, half, dv = 8, 1, 249, 256, 16, 16
     mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=256, num_heads=H, max_batch=B)
