@@ -81,19 +81,48 @@ def _check_tensor(name, t, dtype=torch.float32):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _c_state(s: State, cfg: Config) -> _lib.CState:
-    per_k = cfg.num_heads * cfg.sqrt_slots * cfg.half
-    per_v = cfg.num_heads * cfg.num_slots * cfg.dim_v
+def state_strides(shapes, cfg: Config, batch: int):
+    """Element strides between sequences of a state whose tables have the
+    given shapes (k1, k2, v), after checking that they hold what a call with
+    `batch` sequences reads and writes:
+
+      per-sequence  k1, k2 [B', H, n, d_h], v [B', H, N, d_v] with B' >= batch
+                    (the same B' in all three) -> one sequence's tables apart;
+      shared        k1, k2 [H, n, d_h], v [H, N, d_v] -> stride 0.
+
+    Raises ValueError otherwise: the C library cannot see allocation sizes,
+    so this is what keeps it inside the caller's tensors."""
+    H, n, dh, N, dv = cfg.num_heads, cfg.sqrt_slots, cfg.half, cfg.num_slots, cfg.dim_v
+    k1, k2, v = (tuple(int(d) for d in s) for s in shapes)
+    if len(k1) == 3:
+        if k1 != (H, n, dh) or k2 != (H, n, dh) or v != (H, N, dv):
+            raise ValueError(f"shared state tables must be k1, k2 [{H}, {n}, {dh}] and "
+                             f"v [{H}, {N}, {dv}]; got {k1}, {k2}, {v}")
+        return 0, 0
+    if len(k1) != 4 or k1[1:] != (H, n, dh) or k2[1:] != (H, n, dh) or len(v) != 4 or v[1:] != (H, N, dv):
+        raise ValueError(f"per-sequence state tables must be k1, k2 [B, {H}, {n}, {dh}] and "
+                         f"v [B, {H}, {N}, {dv}]; got {k1}, {k2}, {v}")
+    if not (k1[0] == k2[0] == v[0]):
+        raise ValueError(f"state tables hold different numbers of sequences: {k1[0]}, {k2[0]}, {v[0]}")
+    if k1[0] < batch:
+        raise ValueError(f"state tables hold {k1[0]} sequence(s), the call carries {batch}")
+    return H * n * dh, H * N * dv
+
+
+def _c_state(s: State, cfg: Config, batch: int) -> _lib.CState:
     for name, t in (("k1", s.k1), ("k2", s.k2), ("v", s.v)):
         _check_tensor(f"state.{name}", t)
-    shared = s.k1.dim() == 3
-    if shared:
-        stride_k = stride_v = 0
-    else:
-        stride_k, stride_v = per_k, per_v
-    if s.k1.numel() % per_k or s.k2.numel() != s.k1.numel() or s.v.numel() % per_v:
-        raise ValueError("state tables do not match the configuration")
+    stride_k, stride_v = state_strides((s.k1.shape, s.k2.shape, s.v.shape), cfg, batch)
     return _lib.CState(s.k1.data_ptr(), s.k2.data_ptr(), s.v.data_ptr(), stride_k, stride_v)
+
+
+def check_rows(name: str, shape, batch: int, rows: int, heads: int, width: int) -> None:
+    """`name` must be [batch, rows, heads, width] (or [batch, rows, width]
+    when heads == 1): a caller-supplied output the library writes in full."""
+    shape = tuple(int(d) for d in shape)
+    ok = shape == (batch, rows, heads, width) or (heads == 1 and shape == (batch, rows, width))
+    if not ok:
+        raise ValueError(f"{name} must be [{batch}, {rows}, {heads}, {width}], got {list(shape)}")
 
 
 def empty_state(cfg: Config, batch: int, device="cuda") -> State:
@@ -169,12 +198,13 @@ class Memory:
             raise ValueError("targets must be [B, T, H, d_v]")
         if next is None:
             next = empty_state(cfg, B, queries.device)
-        c_past = _c_state(past, cfg)
-        c_next = _c_state(next, cfg)
+        c_past = _c_state(past, cfg, B)
+        c_next = _c_state(next, cfg, B)
         if retrieved is None:
             retrieved = torch.empty((B, T, cfg.num_heads, cfg.dim_v), device=queries.device)
         else:
             _check_tensor("retrieved", retrieved)
+            check_rows("retrieved", retrieved.shape, B, T, cfg.num_heads, cfg.dim_v)
         slots = weights = None
         if return_selection:
             slots = torch.empty((B, T, cfg.num_heads, cfg.topk), device=queries.device, dtype=torch.int32)
@@ -241,8 +271,8 @@ class Memory:
                 raise ValueError(f"b_gate must have {H} entries")
         if next is None:
             next = empty_state(cfg, B, x.device)
-        c_past = _c_state(past, cfg)
-        c_next = _c_state(next, cfg)
+        c_past = _c_state(past, cfg, B)
+        c_next = _c_state(next, cfg, B)
         if out is None:
             out = torch.empty((B, S, D), device=x.device)
         else:
