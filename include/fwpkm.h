@@ -183,6 +183,38 @@ int fwpkm_forward_chunk_weighted(fwpkm_handle* h,
                                  float* retrieved, int32_t* out_slots, float* out_weights,
                                  hipStream_t stream);
 
+/* ---- without device allocation --------------------------------------------
+ * For callers that cannot allocate device memory: code being captured into a
+ * HIP graph, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * fwpkm_forward_chunk with the same arguments, rules and results (the same
+ * kernels run), except where the workspace lives: a fixed array of
+ * FWPKM_NOALLOC_SCRATCH_BYTES bytes in the library's device data instead of
+ * the handle's allocation.  The call never calls hipMalloc, hipFree or any
+ * other allocating routine, and neither allocates nor touches the handle's
+ * own workspace (the handle supplies the configuration only).
+ *
+ *   - Limit: the call's workspace, fwpkm_workspace_bytes of the
+ *     configuration with max_batch = batch and chunk_size = tokens, must not
+ *     exceed FWPKM_NOALLOC_SCRATCH_BYTES, else FWPKM_ERR_UNSUPPORTED (checked
+ *     with the other arguments, before anything is enqueued).
+ *   - Each GPU holds its own copy of the array from library load until the
+ *     process ends.  The first call on a device looks its address up (a
+ *     symbol query, not an allocation) with that device current.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents: calls that overlap in time on one GPU (other streams,
+ *     threads or handles) race and give undefined results; order them on one
+ *     stream.  Nothing in the array needs to start at zero: every call
+ *     writes each part before reading it.
+ *   - Per-kernel timing (fwpkm_profile_enable) does not record these calls. */
+#define FWPKM_NOALLOC_SCRATCH_BYTES (64u << 20)
+int fwpkm_forward_chunk_noalloc(fwpkm_handle* h,
+                                const float* queries, const float* targets,
+                                int32_t batch, int32_t tokens, float lr,
+                                const fwpkm_state* past_state, const fwpkm_state* next_state,
+                                float* retrieved, int32_t* out_slots, float* out_weights,
+                                hipStream_t stream);
+
 /* ---- sequence-level layer ------------------------------------------------
  * Whole token sequences through the memory [PyPI page
  * "fast-weight-product-key-memory", Usage: model-width tokens in, memories

@@ -27,6 +27,7 @@ MAX_SQRT_SLOTS = 4096
 MAX_HALF = 1024
 MAX_DIM_V = 2048
 MAX_CHUNK = 1024
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every symbol the header declares
 EXPORTS = (
@@ -34,6 +35,7 @@ EXPORTS = (
     "fwpkm_workspace_bytes",
     "fwpkm_forward_chunk",
     "fwpkm_forward_chunk_weighted",
+    "fwpkm_forward_chunk_noalloc",
     "fwpkm_sequence_workspace_bytes",
     "fwpkm_forward_sequence",
     "fwpkm_destroy",
@@ -113,6 +115,8 @@ def load() -> ctypes.CDLL:
         ctypes.c_void_p,                       # stream
     ]
     lib.fwpkm_forward_chunk_weighted.restype = ctypes.c_int
+    lib.fwpkm_forward_chunk_noalloc.argtypes = lib.fwpkm_forward_chunk.argtypes
+    lib.fwpkm_forward_chunk_noalloc.restype = ctypes.c_int
     lib.fwpkm_sequence_workspace_bytes.argtypes = [ctypes.POINTER(CConfig), ctypes.c_int32,
                                                    ctypes.c_int32]
     lib.fwpkm_sequence_workspace_bytes.restype = ctypes.c_size_t

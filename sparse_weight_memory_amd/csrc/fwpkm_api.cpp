@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -129,6 +130,40 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 }  // namespace
 
+// The workspace of fwpkm_forward_chunk_noalloc: a fixed array in the code
+// object's zero-initialised device data, so each GPU the library runs on
+// holds one copy from load until the process ends and no call allocates.
+// On the host the name is a stand-in, not a device address: host code uses
+// only the address hipGetSymbolAddress reports for the current device.
+static __device__ __align__(256) unsigned char scratch[FWPKM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices] = {};   // device address of `scratch`, per device
+
+// Device address of `scratch` on device `dev` (the current device), looked
+// up once per device.
+int scratch_of_device(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FWPKM_ERR_UNSUPPORTED, "device %d: the fixed workspace serves devices 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(FWPKM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    }
+    g_scratch[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch[dev];
+  return FWPKM_OK;
+}
+
+}  // namespace
+
 struct fwpkm_handle {
   fwpkm_config cfg;
   int device = -1;
@@ -159,8 +194,8 @@ hipEvent_t take_event(fwpkm_handle* h) {
 // Run `fn(timing)`: with profiling on, `timing` carries a start/stop event
 // pair that the launch stamps (kernels: from the dispatch itself).
 template <typename F>
-hipError_t timed(fwpkm_handle* h, int kernel, F&& fn) {
-  if (!h->prof) return fn(nullptr);
+hipError_t timed(fwpkm_handle* h, bool on, int kernel, F&& fn) {
+  if (!on) return fn(nullptr);
   fwpkm::LaunchTiming tm;
   tm.beg = take_event(h);
   tm.end = take_event(h);
@@ -204,7 +239,8 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
                         const float* token_weights, int32_t batch, int32_t tokens, float lr,
                         const fwpkm_state* past, const fwpkm_state* next,
                         float* retrieved, int32_t* out_slots, float* out_weights,
-                        int64_t out_rows_b, hipStream_t stream, bool dry_run = false);
+                        int64_t out_rows_b, hipStream_t stream, bool dry_run = false,
+                        bool noalloc = false);
 
 int fwpkm_forward_chunk(fwpkm_handle* h, const float* queries, const float* targets,
                         int32_t batch, int32_t tokens, float lr,
@@ -222,6 +258,15 @@ int fwpkm_forward_chunk_weighted(fwpkm_handle* h, const float* queries, const fl
                                  hipStream_t stream) {
   return forward_impl(h, queries, targets, token_weights, batch, tokens, lr, past, next, retrieved,
                       out_slots, out_weights, 0, stream);
+}
+
+int fwpkm_forward_chunk_noalloc(fwpkm_handle* h, const float* queries, const float* targets,
+                                int32_t batch, int32_t tokens, float lr,
+                                const fwpkm_state* past, const fwpkm_state* next,
+                                float* retrieved, int32_t* out_slots, float* out_weights,
+                                hipStream_t stream) {
+  return forward_impl(h, queries, targets, nullptr, batch, tokens, lr, past, next, retrieved,
+                      out_slots, out_weights, 0, stream, /*dry_run=*/false, /*noalloc=*/true);
 }
 
 size_t fwpkm_sequence_workspace_bytes(const fwpkm_config* cfg, int32_t batch, int32_t seq) {
@@ -324,11 +369,11 @@ int fwpkm_forward_sequence(fwpkm_handle* h, const float* x, const float* w_in,
   sa.Nq = H * c.dim_qk;
   sa.Nv = H * c.dim_v;
   using fwpkm::LaunchTiming;
-  hipError_t e = timed(h, 8, [&](const LaunchTiming* tm) { return fwpkm::launch_kf_project(sa, stream, tm); });
+  hipError_t e = timed(h, h->prof, 8, [&](const LaunchTiming* tm) { return fwpkm::launch_kf_project(sa, stream, tm); });
   if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "projection kernel: %s", hipGetErrorString(e));
   for (int ci = 0; ci < nchunks; ++ci)
     if ((rc = chunk_call(ci, false)) != FWPKM_OK) return rc;
-  e = timed(h, 9, [&](const LaunchTiming* tm) { return fwpkm::launch_kf_gate(sa, stream, tm); });
+  e = timed(h, h->prof, 9, [&](const LaunchTiming* tm) { return fwpkm::launch_kf_gate(sa, stream, tm); });
   if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "gate kernel: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return FWPKM_OK;
@@ -386,11 +431,15 @@ int fwpkm_profile_read(fwpkm_handle* h, double* ms, int64_t* launches) {
 // out_rows_b: (token, head) rows between sequences in retrieved, out_slots
 // and out_weights (0: tokens * H, the packed layout of a chunk call).
 // dry_run: validate only, enqueue nothing.
+// noalloc: use the fixed array `scratch` as the workspace (never the
+// handle's, which is then neither allocated nor touched) and record no
+// timing events.
 static int forward_impl(fwpkm_handle* h, const float* queries, const float* targets,
                         const float* token_weights, int32_t batch, int32_t tokens, float lr,
                         const fwpkm_state* past, const fwpkm_state* next,
                         float* retrieved, int32_t* out_slots, float* out_weights,
-                        int64_t out_rows_b, hipStream_t stream, bool dry_run) {
+                        int64_t out_rows_b, hipStream_t stream, bool dry_run,
+                        bool noalloc) {
   // ---------------------------------------------------------- validation
   if (!h) return fail(FWPKM_ERR_INVALID_ARG, "handle is NULL");
   const fwpkm_config& c = h->cfg;
@@ -455,24 +504,40 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
   for (const Range& b : {nk1, nk2, nv})
     if (overlap(b, rq) || overlap(b, ry) || (rw.lo != rw.hi && overlap(b, rw)))
       return fail(FWPKM_ERR_ALIAS, "next_state overlaps queries, targets or token weights");
-  if (dry_run) return FWPKM_OK;
-
   // ---------------------------------------------------------- workspace
+  const int64_t U = (int64_t)batch * H;
+  const WsLayout L = ws_layout(c, U, tokens);
+  if (noalloc && L.total > (size_t)FWPKM_NOALLOC_SCRATCH_BYTES)
+    return fail(FWPKM_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of workspace, more than the %u-byte fixed array of "
+                "fwpkm_forward_chunk_noalloc (use fwpkm_forward_chunk)",
+                L.total, (unsigned)FWPKM_NOALLOC_SCRATCH_BYTES);
+  if (dry_run) return FWPKM_OK;
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  if (!h->ws) {
-    e = hipMalloc(&h->ws, h->ws_bytes);
-    if (e != hipSuccess) {
-      h->ws = nullptr;
-      (void)hipGetLastError();
-      if (e == hipErrorOutOfMemory) return fail(FWPKM_ERR_OOM, "workspace of %zu bytes: %s", h->ws_bytes, hipGetErrorString(e));
-      return fail(FWPKM_ERR_HIP, "hipMalloc: %s", hipGetErrorString(e));
+  char* ws = nullptr;
+  if (noalloc) {
+    const int rc = scratch_of_device(dev, &ws);
+    if (rc != FWPKM_OK) return rc;
+  } else {
+    if (!h->ws) {
+      e = hipMalloc(&h->ws, h->ws_bytes);
+      if (e != hipSuccess) {
+        h->ws = nullptr;
+        (void)hipGetLastError();
+        if (e == hipErrorOutOfMemory) return fail(FWPKM_ERR_OOM, "workspace of %zu bytes: %s", h->ws_bytes, hipGetErrorString(e));
+        return fail(FWPKM_ERR_HIP, "hipMalloc: %s", hipGetErrorString(e));
+      }
+      h->device = dev;
+    } else if (dev != h->device) {
+      return fail(FWPKM_ERR_INVALID_ARG, "handle's workspace lives on device %d, current device is %d", h->device, dev);
     }
-    h->device = dev;
-  } else if (dev != h->device) {
-    return fail(FWPKM_ERR_INVALID_ARG, "handle's workspace lives on device %d, current device is %d", h->device, dev);
+    ws = static_cast<char*>(h->ws);
   }
+  // per-kernel events only on the handle's own path (creating events is an
+  // allocation the fixed-workspace path must not make)
+  const bool prof = h->prof && !noalloc;
 
   // ---------------------------------------------------------- enqueue
   if (!inplace) {
@@ -480,7 +545,7 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
         {next->k1, past->k1, next->batch_stride_k, past->batch_stride_k, sk},
         {next->k2, past->k2, next->batch_stride_k, past->batch_stride_k, sk},
         {next->v, past->v, next->batch_stride_v, past->batch_stride_v, sv}};
-    e = timed(h, 4, [&](const fwpkm::LaunchTiming* tm) {
+    e = timed(h, prof, 4, [&](const fwpkm::LaunchTiming* tm) {
       hipError_t r = tm ? hipEventRecord(tm->beg, stream) : hipSuccess;
       for (const auto& cp : cps) {
         for (int b = 0; b < batch && r == hipSuccess; ++b) {
@@ -494,9 +559,6 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
     if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "state copy: %s", hipGetErrorString(e));
   }
 
-  const int64_t U = (int64_t)batch * H;
-  const WsLayout L = ws_layout(c, U, tokens);
-  char* ws = static_cast<char*>(h->ws);
   fwpkm::ChunkArgs a{};
   a.n = n;
   a.half = half;
@@ -551,24 +613,24 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
   a.addr_ell = reinterpret_cast<float*>(ws + L.addr_ell);
 
   using fwpkm::LaunchTiming;
-  if ((e = timed(h, 0, [&](const LaunchTiming* tm) { return fwpkm::launch_ka(a, stream, tm); })) != hipSuccess)
+  if ((e = timed(h, prof, 0, [&](const LaunchTiming* tm) { return fwpkm::launch_ka(a, stream, tm); })) != hipSuccess)
     return fail(FWPKM_ERR_HIP, "score kernel: %s", hipGetErrorString(e));
-  if ((e = timed(h, 1, [&](const LaunchTiming* tm) { return fwpkm::launch_kb(a, write, stream, tm); })) != hipSuccess)
+  if ((e = timed(h, prof, 1, [&](const LaunchTiming* tm) { return fwpkm::launch_kb(a, write, stream, tm); })) != hipSuccess)
     return fail(FWPKM_ERR_HIP, "read kernel: %s", hipGetErrorString(e));
   if (write) {
     // the addressing gradient is taken at the starting keys, before the update
     if (addr) {
-      if ((e = timed(h, 5, [&](const LaunchTiming* tm) { return fwpkm::launch_ke_stats(a, stream, tm); })) != hipSuccess)
+      if ((e = timed(h, prof, 5, [&](const LaunchTiming* tm) { return fwpkm::launch_ke_stats(a, stream, tm); })) != hipSuccess)
         return fail(FWPKM_ERR_HIP, "addressing statistics kernel: %s", hipGetErrorString(e));
-      if ((e = timed(h, 6, [&](const LaunchTiming* tm) { return fwpkm::launch_ke_grad(a, stream, tm); })) != hipSuccess)
+      if ((e = timed(h, prof, 6, [&](const LaunchTiming* tm) { return fwpkm::launch_ke_grad(a, stream, tm); })) != hipSuccess)
         return fail(FWPKM_ERR_HIP, "addressing gradient kernel: %s", hipGetErrorString(e));
     }
-    if ((e = timed(h, 2, [&](const LaunchTiming* tm) { return fwpkm::launch_kc(a, stream, tm); })) != hipSuccess)
+    if ((e = timed(h, prof, 2, [&](const LaunchTiming* tm) { return fwpkm::launch_kc(a, stream, tm); })) != hipSuccess)
       return fail(FWPKM_ERR_HIP, "sort kernel: %s", hipGetErrorString(e));
-    if ((e = timed(h, 3, [&](const LaunchTiming* tm) { return fwpkm::launch_kd(a, stream, tm); })) != hipSuccess)
+    if ((e = timed(h, prof, 3, [&](const LaunchTiming* tm) { return fwpkm::launch_kd(a, stream, tm); })) != hipSuccess)
       return fail(FWPKM_ERR_HIP, "update kernel: %s", hipGetErrorString(e));
     if (addr) {
-      if ((e = timed(h, 7, [&](const LaunchTiming* tm) { return fwpkm::launch_ke_apply(a, stream, tm); })) != hipSuccess)
+      if ((e = timed(h, prof, 7, [&](const LaunchTiming* tm) { return fwpkm::launch_ke_apply(a, stream, tm); })) != hipSuccess)
         return fail(FWPKM_ERR_HIP, "addressing step kernel: %s", hipGetErrorString(e));
     }
   }

@@ -179,7 +179,7 @@ class Memory:
     def forward_chunk(self, queries: torch.Tensor, targets: torch.Tensor, lr: float,
                       past: State, next: Optional[State] = None,
                       return_selection: bool = False, retrieved: Optional[torch.Tensor] = None,
-                      token_weights: Optional[torch.Tensor] = None):
+                      token_weights: Optional[torch.Tensor] = None, noalloc: bool = False):
         """One chunk: (retrieved [B, T, H, d_v], next state) from past state.
 
         queries [B, T, H, d_qk] (or [B, T, d_qk] when H == 1), targets likewise
@@ -187,6 +187,10 @@ class Memory:
         (functional update); next=past updates in place.  token_weights
         [B, T, H] (or [B, T] when H == 1) scales each token's loss; a weight
         of 0 reads without writing (fwpkm_forward_chunk_weighted).
+        noalloc=True calls fwpkm_forward_chunk_noalloc, which works in the
+        library's fixed device workspace and allocates nothing; to allocate
+        nothing in this method either, pass next and retrieved and leave
+        return_selection False.  It takes no token weights.
         """
         cfg = self.cfg
         _check_tensor("queries", queries)
@@ -212,7 +216,14 @@ class Memory:
         stream = torch.cuda.current_stream(queries.device).cuda_stream
         sel_ptrs = (slots.data_ptr() if slots is not None else None,
                     weights.data_ptr() if weights is not None else None)
-        if token_weights is None:
+        if noalloc:
+            if token_weights is not None:
+                raise ValueError("fwpkm_forward_chunk_noalloc takes no token weights")
+            rc = self._lib.fwpkm_forward_chunk_noalloc(
+                self._h, queries.data_ptr(), targets.data_ptr(), B, T, float(lr),
+                ctypes.byref(c_past), ctypes.byref(c_next), retrieved.data_ptr(),
+                *sel_ptrs, stream)
+        elif token_weights is None:
             rc = self._lib.fwpkm_forward_chunk(
                 self._h, queries.data_ptr(), targets.data_ptr(), B, T, float(lr),
                 ctypes.byref(c_past), ctypes.byref(c_next), retrieved.data_ptr(),
