@@ -18,9 +18,8 @@ import pytest
 import torch
 
 from oracle import fwpkm_oracle as O
-
-RTOL_CHUNK, ATOL_CHUNK = 1e-4, 1e-5
-RTOL_CHAIN, ATOL_CHAIN = 1e-3, 1e-4
+from oracle.compare import (ATOL_CHAIN, ATOL_CHUNK, RTOL_CHAIN, RTOL_CHUNK,  # noqa: F401
+                            error_stats, selection_overrides, validate_adopted_selection)
 
 
 def need_gpu():
@@ -84,96 +83,6 @@ def oracle_units(state, q, y, lr, k, eps, mode, units, H, overrides=None, tw=Non
     return rets, new, results
 
 
-def _tie_window(x, y):
-    """Z17's near-tie width around two values (relative 1e-6, floor 1)."""
-    return O.NEAR_TIE_REL * max(abs(x), abs(y), 1.0)
-
-
-# Exact-tie enumeration gives up beyond this many candidate slots per token
-# (then only the symmetric difference is checked for exact ties).
-_MAX_WINDOW_SLOTS = 1 << 20
-
-
-def validate_adopted_selection(r, t, chosen, n):
-    """Check that `chosen`, a selection the GPU made for token t where it
-    differs from the oracle's, is one an fp32 ranking may legitimately make.
-
-    r is the oracle's (non-overridden) UnitChunkResult of the unit.  Raises
-    AssertionError unless
-      * chosen holds k distinct slots in [0, n*n);
-      * every slot in the symmetric difference with the oracle's set has an
-        oracle value within the near-tie window of the k-th best value (a
-        slot the GPU dropped was not clearly better, one it took was not
-        clearly worse);
-      * where float64 values tie exactly, the lower slot was taken: no chosen
-        slot has a left-out slot of exactly its value and a lower index
-        (ties by lower slot, as both sides order candidates).
-    """
-    k = r.slots.shape[1]
-    N = n * n
-    chosen = [int(s) for s in chosen]
-    assert len(chosen) == k and len(set(chosen)) == k, (
-        f"token {t}: GPU selection {chosen} is not {k} distinct slots")
-    assert all(0 <= s < N for s in chosen), f"token {t}: GPU selection {chosen} leaves [0, {N})"
-    v1, v2 = r.half_values
-    sign = 1.0 if r.mode == O.IDW else -1.0          # order key: ascending is best first
-
-    def value(s):
-        return float(v1[t, s // n] + v2[t, s % n])
-
-    d_k = float(r.values[t, k - 1])                  # the oracle's k-th best value
-    mine, theirs = set(chosen), set(int(s) for s in r.slots[t])
-    for s in sorted(mine ^ theirs):
-        d = value(s)
-        assert abs(d - d_k) <= _tie_window(d, d_k), (
-            f"token {t}: slot {s} ({'taken' if s in mine else 'dropped'} by the GPU) has value "
-            f"{d!r}, outside the near-tie window of the k-th best {d_k!r}")
-    # slots whose value could lie within the window: per half, the sub-keys
-    # that can still reach it with the other half's best value
-    o1, o2 = sign * v1[t], sign * v2[t]
-    lim = sign * d_k + _tie_window(d_k, d_k) * 1.000001
-    A = np.flatnonzero(o1 + o2.min() <= lim)
-    B = np.flatnonzero(o2 + o1.min() <= lim)
-    if A.size * B.size <= _MAX_WINDOW_SLOTS:
-        cand = (A[:, None] * n + B[None, :]).reshape(-1)
-        cval = (v1[t, A][:, None] + v2[t, B][None, :]).reshape(-1)
-    else:
-        cand = np.asarray(sorted(mine ^ theirs), dtype=np.int64)
-        cval = np.asarray([value(s) for s in cand])
-    left_out = ~np.isin(cand, np.asarray(chosen))
-    for s in chosen:
-        d = value(s)
-        lower = cand[left_out & (cval == d) & (cand < s)]
-        assert lower.size == 0, (
-            f"token {t}: GPU took slot {s} over slot {int(lower[0])} of exactly the same value "
-            f"{d!r} (ties go to the lower slot)")
-
-
-def selection_overrides(results, gpu_slots, H, units, n=None):
-    """Compare slot sets; returns ({u: {t: gpu set}}, near-tie count).
-
-    A set may differ from the oracle's only at a near-tie (k-th and (k+1)-th
-    best within 1e-6 relative), and then only as validate_adopted_selection
-    allows; the oracle then adopts the GPU's set for that token."""
-    overrides, ties = {}, 0
-    for u in units:
-        b, h = divmod(u, H)
-        r = results[u]
-        nn = n if n is not None else r.half_values[0].shape[1]
-        g = gpu_slots[b, :, h]
-        for t in range(g.shape[0]):
-            gs = sorted(int(s) for s in g[t])
-            os_ = sorted(int(s) for s in r.slots[t])
-            if gs != os_:
-                assert r.near_tie[t], (
-                    f"unit {u} token {t}: GPU slots {gs} != oracle {os_} without a near-tie "
-                    f"(k-th {r.values[t, -1]!r}, (k+1)-th {r.value_k1[t]!r})")
-                validate_adopted_selection(r, t, gs, nn)
-                overrides.setdefault(u, {})[t] = gs
-                ties += 1
-    return overrides, ties
-
-
 def assert_close(name, got, want, rtol, atol):
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
@@ -232,3 +141,67 @@ def compare_chunk(mem, st_host, q, y, lr, units=None, rtol=RTOL_CHUNK, atol=ATOL
     for name in ("k1", "k2", "v"):
         assert_close(f"{label} next {name}", got[name], new[name], rtol, atol)
     return new, ties, nxt
+
+
+def mirror_units(dev_state, units):
+    """Host copy (oracle layout, float32) of some units' tables on the GPU."""
+    return state_to_host(dev_state, units)
+
+
+def teacher_forced_step(mem, dev_state, mirror, units, q, y, lr, label="", tw=None):
+    """One chunk on the GPU (every unit, in place, the launch the benchmark
+    times) checked against the oracle on sampled units, teacher-forced: the
+    oracle starts from `mirror`, a host copy of those units' tables equal to
+    the GPU's before the chunk, and afterwards `mirror` is brought to the
+    GPU's new state (sub-key tables copied whole, value rows at the slots the
+    GPU selected: the only rows it writes).
+
+    q, y [B, C, H, d] numpy.  Returns (near-ties, error stats dict)."""
+    cfg = mem.cfg
+    H = cfg.num_heads
+    say(label, "gpu chunk (in place)")
+    ret, _, slots, weights = mem.forward_chunk(to_dev(q), to_dev(y), lr, dev_state, next=dev_state,
+                                               return_selection=True,
+                                               token_weights=None if tw is None else to_dev(tw))
+    torch.cuda.synchronize()
+    ret = ret.cpu().numpy()
+    slots_h = slots.cpu().numpy()
+    weights_h = weights.cpu().numpy()
+    mode = mode_name(cfg.score_mode)
+    addr = getattr(cfg, "addr_weight", 0.0)
+    rets, new, results = oracle_units(mirror, q, y, lr, cfg.topk, cfg.eps, mode, units, H, tw=tw,
+                                      addr=addr)
+    overrides, ties = selection_overrides(results, slots_h, H, units)
+    if overrides:
+        rets, new, results = oracle_units(mirror, q, y, lr, cfg.topk, cfg.eps, mode, units, H,
+                                          overrides, tw=tw, addr=addr)
+    worst = {"retrieved": 0.0, "weights": 0.0, "k1": 0.0, "k2": 0.0, "v": 0.0}
+    for i, u in enumerate(units):
+        b, h = divmod(u, H)
+        assert_close(f"{label} retrieved u{u}", ret[b, :, h], rets[u], RTOL_CHUNK, ATOL_CHUNK)
+        worst["retrieved"] = max(worst["retrieved"],
+                                 error_stats(ret[b, :, h], rets[u], RTOL_CHUNK, ATOL_CHUNK)["tol_used"])
+        r = results[u]
+        go = np.argsort(slots_h[b, :, h], axis=1)
+        oo = np.argsort(r.slots, axis=1)
+        assert (np.take_along_axis(slots_h[b, :, h], go, 1) == np.take_along_axis(r.slots, oo, 1)).all()
+        gw = np.take_along_axis(weights_h[b, :, h], go, 1)
+        ow = np.take_along_axis(r.weights, oo, 1)
+        assert_close(f"{label} weights u{u}", gw, ow, RTOL_CHUNK, ATOL_CHUNK)
+        worst["weights"] = max(worst["weights"], error_stats(gw, ow, RTOL_CHUNK, ATOL_CHUNK)["tol_used"])
+        if lr == 0.0:
+            continue
+        # sub-key tables whole; value rows where either side wrote
+        for name in ("k1", "k2"):
+            got = getattr(dev_state, name)[b, h].cpu().numpy()
+            assert_close(f"{label} next {name} u{u}", got, new[name][i], RTOL_CHUNK, ATOL_CHUNK)
+            worst[name] = max(worst[name], error_stats(got, new[name][i], RTOL_CHUNK, ATOL_CHUNK)["tol_used"])
+            mirror[name][i] = got
+        gpu_rows = np.unique(slots_h[b, :, h])
+        rows = np.union1d(gpu_rows, r.updates["v"][0] if r.updates else gpu_rows)
+        idx = torch.as_tensor(rows, device=dev_state.v.device, dtype=torch.long)
+        got = dev_state.v[b, h].index_select(0, idx).cpu().numpy()
+        assert_close(f"{label} next v u{u}", got, new["v"][i][rows], RTOL_CHUNK, ATOL_CHUNK)
+        worst["v"] = max(worst["v"], error_stats(got, new["v"][i][rows], RTOL_CHUNK, ATOL_CHUNK)["tol_used"])
+        mirror["v"][i][rows] = got
+    return ties, worst

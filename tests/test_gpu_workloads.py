@@ -2,8 +2,11 @@
 benchmark times (every unit of the batch in one call, state updated in place).
 
 The oracle covers sampled units (units are independent memories, so a unit's
-result does not depend on the others) for every chunk it can afford; the long
-stream is checked teacher-forced at the start of its second pass.
+result does not depend on the others) for every chunk it can afford, chained
+(each side runs its own chain) and teacher-forced (the oracle restarts every
+chunk from a host copy of the GPU's tables); the streams are also checked
+teacher-forced through their second pass, the state a repeated stream
+leaves.
 """
 
 import numpy as np
@@ -12,8 +15,8 @@ import torch
 
 from oracle import fwpkm_oracle as O
 from parity_helpers import (ATOL_CHAIN, ATOL_CHUNK, RTOL_CHAIN, RTOL_CHUNK, assert_close,
-                            compare_chunk, need_gpu, oracle_units, say, selection_overrides,
-                            state_to_host, to_dev)
+                            compare_chunk, mirror_units, need_gpu, oracle_units, say,
+                            selection_overrides, state_to_host, teacher_forced_step, to_dev)
 from workloads import chunk_inputs, draw_queries, draw_targets, get_config, initial_tables
 
 pytestmark = pytest.mark.gpu
@@ -83,32 +86,62 @@ def test_library_default_shape_single_chunk_full():
     compare_chunk(mem, st, ci.queries, ci.targets, w.lr, label=w.name)
 
 
+def _teacher_forced_pass(mem, dev, Q, Y, w, units, chunks, label):
+    """Chunks 0..chunks-1 of a pass on the GPU (all units, in place), each
+    checked teacher-forced on `units` from a host mirror of the GPU tables."""
+    mirror = mirror_units(dev, units)
+    ties, worst = 0, {}
+    for c in range(chunks):
+        ci = chunk_inputs(Q, Y, w, c)
+        nt, wc = teacher_forced_step(mem, dev, mirror, units, ci.queries, ci.targets, w.lr,
+                                     label=f"{label} c{c}")
+        ties += nt
+        for key, val in wc.items():
+            worst[key] = max(worst.get(key, 0.0), val)
+    say(label, "near-ties", ties, "worst error / tolerance", worst)
+    return ties
+
+
 def test_training_length_stream_sampled_units():
-    """8 sequences x 4096 clustered tokens, 16 chained chunks; units 0 and 5 checked."""
+    """8 sequences x 4096 clustered tokens, 16 chained chunks; units 0 and 5
+    chained, then every unit teacher-forced through the first pass from the
+    initial tables (the benchmark's timed state) and through a second pass
+    of the same stream."""
     need_gpu()
     w = get_config(3)
     _chained(w, units=[0, 5], chunks=w.chunks)
+    mem = _mem_for(w)
+    tables = initial_tables(w)
+    Q, Y = draw_queries(w), draw_targets(w)
+    dev = _device_state(tables, w.batch)
+    units = list(range(w.units))
+    _teacher_forced_pass(mem, dev, Q, Y, w, units, w.chunks, f"{w.name} pass1")
+    _teacher_forced_pass(mem, dev, Q, Y, w, units, w.chunks, f"{w.name} pass2")
 
 
 def test_multihead_stream_sampled_units():
-    """4 heads x 262,144 slots, top-16, batch 4 x 8192 tokens; units (0,0) and (2,3)."""
+    """4 heads x 262,144 slots, top-16, batch 4 x 8192 tokens; units (0,0)
+    and (2,3) chained with every chunk's retrieved checked, then one unit
+    per head (on four XCDs) teacher-forced through the first four chunks."""
     need_gpu()
     w = get_config(4)
-    _chained(w, units=[0, 11], chunks=w.chunks, check_every_chunk=False)
+    _chained(w, units=[0, 11], chunks=w.chunks, check_every_chunk=True)
+    mem = _mem_for(w)
+    Q, Y = draw_queries(w), draw_targets(w)
+    dev = _device_state(initial_tables(w), w.batch)
+    _teacher_forced_pass(mem, dev, Q, Y, w, [0, 5, 10, 15], 4, f"{w.name} tf")
 
 
 def test_long_context_two_passes():
-    """1 x 131,072 tokens over 2^20 slots, read twice: the first 16 chunks chained,
-    then the whole first pass on the GPU and the second pass's first chunk
-    teacher-forced from the GPU state."""
+    """1 x 131,072 tokens over 2^20 slots, read twice: the first 16 chunks
+    chained, then the rest of the first pass on the GPU and the second
+    pass's first 16 chunks teacher-forced from the GPU state."""
     need_gpu()
     w = get_config(5)
-    mem, dev, Q, Y = _chained(w, units=[0], chunks=16, check_every_chunk=False)
+    mem, dev, Q, Y = _chained(w, units=[0], chunks=16)
     for c in range(16, w.chunks):
         ci = chunk_inputs(Q, Y, w, c)
         mem.forward_chunk(to_dev(ci.queries), to_dev(ci.targets), w.lr, dev, next=dev)
     torch.cuda.synchronize()
-    say(w.name, "first pass done on the GPU; second pass, chunk 0, teacher-forced")
-    st = state_to_host(dev)
-    ci = chunk_inputs(Q, Y, w, 0)
-    compare_chunk(mem, st, ci.queries, ci.targets, w.lr, label=f"{w.name} pass2 c0")
+    say(w.name, "first pass done on the GPU; second pass, 16 chunks, teacher-forced")
+    _teacher_forced_pass(mem, dev, Q, Y, w, [0], 16, f"{w.name} pass2")
