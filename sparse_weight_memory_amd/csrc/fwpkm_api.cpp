@@ -34,7 +34,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Byte sizes of the workspace regions for `units` units of `tokens` tokens.
 struct WsLayout {
-  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, pay, long_rec, short_rec, kinds;
+  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, ent_row, ent_tw, kinds;
   size_t addr_s, addr_dk, addr_tok, addr_ell, total;
 };
 
@@ -51,9 +51,8 @@ WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
   L.g = take(sizeof(float) * units * tokens * c.dim_v);
   L.keys = take(sizeof(int) * 3 * units * P);
   L.coef = take(sizeof(float) * 2 * units * P);
-  L.pay = take(sizeof(int) * 3 * units * P);
-  L.long_rec = take(sizeof(int4) * 3 * units * P);
-  L.short_rec = take(sizeof(int4) * 3 * units * P);
+  L.ent_row = take(sizeof(int) * 3 * units * P);
+  L.ent_tw = take(sizeof(int2) * 3 * units * P);
   // regions per list shrink as units grow: 3 * units * regions <= max(256, 3 * units)
   L.kinds = take(sizeof(int4) * std::max<int64_t>(256, 3 * units));
   // addressing loss (only with addr_weight != 0): every token's score over
@@ -593,9 +592,8 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
   a.g = reinterpret_cast<float*>(ws + L.g);
   a.keys = reinterpret_cast<int*>(ws + L.keys);
   a.coef = reinterpret_cast<float*>(ws + L.coef);
-  a.pay = reinterpret_cast<int*>(ws + L.pay);
-  a.long_rec = reinterpret_cast<int4*>(ws + L.long_rec);
-  a.short_rec = reinterpret_cast<int4*>(ws + L.short_rec);
+  a.ent_row = reinterpret_cast<int*>(ws + L.ent_row);
+  a.ent_tw = reinterpret_cast<int2*>(ws + L.ent_tw);
   a.kinds = reinterpret_cast<int4*>(ws + L.kinds);
   a.regions = fwpkm::group_regions((int)U);
   a.region_bits = 0;

@@ -13,8 +13,7 @@ constexpr int kTokTile = 16;        // tokens per score workgroup (MFMA N)
 constexpr int kAddrPad = 256;   // score-row pitch multiple of the addressing loss (4 loads per lane)
 constexpr int kGroupWaves = 8;      // waves of one grouping workgroup
 constexpr int kSortMaxPairs = 8192; // C*k limit of the in-LDS sort
-constexpr int kShortSeg = 16;       // longest segment one update wave sums alone
-constexpr int kUpdMaxLists = 3072;  // 3 * units the update kernel can index
+constexpr int kUpdMaxLists = 3072;  // 3 * units (lists) a chunk may carry
 #define FWPKM_MAX_HALF_DIM 1024     // largest d_h the score kernel stages
 
 // Invalid entries: they order after every real candidate.
@@ -91,10 +90,9 @@ struct ChunkArgs {
   float* coef;     // [2, U, P] merged key coefficient of a K1 / K2 pair
   // grouping output, per (list, unit) in [3, U, P] arrays; region r of a list
   // owns entries [offset_r, offset_r + its pairs)
-  int* pay;        // each list's kept pair indices, sorted by row (stable)
-  int4* long_rec;  // (row, first pair, pairs, 0) of segments > kShortSeg pairs
-  int4* short_rec; // the same for the other segments
-  int4* kinds;     // [3, U, regions] (long segments, short segments, offset_r, 0)
+  int* ent_row;    // each list's kept entries' rows, sorted by row (stable)
+  int2* ent_tw;    // their (token, weight bits): V softmax weight / K coefficient
+  int4* kinds;     // [3, U, regions] (0, 0, offset_r, entries)
   int regions;     // hash regions per (list, unit), a power of two
   int region_bits; // log2(regions)
   int pw;          // floats per row = max(d_v, d_h)
@@ -118,6 +116,14 @@ struct ChunkArgs {
   FastDiv div_U;       // x / U
   FastDiv div_upx;     // x / (U / 8): units per XCD
   FastDiv div_nbx;     // x / ceil(T / 4): read workgroups per unit
+  // update-kernel geometry, derived on the host by its launcher: column
+  // slices of kd_sw floats, kd_sv of them per V row and kd_sk per K row,
+  // 2^kd_sg_bits groups of hash regions per (list, unit)
+  int kd_sv;
+  int kd_sk;
+  int kd_sg_bits;
+  FastDiv kd_div_pu;   // x / ((kd_sv + 2 kd_sk) << kd_sg_bits): workgroups per unit
+  FastDiv kd_div_sk;   // x / kd_sk
 };
 
 // `a` with the decomposition divisors filled in
@@ -155,6 +161,13 @@ __device__ __forceinline__ int64_t seq_chunk_row(const SeqArgs& s, int b, int t)
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Token of pair p = t*k + m without an integer divide: (p + 1/2) / k lies at
+// least 1/(2k) >= 1/64 away from an integer, relative 2e-6 at p < 8192, far
+// above the reciprocal's error.
+__device__ __forceinline__ int token_of(int p, int k) {
+  return (int)(((float)p + 0.5f) * __builtin_amdgcn_rcpf((float)k));
+}
 
 // Units and XCDs.  Workgroup i of every launch runs on XCD i % 8 (the
 // dispatcher deals workgroups to the eight XCDs in turn), each XCD has its

@@ -30,12 +30,15 @@
 // row shifts; rows and pair indices move together, so no pass looks a key up
 // indirectly.
 //
-// Outputs per region, at its offset in the (list, unit) arrays:
-//   pay        the kept pair indices in sorted order -- the update kernel
-//              reads a segment's pairs with one load;
-//   long_rec   (row, first pair, pairs) of segments longer than kShortSeg;
-//   short_rec  the same for the other segments;
-//   kinds      (long count, short count, offset).
+// Outputs per region, at its offset in the (list, unit) arrays (regions
+// follow one another in hash order, so a run of regions is one contiguous
+// run of entries):
+//   ent_row    the kept entries' rows in sorted order (a segment is a run of
+//              equal rows);
+//   ent_tw     their (token, weight) -- the pair's softmax weight for V, its
+//              merged key coefficient for K1 / K2 -- so the update kernel
+//              reads everything about an entry in one round;
+//   kinds      (0, 0, offset, entries).
 
 #include "fwpkm_device.h"
 #include "fwpkm_launch.h"
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   }
   int4* kinds = a.kinds + ((int64_t)list * a.U + u) * a.regions + region;
   if (M == 0) {                     // block-uniform
-    if (tid == 0) *kinds = make_int4(0, 0, off, 0);
+    if (tid == 0) *kinds = make_int4(0, 0, off, 0);   // no entries
     return;
   }
   // regions of at most kRankMax entries whose rows need two or more radix
@@ -317,80 +320,32 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   }
   }
 
-  // ---- segments: heads of runs of equal rows.  The pong buffers are free
-  // now; segment starts go to kd[0..nseg], whose last entry may spill into
-  // id[0] (kd and id are adjacent and both unused).
-  int* segl = kd;
-  int heads_w = 0;
-  for (int tile = t_lo; tile < t_hi; ++tile) {
-    const int i = tile * kWave + lane;
-    const bool head = i < M && (i == 0 || ks[i - 1] != ks[i]);
-    heads_w += __popcll(__ballot(head));
-  }
-  if (lane == 0) red[wave] = heads_w;
-  __syncthreads();
-  int hbase = 0, nseg = 0;
-#pragma unroll
-  for (int w = 0; w < kGroupWaves; ++w) {
-    const int t = red[w];
-    hbase += w < wave ? t : 0;
-    nseg += t;
-  }
-  int* pay = a.pay + lbase + off;
-  for (int tile = t_lo; tile < t_hi; ++tile) {
-    const int i = tile * kWave + lane;
-    const bool head = i < M && (i == 0 || ks[i - 1] != ks[i]);
-    const unsigned long long m = __ballot(head);
-    if (head) segl[hbase + __popcll(m & lanes_below())] = i;
-    if (i < M) pay[i] = is[i];
-    hbase += __popcll(m);
-  }
-  if (tid == 0) segl[nseg] = M;
-  __syncthreads();
+  if (tid == 0) *kinds = make_int4(0, 0, off, M);
 
-  // ---- segment records, long and short ones apart, each in segment order
-  const int stiles = (nseg + kWave - 1) / kWave;
-  const int stpw = (stiles + kGroupWaves - 1) / kGroupWaves;
-  const int s_lo = wave * stpw, s_hi = min(stiles, s_lo + stpw);
-  int nl = 0, ns = 0;
-  for (int tile = s_lo; tile < s_hi; ++tile) {
-    const int s = tile * kWave + lane;
-    const bool in = s < nseg;
-    const bool lng = in && segl[s + 1] - segl[s] > kShortSeg;
-    nl += __popcll(__ballot(lng));
-    ns += __popcll(__ballot(in && !lng));
-  }
-  if (lane == 0) {
-    red[wave] = nl;
-    red[kGroupWaves + wave] = ns;
-  }
-  __syncthreads();
-  int lb = 0, sb = 0, tot_long = 0, tot_short = 0;
+  // ---- entries in sorted order: row, then (token, weight or coefficient)
+  // of the pair; the weight lookups of a wave go out together
+  int* erow = a.ent_row + lbase + off;
+  int2* etw = a.ent_tw + lbase + off;
+  const float* wsrc = list == 0 ? a.sel_w + (int64_t)u * P
+                                : a.coef + (int64_t)(list - 1) * a.U * P + (int64_t)u * P;
+  constexpr int kOutTiles = kScanTiles;
+  float wv[kOutTiles];
+  int pv[kOutTiles];
 #pragma unroll
-  for (int w = 0; w < kGroupWaves; ++w) {
-    lb += w < wave ? red[w] : 0;
-    sb += w < wave ? red[kGroupWaves + w] : 0;
-    tot_long += red[w];
-    tot_short += red[kGroupWaves + w];
+  for (int j = 0; j < kOutTiles; ++j) {
+    const int i = (t_lo + j) * kWave + lane;
+    pv[j] = (t_lo + j < t_hi && i < M) ? is[i] : 0;
   }
-  int4* lrec = a.long_rec + lbase + off;
-  int4* srec = a.short_rec + lbase + off;
-  for (int tile = s_lo; tile < s_hi; ++tile) {
-    const int s = tile * kWave + lane;
-    const bool in = s < nseg;
-    const int s0 = in ? segl[s] : 0;
-    const int len = in ? segl[s + 1] - s0 : 0;
-    const bool lng = in && len > kShortSeg;
-    const unsigned long long ml = __ballot(lng), msh = __ballot(in && !lng);
-    if (in) {
-      const int4 rec = make_int4(ks[s0], off + s0, len, 0);
-      if (lng) lrec[lb + __popcll(ml & lanes_below())] = rec;
-      else srec[sb + __popcll(msh & lanes_below())] = rec;
+#pragma unroll
+  for (int j = 0; j < kOutTiles; ++j) wv[j] = wsrc[pv[j]];
+#pragma unroll
+  for (int j = 0; j < kOutTiles; ++j) {
+    const int i = (t_lo + j) * kWave + lane;
+    if (t_lo + j < t_hi && i < M) {
+      erow[i] = ks[i];
+      etw[i] = make_int2(token_of(pv[j], a.k), __float_as_int(wv[j]));
     }
-    lb += __popcll(ml);
-    sb += __popcll(msh);
   }
-  if (tid == 0) *kinds = make_int4(tot_long, tot_short, off, 0);
 }
 
 int group_regions(int units) {

@@ -7,23 +7,38 @@
 //   K1 row  IDW: theta_r <- theta_r - lr * (1/n_r) sum_p c_p (q1_{t_p} - theta_r)
 //           dot: theta_r <- theta_r - lr * (1/n_r) sum_p c_p q1_{t_p}
 //   K2 row  likewise with q2.
-// All gradients are taken at the chunk's starting weights: each row is
-// written once, by the wave that finishes it, after every wave that reads its
-// old value has done so (within the workgroup), so updating in place is
-// exact.
+// All gradients are taken at the chunk's starting weights: every (row,
+// column) is read and then written by one wave of one workgroup, so
+// updating in place is exact.
 // [agifrontier tutorial "Fast-weight Product Key Memory", update equation
 // theta' = theta - eta grad L_MSE; gist.science summary, section 2: Key and
 // Value matrices updated online, gradients of a slot used several times in a
 // chunk averaged; sciencestack.ai contents: no gradient clipping]
 //
-// Work distribution, over every region of every list and unit: a task is
-// either one long segment (more than kShortSeg pairs), which the W waves of a
-// workgroup split into contiguous pieces and combine in LDS in wave order,
-// or up to W short segments, one per wave.  A segment's record (row, first
-// pair, pairs) and its sorted pair indices come straight from the grouping
-// kernel; a pair's coefficient is loaded beside its data row, so a wave
-// reaches the data rows after two dependent loads.  Every sum runs in a fixed order, so results do not
-// depend on scheduling, and no atomics are used.
+// Work distribution.  A row's gradient is a sum over its tokens' data rows
+// (g_t for V, a query half for K), and a row touched by many tokens (the
+// common case with clustered queries) would stream all of those rows through
+// one compute unit.  Instead every list is cut into column slices of SW
+// floats: a workgroup owns (unit, list, column slice, group of hash
+// regions), stages that slice of every token's data row in LDS once, and
+// sums each of its rows' pairs from LDS.  A hot row is thus spread over as
+// many compute units as its list has slices, and each pair costs an LDS read
+// instead of a dependent global load.
+//
+// The grouping kernel leaves, per (list, unit), the kept entries sorted by
+// row, each with its token and weight (coefficient), regions one after
+// another; a group of consecutive regions is one contiguous run of entries,
+// whose segments (runs of one row) this kernel finds itself.  A workgroup
+// thus needs two dependent global rounds (region offsets, then entries)
+// before it can sum.  Each wave takes work items in turn: a segment of at
+// most kKdPiece pairs, or one kKdPiece-pair piece of a longer segment (the
+// pieces' partial sums meet in LDS and are added in piece order).  Inside a
+// wave the lanes form SW/4 float4 columns times 256/SW pair groups; lane l
+// holds the token and weight of one pair, pair group g sums pairs g,
+// g + groups, ... as DPP broadcasts hand them over (only as many steps as the
+// item needs), and a fixed butterfly adds the groups.  Every sum runs in
+// one fixed order, results do not depend on scheduling, and no atomics are
+// used.
 
 #include "fwpkm_device.h"
 #include "fwpkm_launch.h"
@@ -32,367 +47,505 @@ namespace fwpkm {
 
 namespace {
 
+constexpr int kKdWaves = 16;                    // waves of an update workgroup
+constexpr int kKdThreads = kKdWaves * kWave;
+constexpr int kKdDataBytes = 64 * 1024;         // a column slice of every token's data row
+constexpr int kKdEntCap = 2048;                 // entries (pairs) staged at a time
+constexpr int kKdPer = kKdEntCap / kKdThreads;  // entries per thread
+constexpr int kKdPiece = kWave;                 // pairs one wave sums; longer segments are cut
+constexpr int kKdMaxLong = 2 * kKdEntCap / kKdPiece;   // pieces of long segments per batch
+constexpr int kKdMaxPieces = 1023;              // pieces of a batch (segments of > 4 pairs)
+static_assert(kKdEntCap / 5 + kKdMaxLong <= kKdMaxPieces, "piece count fits its field");
+constexpr int kKdPrefetch = 2;                  // old-row float4 prefetched per lane per round
+static_assert(kKdPer * kKdThreads == kKdEntCap, "whole entries per thread");
 
-// Regions in XCD-affine order (unit count a multiple of 8): position r =
-// ((x * 3 + list) * (U / 8) + ul) * regions + rg holds region
-// (list * U + x * (U / 8) + ul) * regions + rg, so the regions of the units
-// XCD x runs (see unit_affine_item) are positions [x L / 8, (x + 1) L / 8).
-// The identity otherwise.
-__device__ __forceinline__ int region_at(int r, const ChunkArgs& a) {
-  const int units = a.U;
-  if (units % kXcds != 0) return r;
-  const int upx = units / kXcds;
-  const int rg = r & (a.regions - 1);           // regions is a power of two
-  const int rest = r >> a.region_bits;
-  const int lx = fast_div(rest, a.div_upx);     // x * 3 + list
-  const int ul = rest - lx * upx;
-  const int x = lx / 3, list = lx - 3 * x;
-  return (((list * units + x * upx + ul) << a.region_bits) | rg);
+// LDS layout (byte offsets) for chunks of T tokens and slices of SW floats.
+struct KdLds {
+  int dat, ent_t, ent_w, ent_row, seg_beg, seg_item, short_seg, items, part, part_c, red, total;
+};
+__host__ __device__ constexpr int kd_align(int x) { return (x + 15) & ~15; }
+__host__ __device__ constexpr KdLds kd_lds_layout(int T, int SW) {
+  KdLds L{};
+  int o = 0;
+  L.dat = o;      o = kd_align(o + T * (SW / 4 + 1) * 16);        // [T][SW/4 + 1] float4 (padded rows)
+  L.ent_t = o;    o = kd_align(o + kKdEntCap * 4);
+  L.ent_w = o;    o = kd_align(o + kKdEntCap * 4);
+  L.ent_row = o;  o = kd_align(o + (kKdEntCap + 1) * 4);         // + the row after the batch
+  L.seg_beg = o;  o = kd_align(o + (kKdEntCap + 1) * 4);         // segment starts, then the end
+  L.seg_item = o; o = kd_align(o + kKdEntCap * 4);               // short index | piece << 12 | slot << 22
+  L.short_seg = o; o = kd_align(o + kKdEntCap * 4);              // short segments in order
+  L.items = o;    o = kd_align(o + kKdMaxPieces * 4);            // pieces of longer segments
+  L.part = o;     o = kd_align(o + kKdMaxLong * (SW / 4) * 16);  // partial sums of long pieces
+  L.part_c = o;   o = kd_align(o + kKdMaxLong * 4);
+  L.red = o;      o = kd_align(o + 4 * kKdWaves * 4);
+  L.total = o;
+  return L;
 }
 
-// pref[i] = tasks of the regions at positions [r0, i) (region_at order) for
-// i in [r0, r1]; nlong / nshort / offs receive those regions' counts, by
-// position.  All threads of the block take part.
-template <int W>
-__device__ void task_prefix(const ChunkArgs& a, int r0, int r1, int* pref,
-                            int* nlong, int* nshort, int* offs, int* wtot) {
-  constexpr int NT = W * kWave;
-  const int tid = threadIdx.x, wave = tid / kWave;
-  const int per = (r1 - r0 + NT - 1) / NT;
-  const int beg = r0 + tid * per;
-  int local = 0;
-  for (int j = 0; j < per; ++j) {
-    if (beg + j < r1) {
-      const int4 kd = a.kinds[region_at(beg + j, a)];
-      nlong[beg + j] = kd.x;
-      nshort[beg + j] = kd.y;
-      offs[beg + j] = kd.z;
-      local += kd.x + (kd.y + W - 1) / W;
-    }
-  }
-  const int incl = wave_inclusive_scan(local);
-  if (lane_id() == kWave - 1) wtot[wave] = incl;
+// Exclusive scan of one int per thread over the block; *total = the sum.
+// `red` (kKdWaves ints) must not be written again before the caller's next
+// barrier.
+__device__ __forceinline__ int kd_block_scan(int x, int* red, int* total) {
+  const int wave = threadIdx.x / kWave;
+  const int incl = wave_inclusive_scan(x);
+  if (lane_id() == kWave - 1) red[wave] = incl;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wtot[w];
-  int run = base + incl - local;
-  for (int j = 0; j < per; ++j) {
-    if (beg + j < r1) {
-      pref[beg + j] = run;
-      run += nlong[beg + j] + (nshort[beg + j] + W - 1) / W;
+  int base = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kKdWaves; ++w) {
+    const int t = red[w];
+    base += w < wave ? t : 0;
+    sum += t;
+  }
+  *total = sum;
+  return base + incl - x;
+}
+
+__device__ __forceinline__ float4 f4_fma(float w, float4 x, float4 acc) {
+  acc.x = fmaf(w, x.x, acc.x); acc.y = fmaf(w, x.y, acc.y);
+  acc.z = fmaf(w, x.z, acc.z); acc.w = fmaf(w, x.w, acc.w);
+  return acc;
+}
+
+__device__ __forceinline__ float4 f4_add(float4 x, float4 y) {
+  return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+}
+
+template <int S>
+__device__ __forceinline__ float4 f4_xor(float4 v) {
+  return make_float4(xor_lane<S>(v.x), xor_lane<S>(v.y), xor_lane<S>(v.z), xor_lane<S>(v.w));
+}
+
+// Sum over the pair groups (lane bits from log2(L4) up): a fixed butterfly,
+// every lane receives the total.  All lanes active.
+template <int L4>
+__device__ __forceinline__ void pair_group_sum(float4& acc, float& cs) {
+  if constexpr (L4 <= 4) { acc = f4_add(acc, f4_xor<4>(acc)); cs += xor_lane<4>(cs); }
+  if constexpr (L4 <= 8) { acc = f4_add(acc, f4_xor<8>(acc)); cs += xor_lane<8>(cs); }
+  if constexpr (L4 <= 16) { acc = f4_add(acc, f4_xor<16>(acc)); cs += xor_lane<16>(cs); }
+  acc = f4_add(acc, f4_xor<32>(acc));
+  cs += xor_lane<32>(cs);
+}
+
+// Lane (lane & ~(L4 - 1)) + S's value, for every lane: DPP broadcasts within
+// quads (L4 = 4) or rows of 16 (L4 = 16; two of them for halves, L4 = 8).
+template <int L4, int S>
+__device__ __forceinline__ int group_bcast(int x) {
+  static_assert(S >= 0 && S < L4, "step");
+  if constexpr (L4 == 4) {
+    return __builtin_amdgcn_update_dpp(0, x, S * 0x55, 0xF, 0xF, false);         // quad_perm [S,S,S,S]
+  } else if constexpr (L4 == 16) {
+    return __builtin_amdgcn_update_dpp(0, x, 0x150 + S, 0xF, 0xF, false);        // row_newbcast:S
+  } else {
+    const int lo = __builtin_amdgcn_update_dpp(0, x, 0x150 + S, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, x, 0x150 + 8 + S, 0xF, 0xF, false);
+    return (lane_id() & 8) ? hi : lo;
+  }
+}
+
+// Steps S, S+1, ... < steps of an item, four at a time (their LDS reads go
+// out together; a step past the item's pairs adds weight 0): step s hands
+// pair group g its pair held by lane g * L4 + s (pair s * groups + g).
+// `steps` is wave-uniform, in a scalar register.
+template <int L4, int S>
+__device__ __forceinline__ void sum_steps(int steps, int my_t, int my_w, const float4* dat, int c4,
+                                          float4& acc, float& cs) {
+  if constexpr (S < L4) {
+    static_assert(L4 % 4 == 0, "whole batches of four steps");
+    if (S >= steps) return;
+    const int t[4] = {group_bcast<L4, S>(my_t), group_bcast<L4, S + 1>(my_t),
+                      group_bcast<L4, S + 2>(my_t), group_bcast<L4, S + 3>(my_t)};
+    const float w[4] = {__int_as_float(group_bcast<L4, S>(my_w)),
+                        __int_as_float(group_bcast<L4, S + 1>(my_w)),
+                        __int_as_float(group_bcast<L4, S + 2>(my_w)),
+                        __int_as_float(group_bcast<L4, S + 3>(my_w))};
+    float4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = dat[t[i] * (L4 + 1) + c4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = f4_fma(w[i], x[i], acc);
+      cs += w[i];
     }
+    sum_steps<L4, S + 4>(steps, my_t, my_w, dat, c4, acc, cs);
   }
-  if (tid == NT - 1) pref[r1] = run;
-  __syncthreads();
-}
-
-// The position in [r0, r1) of the region holding `task`: the largest r with
-// pref[r] <= task (pref is nondecreasing and pref[r0] <= task < pref[r1]).
-// A 64-way search per round: lane l tests position lo + l * step, and the
-// lanes that pass are a prefix of the wave.
-__device__ __forceinline__ int find_region(const int* pref, int r0, int r1, int task) {
-  int lo = r0, span = r1 - r0;
-  while (span > 1) {
-    const int step = (span + kWave - 1) / kWave;
-    const int at = lo + lane_id() * step;
-    const bool ok = at < lo + span && pref[at] <= task;
-    const int c = __popcll(__ballot(ok));        // >= 1: position lo passes
-    lo += (c - 1) * step;
-    span = min(step, r0 + (r1 - r0) - lo);
-  }
-  return lo;
-}
-
-// A table row as R float4 per lane, unguarded: columns past the row re-read
-// its last float4.  Those lanes' sums are never stored, so the values need no
-// mask, and nothing consumes the loads before the pair sums need them.
-template <int R>
-__device__ __forceinline__ void load_row(const float4* row, int width4, float4 (&out)[R]) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int c = lane + 64 * r;
-    out[r] = row[c < width4 ? c : width4 - 1];
-  }
-}
-
-// Token of pair p = t*k + m without an integer divide: (p + 1/2) / k lies at
-// least 1/(2k) >= 1/64 away from an integer, relative 2e-6 at p < 8192, far
-// above the reciprocal's error.
-__device__ __forceinline__ int token_of(int p, int k) {
-  return (int)(((float)p + 0.5f) * __builtin_amdgcn_rcpf((float)k));
-}
-
-// One wave's sum over the sorted pairs pay[0, n) of a V segment:
-// sum_p w_p g_{t_p}.  NB data rows are in flight at a time.  The row's
-// current value goes into `old`, loaded in the first round beside the pairs'
-// data (loads outstanding at a loop's head would be waited for there).
-template <int R, int NB>
-__device__ __forceinline__ void sum_value_pairs(const ChunkArgs& a, int u, const int* pay,
-                                                int n, const float4* trow, int width4,
-                                                float4 (&old)[R], float4 (&acc)[R]) {
-  const int lane = lane_id();
-  const float* gbase = a.g + (int64_t)u * a.T * a.dv;
-  const float* sw = a.sel_w + (int64_t)u * a.P;
-  for (int base = 0; base < n; base += kWave) {
-    const int nb = min(kWave, n - base);
-    const int pl = lane < nb ? pay[base + lane] : 0;
-    const int tl = token_of(pl, a.k);
-    float wl = 0.f;
-    for (int i = 0; i < nb; i += NB) {
-      float4 gv[NB][R];
-#pragma unroll
-      for (int jj = 0; jj < NB; ++jj) {
-        const int t = readlane_i(tl, min(i + jj, nb - 1));
-        const float4* gr = reinterpret_cast<const float4*>(gbase + (int64_t)t * a.dv);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int c = lane + 64 * r;
-          gv[jj][r] = (i + jj < nb && c < width4) ? gr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-      // the pairs' weights and the row's value go out behind the first
-      // round's data rows (loads outstanding at a loop's head are waited for
-      // there); lanes >= nb read pair 0's weight, never used
-      if (i == 0) {
-        wl = sw[pl];
-        if (base == 0) load_row<R>(trow, width4, old);
-      }
-#pragma unroll
-      for (int jj = 0; jj < NB; ++jj) {
-        if (i + jj < nb) {
-          const float w = readlane_f(wl, i + jj);
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            acc[r].x += w * gv[jj][r].x; acc[r].y += w * gv[jj][r].y;
-            acc[r].z += w * gv[jj][r].z; acc[r].w += w * gv[jj][r].w;
-          }
-        }
-      }
-    }
-  }
-}
-
-// One wave's sum over the pairs pay[0, n) of a K segment (half h):
-//   IDW sum_p c_p (q_h[t_p] - old),  dot sum_p c_p q_h[t_p];
-// `old` (the row's current value) is loaded as for value segments.
-template <int R, int NB>
-__device__ __forceinline__ void sum_key_pairs(const ChunkArgs& a, int u, int h, const int* pay,
-                                              int n, const float4* trow, int width4,
-                                              float4 (&old)[R], float4 (&acc)[R]) {
-  const int lane = lane_id();
-  const int b = fast_div(u, a.div_H), hh = u - b * a.H;
-  const bool idw = a.mode == 0;
-  const float* cf = a.coef + (int64_t)h * a.U * a.P + (int64_t)u * a.P;
-  for (int base = 0; base < n; base += kWave) {
-    const int nb = min(kWave, n - base);
-    const int pl = lane < nb ? pay[base + lane] : 0;
-    const int tl = token_of(pl, a.k);
-    float cl = 0.f;
-    for (int i = 0; i < nb; i += NB) {
-      float4 qv[NB][R];
-#pragma unroll
-      for (int jj = 0; jj < NB; ++jj) {
-        const int t = readlane_i(tl, min(i + jj, nb - 1));
-        const float4* qr = reinterpret_cast<const float4*>(
-            a.q + ((int64_t)(b * a.T + t) * a.H + hh) * a.dqk + h * a.half);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int c = lane + 64 * r;
-          qv[jj][r] = (i + jj < nb && c < width4) ? qr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-      // coefficients and the row's value behind the first round's data rows
-      if (i == 0) {
-        cl = cf[pl];
-        if (base == 0) load_row<R>(trow, width4, old);
-      }
-#pragma unroll
-      for (int jj = 0; jj < NB; ++jj) {
-        if (i + jj < nb) {
-          const float cc = readlane_f(cl, i + jj);
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            float4 x = qv[jj][r];
-            if (idw) { x.x -= old[r].x; x.y -= old[r].y; x.z -= old[r].z; x.w -= old[r].w; }
-            acc[r].x += cc * x.x; acc[r].y += cc * x.y; acc[r].z += cc * x.z; acc[r].w += cc * x.w;
-          }
-        }
-      }
-    }
-  }
-}
-
-// Waves per SIMD each variant is compiled for: two workgroups of W waves per
-// compute unit (four SIMDs), so a chunk's tasks fit on the device at once
-// (the register budget per wave is 512 / waves).
-template <int W>
-constexpr int kd_waves_per_simd() { return 2 * W / 4; }
-constexpr int kKdResidentPerCu = 2;
-
-// LDS of one update workgroup for L regions: partial sums, then the region
-// table.
-template <int R, int W>
-__host__ __device__ constexpr size_t kd_parts_bytes() {
-  return sizeof(float4) * (size_t)W * kWave * R;
 }
 
 }  // namespace
 
-template <int R, int W, int NB>
-__global__ __launch_bounds__(W * kWave, kd_waves_per_simd<W>()) void kd_update(ChunkArgs a) {
-  extern __shared__ float4 kd_lds[];
-  float4* parts = kd_lds;                                             // [W][64 R]
-  const int L = 3 * a.U * a.regions;
-  int* pref = reinterpret_cast<int*>(kd_lds + (size_t)W * kWave * R); // [L + 1]
-  int* nlong = pref + L + 1;                                          // [L]
-  int* nshort = nlong + L;                                            // [L]
-  int* offs = nshort + L;                                             // [L]
-  int* wtot = offs + L;                                               // [W]
-  // workgroups of XCD x take the tasks of that XCD's units (the grid is a
-  // multiple of 8 then) and count only those regions; otherwise every
-  // workgroup strides over all tasks
-  int r_lo = 0, r_hi = L, t_first = blockIdx.x, t_step = gridDim.x;
-  if (a.U % kXcds == 0) {
-    r_lo = (blockIdx.x % kXcds) * (L / kXcds);
-    r_hi = r_lo + L / kXcds;
-    t_first = blockIdx.x / kXcds;
-    t_step = gridDim.x / kXcds;
+template <int SW>
+__global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
+  constexpr int L4 = SW / 4;                 // float4 columns of a slice
+  constexpr int DP = L4 + 1;                 // padded LDS row of the data slice (float4)
+  extern __shared__ float4 kd_lds4[];
+  char* lds = reinterpret_cast<char*>(kd_lds4);
+  const KdLds LL = kd_lds_layout(a.T, SW);
+  float4* dat = reinterpret_cast<float4*>(lds + LL.dat);
+  int* ent_t = reinterpret_cast<int*>(lds + LL.ent_t);
+  int* ent_w = reinterpret_cast<int*>(lds + LL.ent_w);        // float bits
+  int* ent_row = reinterpret_cast<int*>(lds + LL.ent_row);
+  int* seg_beg = reinterpret_cast<int*>(lds + LL.seg_beg);
+  int* seg_item = reinterpret_cast<int*>(lds + LL.seg_item);
+  int* short_seg = reinterpret_cast<int*>(lds + LL.short_seg);
+  int* items = reinterpret_cast<int*>(lds + LL.items);
+  float4* part = reinterpret_cast<float4*>(lds + LL.part);
+  float* part_c = reinterpret_cast<float*>(lds + LL.part_c);
+  int* red = reinterpret_cast<int*>(lds + LL.red);            // [4][kKdWaves]
+
+  // ---- which (unit, list, slice, group)
+  const int sg_bits = a.kd_sg_bits;
+  const int combos = a.kd_sv + 2 * a.kd_sk;
+  const int item = unit_affine_item(blockIdx.x, a.U, combos << sg_bits);
+  const int u = fast_div(item, a.kd_div_pu);
+  const int rest = item - u * (combos << sg_bits);
+  const int combo = rest >> sg_bits;
+  const int grp = rest & ((1 << sg_bits) - 1);
+  int list = 0, slice = combo;
+  if (combo >= a.kd_sv) {
+    const int c2 = combo - a.kd_sv;
+    const int hk = fast_div(c2, a.kd_div_sk);
+    list = 1 + hk;
+    slice = c2 - hk * a.kd_sk;
   }
-  task_prefix<W>(a, r_lo, r_hi, pref, nlong, nshort, offs, wtot);
-  const int t_end = pref[r_hi];
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
-  const int P = a.P;
+  const int width4 = (list == 0 ? a.dv : a.half) >> 2;   // float4 per row
+  const int col4 = slice * L4;                              // first float4 column of the slice
+  const int b = fast_div(u, a.div_H), hh = u - b * a.H;
+  const int T = a.T, P = a.P;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int c4 = lane & (L4 - 1), pg = lane / L4;
+  const bool col_ok = col4 + c4 < width4;
+  const int64_t lbase = ((int64_t)list * a.U + u) * P;
+
+  // ---- this group's run of entries: regions [r0, r0 + RG) (wave 0)
+  const int RG = a.regions >> sg_bits;
+  const int r0 = grp * RG;
+  if (wave == 0) {
+    int4 kd = make_int4(0, 0, 0, 0);
+    if (lane < RG) kd = a.kinds[((int64_t)list * a.U + u) * a.regions + r0 + lane];
+    const int ent = wave_sum(lane < RG ? kd.w : 0);
+    if (lane == 0) {
+      red[3 * kKdWaves] = kd.z;          // lane 0: the first region's offset
+      red[3 * kKdWaves + 1] = ent;
+    }
+  }
+
+  // ---- stage the slice of every token's data row (g_t for V, the query
+  // half for K); columns past the row read zero.  Indices past the data
+  // re-read an entry in range and are masked, so every load goes out at once.
+  {
+    constexpr int kMax = kKdDataBytes / 16 / kKdThreads;   // float4 per thread at most
+    float4 v[kMax];
+#pragma unroll
+    for (int j = 0; j < kMax; ++j) {
+      const int idx = tid + j * kKdThreads;
+      const int t = min(idx / L4, T - 1), cc = idx & (L4 - 1);
+      const int c = min(col4 + cc, width4 - 1);
+      const float4* src = list == 0
+          ? reinterpret_cast<const float4*>(a.g + ((int64_t)u * T + t) * a.dv)
+          : reinterpret_cast<const float4*>(a.q + ((int64_t)(b * T + t) * a.H + hh) * a.dqk +
+                                            (list - 1) * a.half);
+      v[j] = src[c];
+      const unsigned int mk = opaque_mask(col4 + cc < width4);
+      v[j] = make_float4(__uint_as_float(__float_as_uint(v[j].x) & mk),
+                         __uint_as_float(__float_as_uint(v[j].y) & mk),
+                         __uint_as_float(__float_as_uint(v[j].z) & mk),
+                         __uint_as_float(__float_as_uint(v[j].w) & mk));
+    }
+#pragma unroll
+    for (int j = 0; j < kMax; ++j) {
+      const int idx = tid + j * kKdThreads;
+      if (idx / L4 < T) dat[(idx / L4) * DP + (idx & (L4 - 1))] = v[j];
+    }
+  }
+  __syncthreads();
+  const int e_first = red[3 * kKdWaves], e_count = red[3 * kKdWaves + 1];
   const float lr = a.lr;
+  const bool idw_key = list != 0 && a.mode == 0;
+  const int* erow = a.ent_row + lbase + e_first;
+  const int2* etw = a.ent_tw + lbase + e_first;
+  float* tbase = list == 0
+      ? a.v + (int64_t)b * a.stride_v + (int64_t)hh * a.n * a.n * a.dv
+      : (list == 1 ? a.k1 : a.k2) + (int64_t)b * a.stride_k + (int64_t)hh * a.n * a.half;
+  const int rstride = list == 0 ? a.dv : a.half;
 
-  for (int task = t_first; task < t_end; task += t_step) {
-    const int lo = find_region(pref, r_lo, r_hi, task);   // region (position) holding this task
-    const int j = task - pref[lo];
-    const int lu = region_at(lo, a) >> a.region_bits;   // list * U + unit
-    const int list = fast_div(lu, a.div_U);
-    const int u = lu - list * a.U;
-    const int b = fast_div(u, a.div_H), hh = u - b * a.H;
-    const int64_t lbase = (int64_t)lu * P;
-    const int nl = nlong[lo];
-    const bool is_long = j < nl;
-    int4 rec;
-    if (is_long) {
-      rec = a.long_rec[lbase + offs[lo] + j];
-    } else {
-      const int si = (j - nl) * W + wave;
-      if (si >= nshort[lo]) continue;                              // no barrier on this path
-      rec = a.short_rec[lbase + offs[lo] + si];
-    }
-    const int row = rec.x, cnt = rec.z;
-    int p0 = rec.y, np = cnt;
-    if (is_long) {
-      const int ql = (cnt + W - 1) / W;
-      const int r0 = min(cnt, wave * ql);
-      np = min(cnt, r0 + ql) - r0;
-      p0 += r0;
-    }
-    const int* pay = a.pay + lbase + p0;
-    const bool finisher = !is_long || wave == 0;
-
-    float4* trow;
-    int width4;
-    float4 old[R], acc[R];
+  for (int done = 0; done < e_count;) {             // block-uniform
+    const int n = min(kKdEntCap, e_count - done);
+    const bool last = done + n == e_count;
+    // ---- the batch's entries, and the row after it (if any)
+    {
+      int rv[kKdPer];
+      int2 tw[kKdPer];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (list == 0) {
-      width4 = a.dv >> 2;
-      trow = reinterpret_cast<float4*>(
-          a.v + (int64_t)b * a.stride_v + ((int64_t)hh * a.n * a.n + row) * a.dv);
-      // every wave loads the row (used by the finisher only), beside the pairs
-      if (np <= 0) load_row<R>(trow, width4, old);
-      sum_value_pairs<R, NB>(a, u, pay, np, trow, width4, old, acc);
-    } else {
-      const int h = list - 1;
-      width4 = a.half >> 2;
-      trow = reinterpret_cast<float4*>(
-          (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k + ((int64_t)hh * a.n + row) * a.half);
-      if (np <= 0) load_row<R>(trow, width4, old);
-      sum_key_pairs<R, NB>(a, u, h, pay, np, trow, width4, old, acc);
-    }
-
-    if (is_long) {
-      // combine the W pieces in wave order
+      for (int j = 0; j < kKdPer; ++j) {
+        const int e = min(tid + j * kKdThreads, n - 1);
+        rv[j] = erow[done + e];
+        tw[j] = etw[done + e];
+      }
+      const int after = erow[done + (last ? n - 1 : n)];   // the row after the batch
 #pragma unroll
-      for (int r = 0; r < R; ++r) parts[wave * kWave * R + lane + 64 * r] = acc[r];
+      for (int j = 0; j < kKdPer; ++j) {
+        const int e = tid + j * kKdThreads;
+        if (e < n) {
+          ent_row[e] = rv[j];
+          ent_t[e] = tw[j].x;
+          ent_w[e] = tw[j].y;
+        }
+      }
+      if (tid == 0) ent_row[n] = last ? -1 : after;
+    }
+    __syncthreads();
+    // ---- segments: heads of runs of one row.  Unless this is the last
+    // batch, it ends at its last head (a segment is at most one pair per
+    // token, shorter than a batch, so one exists past entry 0).
+    int cut = n;
+    if (!last) {
+      int hmax = 0;
+#pragma unroll
+      for (int j = 0; j < kKdPer; ++j) {
+        const int e = tid + j * kKdThreads + 1;          // heads in (0, n]
+        if (e <= n && ent_row[e] != ent_row[e - 1]) hmax = max(hmax, e);
+      }
+      hmax = max(hmax, xor_lane<32>(hmax));
+      hmax = max(hmax, xor_lane<16>(hmax));
+      hmax = max(hmax, xor_lane<8>(hmax));
+      hmax = max(hmax, xor_lane<4>(hmax));
+      hmax = max(hmax, xor_lane<2>(hmax));
+      hmax = max(hmax, xor_lane<1>(hmax));
+      if (lane == 0) red[kKdWaves + wave] = hmax;
       __syncthreads();
-      if (wave == 0) {
+      cut = 0;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float4 x = parts[lane + 64 * r];
-          for (int w = 1; w < W; ++w) {
-            const float4 y = parts[w * kWave * R + lane + 64 * r];
-            x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+      for (int w = 0; w < kKdWaves; ++w) cut = max(cut, red[kKdWaves + w]);
+    }
+    // entries tid * kKdPer + j: contiguous per thread, so segment starts
+    // come out in order from one scan
+    bool hd[kKdPer];
+    int nh = 0;
+#pragma unroll
+    for (int j = 0; j < kKdPer; ++j) {
+      const int e = tid * kKdPer + j;
+      hd[j] = e < cut && (e == 0 || ent_row[e] != ent_row[e - 1]);
+      nh += hd[j];
+    }
+    int nseg;
+    int sp = kd_block_scan(nh, red, &nseg);
+#pragma unroll
+    for (int j = 0; j < kKdPer; ++j)
+      if (hd[j]) seg_beg[sp++] = tid * kKdPer + j;
+    if (tid == 0) seg_beg[nseg] = cut;
+    __syncthreads();
+    // ---- work.  A segment of at most L4 pairs is short: PG of them share
+    // one pass of a wave, one per pair group.  A longer segment is cut into
+    // kKdPiece-pair pieces, each summed by a whole wave; the pieces of a
+    // segment longer than kKdPiece meet in `part`.
+    {
+      constexpr int PG = kWave / L4;
+      int sh[kKdPer], pcs[kKdPer], slt[kKdPer], tot = 0;
+#pragma unroll
+      for (int j = 0; j < kKdPer; ++j) {
+        const int si = tid * kKdPer + j;
+        const int len = si < nseg ? seg_beg[si + 1] - seg_beg[si] : 0;
+        sh[j] = si < nseg && len <= L4 ? 1 : 0;
+        pcs[j] = len > L4 ? (len + kKdPiece - 1) / kKdPiece : 0;
+        slt[j] = len > kKdPiece ? pcs[j] : 0;
+        tot += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
+      }
+      int total;
+      int pre = kd_block_scan(tot, red + 2 * kKdWaves, &total);
+#pragma unroll
+      for (int j = 0; j < kKdPer; ++j) {
+        const int si = tid * kKdPer + j;
+        if (si < nseg) {
+          seg_item[si] = pre;          // short index | first piece << 12 | first slot << 22
+          if (sh[j]) short_seg[pre & 0xfff] = si;
+          for (int q = 0; q < pcs[j]; ++q) items[((pre >> 12) & 0x3ff) + q] = (si << 5) | q;
+        }
+        pre += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
+      }
+      __syncthreads();
+      const int nshort = total & 0xfff;
+      const int npieces = (total >> 12) & 0x3ff;
+      const int npass = (nshort + PG - 1) / PG;
+
+      // ---- short segments: pass i takes segments i*PG .. i*PG + PG - 1,
+      // pair group g the g-th; lane g*L4 + j holds pair j of its segment.
+      // Waves take passes wave, wave + W, ...; each lane fetches its own
+      // segment's old row value ahead, KS passes per round (unrolled, so no
+      // loop head between the prefetch and its use waits for the loads).
+      constexpr int KS = 4;
+      for (int j0 = 0; wave + j0 * kKdWaves < npass; j0 += KS) {
+        float4 old[KS];
+#pragma unroll
+        for (int r = 0; r < KS; ++r) {
+          const int pi = min(wave + (j0 + r) * kKdWaves, npass - 1);
+          const int s0 = seg_beg[short_seg[min(pi * PG + pg, nshort - 1)]];
+          old[r] = reinterpret_cast<const float4*>(tbase + (int64_t)ent_row[s0] * rstride)[min(col4 + c4, width4 - 1)];
+        }
+#pragma unroll
+        for (int r = 0; r < KS; ++r) {
+          const int pi = wave + (j0 + r) * kKdWaves;
+          if (pi >= npass) break;                                  // wave-uniform
+          const int sidx = pi * PG + pg;
+          const bool has = sidx < nshort;
+          const int si = short_seg[min(sidx, nshort - 1)];
+          const int s0 = seg_beg[si];
+          const int len = has ? seg_beg[si + 1] - s0 : 0;
+          const int my_t = ent_t[s0 + min(c4, max(len - 1, 0))];
+          const int my_w = c4 < len ? ent_w[s0 + c4] : 0;
+          int steps = len;
+          if constexpr (L4 <= 4) steps = max(steps, xor_lane<4>(steps));
+          if constexpr (L4 <= 8) steps = max(steps, xor_lane<8>(steps));
+          if constexpr (L4 <= 16) steps = max(steps, xor_lane<16>(steps));
+          steps = __builtin_amdgcn_readfirstlane(max(steps, xor_lane<32>(steps)));
+          float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+          float cs = 0.f;
+          sum_steps<L4, 0>(steps, my_t, my_w, dat, c4, acc, cs);
+          if (r == 0) {
+            // every prefetched value is taken in before the round's first
+            // store: a later wait for one of them would otherwise also wait
+            // for the stores issued since (one counter covers both)
+#pragma unroll
+            for (int rr = 0; rr < KS; ++rr)
+              asm volatile("" :: "v"(old[rr].x), "v"(old[rr].y), "v"(old[rr].z), "v"(old[rr].w));
           }
-          acc[r] = x;
+          if (has && col_ok) {
+            float4 x = old[r];
+            const float inv = __builtin_amdgcn_rcpf((float)len);
+            if (idw_key) {
+              acc.x = fmaf(-cs, x.x, acc.x); acc.y = fmaf(-cs, x.y, acc.y);
+              acc.z = fmaf(-cs, x.z, acc.z); acc.w = fmaf(-cs, x.w, acc.w);
+            }
+            x.x -= lr * (acc.x * inv); x.y -= lr * (acc.y * inv);
+            x.z -= lr * (acc.z * inv); x.w -= lr * (acc.w * inv);
+            reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride)[col4 + c4] = x;
+          }
         }
       }
-    }
-    if (finisher) {
-      const float inv = 1.0f / (float)cnt;
+
+      // ---- pieces of longer segments, continuing the waves' turns: lane
+      // g*L4 + j holds pair j*PG + g of the piece, pair groups are added by a
+      // butterfly.  A one-piece segment is finished by lane group jj of its
+      // round, whose prefetch register r holds its old row value.
+      constexpr int KP = PG >= 16 ? 1 : kKdPrefetch;
+      constexpr int R = KP * PG;
+      const int w0 = (wave - npass % kKdWaves + kKdWaves) % kKdWaves;
+      for (int j0 = 0; w0 + j0 * kKdWaves < npieces; j0 += R) {
+        float4 old[KP];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int c = lane + 64 * r;
-        if (c < width4) {
-          float4 x = old[r];
-          x.x -= lr * (acc[r].x * inv); x.y -= lr * (acc[r].y * inv);
-          x.z -= lr * (acc[r].z * inv); x.w -= lr * (acc[r].w * inv);
-          trow[c] = x;
+        for (int r = 0; r < KP; ++r) {
+          const int it = min(w0 + (j0 + r * PG + pg) * kKdWaves, npieces - 1);
+          const int s0 = seg_beg[items[it] >> 5];
+          old[r] = reinterpret_cast<const float4*>(tbase + (int64_t)ent_row[s0] * rstride)[min(col4 + c4, width4 - 1)];
+        }
+#pragma unroll
+        for (int r = 0; r < KP; ++r) {
+#pragma unroll
+          for (int jj = 0; jj < PG; ++jj) {
+            const int it = w0 + (j0 + r * PG + jj) * kKdWaves;
+            if (it >= npieces) break;                              // wave-uniform
+            const int packed = items[it];
+            const int si = packed >> 5, q = packed & 31;
+            const int s0 = seg_beg[si];
+            const int len = __builtin_amdgcn_readfirstlane(seg_beg[si + 1] - s0);
+            const int e0 = s0 + q * kKdPiece;
+            const int np = min(kKdPiece, len - q * kKdPiece);
+            const int pj = c4 * PG + pg;
+            const int my_t = ent_t[e0 + min(pj, np - 1)];
+            const int my_w = pj < np ? ent_w[e0 + pj] : 0;
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            float cs = 0.f;
+            sum_steps<L4, 0>((np + PG - 1) / PG, my_t, my_w, dat, c4, acc, cs);
+            pair_group_sum<L4>(acc, cs);
+            if (r == 0 && jj == 0) {
+#pragma unroll
+              for (int rr = 0; rr < KP; ++rr)
+                asm volatile("" :: "v"(old[rr].x), "v"(old[rr].y), "v"(old[rr].z), "v"(old[rr].w));
+            }
+            if (len <= kKdPiece) {
+              if (pg == jj && col_ok) {
+                float4 x = old[r];
+                const float inv = __builtin_amdgcn_rcpf((float)len);
+                if (idw_key) {
+                  acc.x = fmaf(-cs, x.x, acc.x); acc.y = fmaf(-cs, x.y, acc.y);
+                  acc.z = fmaf(-cs, x.z, acc.z); acc.w = fmaf(-cs, x.w, acc.w);
+                }
+                x.x -= lr * (acc.x * inv); x.y -= lr * (acc.y * inv);
+                x.z -= lr * (acc.z * inv); x.w -= lr * (acc.w * inv);
+                reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride)[col4 + c4] = x;
+              }
+            } else {
+              const int slot = (seg_item[si] >> 22) + q;
+              if (pg == 0) part[slot * L4 + c4] = acc;
+              if (lane == 0) part_c[slot] = cs;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // ---- long segments: add the pieces in order and finish the row
+      for (int si = wave; si < nseg; si += kKdWaves) {
+        const int s0 = seg_beg[si];
+        const int len = seg_beg[si + 1] - s0;
+        if (len <= kKdPiece) continue;
+        const int pieces = (len + kKdPiece - 1) / kKdPiece;
+        const int slot0 = seg_item[si] >> 22;
+        if (lane < L4 && col_ok) {
+          float4* trow = reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride) + col4 + c4;
+          float4 x = *trow;
+          float4 acc = part[slot0 * L4 + c4];
+          float cs = part_c[slot0];
+          for (int q = 1; q < pieces; ++q) {
+            acc = f4_add(acc, part[(slot0 + q) * L4 + c4]);
+            cs += part_c[slot0 + q];
+          }
+          const float inv = __builtin_amdgcn_rcpf((float)len);
+          if (idw_key) {
+            acc.x = fmaf(-cs, x.x, acc.x); acc.y = fmaf(-cs, x.y, acc.y);
+            acc.z = fmaf(-cs, x.z, acc.z); acc.w = fmaf(-cs, x.w, acc.w);
+          }
+          x.x -= lr * (acc.x * inv); x.y -= lr * (acc.y * inv);
+          x.z -= lr * (acc.z * inv); x.w -= lr * (acc.w * inv);
+          *trow = x;
         }
       }
     }
-    if (is_long) __syncthreads();   // parts[] is reused by the next task
+    done += cut;
+    __syncthreads();                 // the staged entries are reused
   }
 }
 
 namespace {
 
-int device_cus() {
-  static const int cus = [] {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    return n;
-  }();
-  return cus;
-}
-
-template <int R, int W, int NB>
+template <int SW>
 hipError_t launch_kd_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
-  const int64_t L = (int64_t)3 * a.U * a.regions;
-  const size_t smem = kd_parts_bytes<R, W>() + sizeof(int) * (size_t)(4 * L + 1 + W);
+  const int smem = kd_lds_layout(a.T, SW).total;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&kd_update<R, W, NB>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)(kd_parts_bytes<R, W>() + sizeof(int) * (size_t)(4 * kUpdMaxLists + 1 + W)));
+      reinterpret_cast<const void*>(&kd_update<SW>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      kd_lds_layout(kKdDataBytes / (SW * 4), SW).total);
   if (attr != hipSuccess) return attr;
-  // tasks cannot exceed long segments + short groups of W, per region; more
-  // workgroups than fit on the device at once would only queue behind the
-  // first ones, so the grid stops at what is resident (tasks loop)
-  const int64_t most = (int64_t)3 * a.U * a.P / (kShortSeg + 1) +
-                       (int64_t)3 * a.U * a.P / W + L;
-  const int64_t resident = (int64_t)kKdResidentPerCu * device_cus();
-  int64_t gx = most < resident ? most : resident;
-  if (a.U % kXcds == 0) gx = (gx + kXcds - 1) / kXcds * kXcds;   // whole rounds over the XCDs
-  return fw_launch(kd_update<R, W, NB>, dim3((unsigned)gx), dim3(W * kWave), (uint32_t)smem, s, tm, a);
+  const int64_t per_unit = (int64_t)(a.kd_sv + 2 * a.kd_sk) << a.kd_sg_bits;
+  return fw_launch(kd_update<SW>, dim3((unsigned)(per_unit * a.U)), dim3(kKdThreads), (uint32_t)smem,
+                   s, tm, a);
 }
 
 }  // namespace
 
 hipError_t launch_kd(const ChunkArgs& args, hipStream_t s, const LaunchTiming* tm) {
-  const ChunkArgs a = with_divisors(args);
-  const int r = (a.pw / 4 + 63) / 64;
-  // (float4 per lane per row, waves, rows in flight): the largest of each
-  // that keeps two workgroups per compute unit without register spills
-  if (r <= 1) return launch_kd_as<1, 16, 4>(a, s, tm);
-  if (r <= 2) return launch_kd_as<2, 8, 8>(a, s, tm);
-  if (r <= 4) return launch_kd_as<4, 4, 4>(a, s, tm);
-  return launch_kd_as<8, 4, 2>(a, s, tm);
+  ChunkArgs a = with_divisors(args);
+  // the widest column slice whose data for every token fits kKdDataBytes
+  const int sw = a.T * 64 * 4 <= kKdDataBytes ? 64 : (a.T * 32 * 4 <= kKdDataBytes ? 32 : 16);
+  a.kd_sv = (a.dv + sw - 1) / sw;
+  a.kd_sk = (a.half + sw - 1) / sw;
+  const int combos = a.kd_sv + 2 * a.kd_sk;
+  // groups of hash regions: about one workgroup per compute unit in all
+  int sg = 1, bits = 0;
+  while (sg * 2 <= a.regions && (int64_t)a.U * combos * sg * 2 <= 256) { sg *= 2; ++bits; }
+  a.kd_sg_bits = bits;
+  a.kd_div_pu = make_fastdiv(combos << bits);
+  a.kd_div_sk = make_fastdiv(a.kd_sk);
+  if (sw == 64) return launch_kd_as<64>(a, s, tm);
+  if (sw == 32) return launch_kd_as<32>(a, s, tm);
+  return launch_kd_as<16>(a, s, tm);
 }
 
 }  // namespace fwpkm
