@@ -623,7 +623,8 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
       if ((e = timed(h, prof, 6, [&](const LaunchTiming* tm) { return fwpkm::launch_ke_grad(a, stream, tm); })) != hipSuccess)
         return fail(FWPKM_ERR_HIP, "addressing gradient kernel: %s", hipGetErrorString(e));
     }
-    if ((e = timed(h, prof, 2, [&](const LaunchTiming* tm) { return fwpkm::launch_kc(a, stream, tm); })) != hipSuccess)
+    if (!fwpkm::kd_fuses_grouping(a) &&
+        (e = timed(h, prof, 2, [&](const LaunchTiming* tm) { return fwpkm::launch_kc(a, stream, tm); })) != hipSuccess)
       return fail(FWPKM_ERR_HIP, "sort kernel: %s", hipGetErrorString(e));
     if ((e = timed(h, prof, 3, [&](const LaunchTiming* tm) { return fwpkm::launch_kd(a, stream, tm); })) != hipSuccess)
       return fail(FWPKM_ERR_HIP, "update kernel: %s", hipGetErrorString(e));

@@ -55,6 +55,9 @@ hipError_t launch_kf_project(const SeqArgs& s, hipStream_t st, const LaunchTimin
 hipError_t launch_kf_gate(const SeqArgs& s, hipStream_t st, const LaunchTiming* tm);
 
 // KD: per segment mean gradient and in-place SGD on V, K1 and K2 rows.
+// When kd_fuses_grouping(a) (at most 2048 pairs per unit) the update kernel
+// groups the rows itself and KC must not be launched.
+bool kd_fuses_grouping(const ChunkArgs& a);
 hipError_t launch_kd(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm);
 
 }  // namespace fwpkm

@@ -25,14 +25,22 @@
 // many compute units as its list has slices, and each pair costs an LDS read
 // instead of a dependent global load.
 //
-// The grouping kernel leaves, per (list, unit), the kept entries sorted by
-// row, each with its token and weight (coefficient), regions one after
-// another; a group of consecutive regions is one contiguous run of entries,
-// whose segments (runs of one row) this kernel finds itself.  A workgroup
-// thus needs two dependent global rounds (region offsets, then entries)
-// before it can sum.  Each wave takes work items in turn: a segment of at
-// most kKdPiece pairs, or one kKdPiece-pair piece of a longer segment (the
-// pieces' partial sums meet in LDS and are added in piece order).  Inside a
+// Grouping.  With at most kKdEntCap pairs per unit (kd_write), the
+// workgroup groups its rows itself: in the same round as its data slice it
+// loads the list's row keys and weights (coefficients), keeps the rows of
+// its hash group in pair order, and sorts them stably by row with an LSD
+// radix sort in LDS (8-bit digits, ballot ranking), so a row's pairs stay in
+// ascending token order.  The sort is repeated by the column slices of one
+// group, which is cheaper than a separate grouping launch and its dependent
+// global rounds.  Larger chunks (kd_update) read the grouping kernel's
+// output instead: per (list, unit), the kept entries sorted by row, each
+// with its token and weight, regions one after another, so a group of
+// consecutive regions is one contiguous run of entries, taken in batches
+// cut at segment heads.  Either way the segments (runs of one row) are
+// found here.  Work items: a segment of at most SW/4 pairs is short, and
+// 256/SW of them share a wave pass, one per pair group; a longer segment is
+// cut into kKdPiece-pair pieces, each summed by a whole wave (the pieces'
+// partial sums meet in LDS and are added in piece order).  Inside a
 // wave the lanes form SW/4 float4 columns times 256/SW pair groups; lane l
 // holds the token and weight of one pair, pair group g sums pairs g,
 // g + groups, ... as DPP broadcasts hand them over (only as many steps as the
@@ -171,12 +179,334 @@ __device__ __forceinline__ void sum_steps(int steps, int my_t, int my_w, const f
   }
 }
 
+
+// Radix digit ranking: lanes of this wave holding the same 8-bit digit
+// (among `valid` lanes).
+__device__ __forceinline__ unsigned long long digit_peers(int d, bool valid) {
+  unsigned long long peers = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const unsigned long long on = __ballot((d >> bit) & 1);
+    peers &= ((d >> bit) & 1) ? on : ~on;
+  }
+  return peers;
+}
+
+__device__ __forceinline__ unsigned long long lanes_below() {
+  return (1ull << lane_id()) - 1ull;
+}
+
+// Hash group of a row among 2^bits: multiplicative (Fibonacci) hashing, so
+// rows that many tokens share spread over the groups.
+__device__ __forceinline__ int hash_group(int row, int bits) {
+  return bits == 0 ? 0 : (int)(((unsigned)row * 0x9E3779B1u) >> (32 - bits));
+}
+
+// Which (unit, list, column slice, hash group) an update workgroup owns.
+struct KdWho {
+  int u, list, slice, grp, b, hh, width4, col4;
+};
+
+__device__ __forceinline__ KdWho kd_who(const ChunkArgs& a, int L4) {
+  KdWho w;
+  const int sg_bits = a.kd_sg_bits;
+  const int combos = a.kd_sv + 2 * a.kd_sk;
+  const int item = unit_affine_item(blockIdx.x, a.U, combos << sg_bits);
+  w.u = fast_div(item, a.kd_div_pu);
+  const int rest = item - w.u * (combos << sg_bits);
+  const int combo = rest >> sg_bits;
+  w.grp = rest & ((1 << sg_bits) - 1);
+  w.list = 0;
+  w.slice = combo;
+  if (combo >= a.kd_sv) {
+    const int c2 = combo - a.kd_sv;
+    const int hk = fast_div(c2, a.kd_div_sk);
+    w.list = 1 + hk;
+    w.slice = c2 - hk * a.kd_sk;
+  }
+  w.width4 = (w.list == 0 ? a.dv : a.half) >> 2;   // float4 per row
+  w.col4 = w.slice * L4;                             // first float4 column of the slice
+  w.b = fast_div(w.u, a.div_H);
+  w.hh = w.u - w.b * a.H;
+  return w;
+}
+
+// The slice of every token's data row (g_t for V, the query half for K):
+// loads issued (into v) by kd_stage_load, stored by kd_stage_store.
+// Columns past the row read zero; indices past the data re-read an entry in
+// range and are masked, so every load goes out at once.
+constexpr int kKdStageMax = kKdDataBytes / 16 / kKdThreads;   // float4 per thread at most
+
+template <int L4>
+__device__ __forceinline__ void kd_stage_load(const ChunkArgs& a, const KdWho& w, float4 (&v)[kKdStageMax]) {
+  const int T = a.T, tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kKdStageMax; ++j) {
+    const int idx = tid + j * kKdThreads;
+    const int t = min(idx / L4, T - 1), cc = idx & (L4 - 1);
+    const int c = min(w.col4 + cc, w.width4 - 1);
+    const float4* src = w.list == 0
+        ? reinterpret_cast<const float4*>(a.g + ((int64_t)w.u * T + t) * a.dv)
+        : reinterpret_cast<const float4*>(a.q + ((int64_t)(w.b * T + t) * a.H + w.hh) * a.dqk +
+                                          (w.list - 1) * a.half);
+    v[j] = src[c];
+    const unsigned int mk = opaque_mask(w.col4 + cc < w.width4);
+    v[j] = make_float4(__uint_as_float(__float_as_uint(v[j].x) & mk),
+                       __uint_as_float(__float_as_uint(v[j].y) & mk),
+                       __uint_as_float(__float_as_uint(v[j].z) & mk),
+                       __uint_as_float(__float_as_uint(v[j].w) & mk));
+  }
+}
+
+template <int L4>
+__device__ __forceinline__ void kd_stage_store(int T, const float4 (&v)[kKdStageMax], float4* dat) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kKdStageMax; ++j) {
+    const int idx = tid + j * kKdThreads;
+    if (idx / L4 < T) dat[(idx / L4) * (L4 + 1) + (idx & (L4 - 1))] = v[j];
+  }
+}
+
+// LDS scratch of the segment sums.
+struct KdSeg {
+  int* seg_beg;     // [cut + 1] segment starts, then the end
+  int* seg_item;    // [cut] short index | first piece << 12 | first slot << 22
+  int* short_seg;   // [cut] short segments in order
+  int* items;       // [kKdMaxPieces] pieces of longer segments: segment << 5 | piece
+  float4* part;     // [kKdMaxLong][L4] partial sums of pieces
+  float* part_c;    // [kKdMaxLong] their coefficient sums
+  int* red;         // [4 * kKdWaves] block-scan scratch
+};
+
+// The segments (runs of one row) of the entries [0, cut), sorted by row, in
+// LDS: rows ent_row, tokens ent_t, weights ent_w (float bits); each row's
+// mean gradient is applied to its slice of the table.  cut <= kKdEntCap.
+// Ends after a barrier-free phase: the caller synchronises before reusing
+// the scratch.
+template <int L4>
+__device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho& who,
+                                                const float4* dat, const int* ent_row,
+                                                const int* ent_t, const int* ent_w, int cut,
+                                                const KdSeg& S) {
+  int* seg_beg = S.seg_beg;
+  int* seg_item = S.seg_item;
+  int* short_seg = S.short_seg;
+  int* items = S.items;
+  float4* part = S.part;
+  float* part_c = S.part_c;
+  int* red = S.red;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int c4 = lane & (L4 - 1), pg = lane / L4;
+  const int width4 = who.width4, col4 = who.col4;
+  const bool col_ok = col4 + c4 < width4;
+  const float lr = a.lr;
+  const bool idw_key = who.list != 0 && a.mode == 0;
+  float* tbase = who.list == 0
+      ? a.v + (int64_t)who.b * a.stride_v + (int64_t)who.hh * a.n * a.n * a.dv
+      : (who.list == 1 ? a.k1 : a.k2) + (int64_t)who.b * a.stride_k + (int64_t)who.hh * a.n * a.half;
+  const int rstride = who.list == 0 ? a.dv : a.half;
+
+  // entries tid * kKdPer + j: contiguous per thread, so segment starts
+  // come out in order from one scan
+  bool hd[kKdPer];
+  int nh = 0;
+#pragma unroll
+  for (int j = 0; j < kKdPer; ++j) {
+    const int e = tid * kKdPer + j;
+    hd[j] = e < cut && (e == 0 || ent_row[e] != ent_row[e - 1]);
+    nh += hd[j];
+  }
+  int nseg;
+  int sp = kd_block_scan(nh, red, &nseg);
+#pragma unroll
+  for (int j = 0; j < kKdPer; ++j)
+    if (hd[j]) seg_beg[sp++] = tid * kKdPer + j;
+  if (tid == 0) seg_beg[nseg] = cut;
+  __syncthreads();
+  // ---- work.  A segment of at most L4 pairs is short: PG of them share
+  // one pass of a wave, one per pair group.  A longer segment is cut into
+  // kKdPiece-pair pieces, each summed by a whole wave; the pieces of a
+  // segment longer than kKdPiece meet in `part`.
+  {
+    constexpr int PG = kWave / L4;
+    int sh[kKdPer], pcs[kKdPer], slt[kKdPer], tot = 0;
+#pragma unroll
+    for (int j = 0; j < kKdPer; ++j) {
+      const int si = tid * kKdPer + j;
+      const int len = si < nseg ? seg_beg[si + 1] - seg_beg[si] : 0;
+      sh[j] = si < nseg && len <= L4 ? 1 : 0;
+      pcs[j] = len > L4 ? (len + kKdPiece - 1) / kKdPiece : 0;
+      slt[j] = len > kKdPiece ? pcs[j] : 0;
+      tot += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
+    }
+    int total;
+    int pre = kd_block_scan(tot, red + 2 * kKdWaves, &total);
+#pragma unroll
+    for (int j = 0; j < kKdPer; ++j) {
+      const int si = tid * kKdPer + j;
+      if (si < nseg) {
+        seg_item[si] = pre;          // short index | first piece << 12 | first slot << 22
+        if (sh[j]) short_seg[pre & 0xfff] = si;
+        for (int q = 0; q < pcs[j]; ++q) items[((pre >> 12) & 0x3ff) + q] = (si << 5) | q;
+      }
+      pre += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
+    }
+    __syncthreads();
+    const int nshort = total & 0xfff;
+    const int npieces = (total >> 12) & 0x3ff;
+    const int npass = (nshort + PG - 1) / PG;
+
+    // ---- short segments: pass i takes segments i*PG .. i*PG + PG - 1,
+    // pair group g the g-th; lane g*L4 + j holds pair j of its segment.
+    // Waves take passes wave, wave + W, ...; each lane fetches its own
+    // segment's old row value ahead, KS passes per round (unrolled, so no
+    // loop head between the prefetch and its use waits for the loads).
+    constexpr int KS = 4;
+    for (int j0 = 0; wave + j0 * kKdWaves < npass; j0 += KS) {
+      float4 old[KS];
+#pragma unroll
+      for (int r = 0; r < KS; ++r) {
+        const int pi = min(wave + (j0 + r) * kKdWaves, npass - 1);
+        const int s0 = seg_beg[short_seg[min(pi * PG + pg, nshort - 1)]];
+        old[r] = reinterpret_cast<const float4*>(tbase + (int64_t)ent_row[s0] * rstride)[min(col4 + c4, width4 - 1)];
+      }
+#pragma unroll
+      for (int r = 0; r < KS; ++r) {
+        const int pi = wave + (j0 + r) * kKdWaves;
+        if (pi >= npass) break;                                  // wave-uniform
+        const int sidx = pi * PG + pg;
+        const bool has = sidx < nshort;
+        const int si = short_seg[min(sidx, nshort - 1)];
+        const int s0 = seg_beg[si];
+        const int len = has ? seg_beg[si + 1] - s0 : 0;
+        const int my_t = ent_t[s0 + min(c4, max(len - 1, 0))];
+        const int my_w = c4 < len ? ent_w[s0 + c4] : 0;
+        int steps = len;
+        if constexpr (L4 <= 4) steps = max(steps, xor_lane<4>(steps));
+        if constexpr (L4 <= 8) steps = max(steps, xor_lane<8>(steps));
+        if constexpr (L4 <= 16) steps = max(steps, xor_lane<16>(steps));
+        steps = __builtin_amdgcn_readfirstlane(max(steps, xor_lane<32>(steps)));
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        float cs = 0.f;
+        sum_steps<L4, 0>(steps, my_t, my_w, dat, c4, acc, cs);
+        if (r == 0) {
+          // every prefetched value is taken in before the round's first
+          // store: a later wait for one of them would otherwise also wait
+          // for the stores issued since (one counter covers both)
+#pragma unroll
+          for (int rr = 0; rr < KS; ++rr)
+            asm volatile("" :: "v"(old[rr].x), "v"(old[rr].y), "v"(old[rr].z), "v"(old[rr].w));
+        }
+        if (has && col_ok) {
+          float4 x = old[r];
+          const float inv = __builtin_amdgcn_rcpf((float)len);
+          if (idw_key) {
+            acc.x = fmaf(-cs, x.x, acc.x); acc.y = fmaf(-cs, x.y, acc.y);
+            acc.z = fmaf(-cs, x.z, acc.z); acc.w = fmaf(-cs, x.w, acc.w);
+          }
+          x.x -= lr * (acc.x * inv); x.y -= lr * (acc.y * inv);
+          x.z -= lr * (acc.z * inv); x.w -= lr * (acc.w * inv);
+          reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride)[col4 + c4] = x;
+        }
+      }
+    }
+
+    // ---- pieces of longer segments, continuing the waves' turns: lane
+    // g*L4 + j holds pair j*PG + g of the piece, pair groups are added by a
+    // butterfly.  A one-piece segment is finished by lane group jj of its
+    // round, whose prefetch register r holds its old row value.
+    constexpr int KP = PG >= 16 ? 1 : kKdPrefetch;
+    constexpr int R = KP * PG;
+    const int w0 = (wave - npass % kKdWaves + kKdWaves) % kKdWaves;
+    for (int j0 = 0; w0 + j0 * kKdWaves < npieces; j0 += R) {
+      float4 old[KP];
+#pragma unroll
+      for (int r = 0; r < KP; ++r) {
+        const int it = min(w0 + (j0 + r * PG + pg) * kKdWaves, npieces - 1);
+        const int s0 = seg_beg[items[it] >> 5];
+        old[r] = reinterpret_cast<const float4*>(tbase + (int64_t)ent_row[s0] * rstride)[min(col4 + c4, width4 - 1)];
+      }
+#pragma unroll
+      for (int r = 0; r < KP; ++r) {
+#pragma unroll
+        for (int jj = 0; jj < PG; ++jj) {
+          const int it = w0 + (j0 + r * PG + jj) * kKdWaves;
+          if (it >= npieces) break;                              // wave-uniform
+          const int packed = items[it];
+          const int si = packed >> 5, q = packed & 31;
+          const int s0 = seg_beg[si];
+          const int len = __builtin_amdgcn_readfirstlane(seg_beg[si + 1] - s0);
+          const int e0 = s0 + q * kKdPiece;
+          const int np = min(kKdPiece, len - q * kKdPiece);
+          const int pj = c4 * PG + pg;
+          const int my_t = ent_t[e0 + min(pj, np - 1)];
+          const int my_w = pj < np ? ent_w[e0 + pj] : 0;
+          float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+          float cs = 0.f;
+          sum_steps<L4, 0>((np + PG - 1) / PG, my_t, my_w, dat, c4, acc, cs);
+          pair_group_sum<L4>(acc, cs);
+          if (r == 0 && jj == 0) {
+#pragma unroll
+            for (int rr = 0; rr < KP; ++rr)
+              asm volatile("" :: "v"(old[rr].x), "v"(old[rr].y), "v"(old[rr].z), "v"(old[rr].w));
+          }
+          if (len <= kKdPiece) {
+            if (pg == jj && col_ok) {
+              float4 x = old[r];
+              const float inv = __builtin_amdgcn_rcpf((float)len);
+              if (idw_key) {
+                acc.x = fmaf(-cs, x.x, acc.x); acc.y = fmaf(-cs, x.y, acc.y);
+                acc.z = fmaf(-cs, x.z, acc.z); acc.w = fmaf(-cs, x.w, acc.w);
+              }
+              x.x -= lr * (acc.x * inv); x.y -= lr * (acc.y * inv);
+              x.z -= lr * (acc.z * inv); x.w -= lr * (acc.w * inv);
+              reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride)[col4 + c4] = x;
+            }
+          } else {
+            const int slot = (seg_item[si] >> 22) + q;
+            if (pg == 0) part[slot * L4 + c4] = acc;
+            if (lane == 0) part_c[slot] = cs;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // ---- long segments: add the pieces in order and finish the row
+    for (int si = wave; si < nseg; si += kKdWaves) {
+      const int s0 = seg_beg[si];
+      const int len = seg_beg[si + 1] - s0;
+      if (len <= kKdPiece) continue;
+      const int pieces = (len + kKdPiece - 1) / kKdPiece;
+      const int slot0 = seg_item[si] >> 22;
+      if (lane < L4 && col_ok) {
+        float4* trow = reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride) + col4 + c4;
+        float4 x = *trow;
+        float4 acc = part[slot0 * L4 + c4];
+        float cs = part_c[slot0];
+        for (int q = 1; q < pieces; ++q) {
+          acc = f4_add(acc, part[(slot0 + q) * L4 + c4]);
+          cs += part_c[slot0 + q];
+        }
+        const float inv = __builtin_amdgcn_rcpf((float)len);
+        if (idw_key) {
+          acc.x = fmaf(-cs, x.x, acc.x); acc.y = fmaf(-cs, x.y, acc.y);
+          acc.z = fmaf(-cs, x.z, acc.z); acc.w = fmaf(-cs, x.w, acc.w);
+        }
+        x.x -= lr * (acc.x * inv); x.y -= lr * (acc.y * inv);
+        x.z -= lr * (acc.z * inv); x.w -= lr * (acc.w * inv);
+        *trow = x;
+      }
+    }
+  }
+}
+
 }  // namespace
 
+// Large chunks: entries grouped by the grouping kernel (kc_sort).
 template <int SW>
 __global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
   constexpr int L4 = SW / 4;                 // float4 columns of a slice
-  constexpr int DP = L4 + 1;                 // padded LDS row of the data slice (float4)
   extern __shared__ float4 kd_lds4[];
   char* lds = reinterpret_cast<char*>(kd_lds4);
   const KdLds LL = kd_lds_layout(a.T, SW);
@@ -184,89 +514,41 @@ __global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
   int* ent_t = reinterpret_cast<int*>(lds + LL.ent_t);
   int* ent_w = reinterpret_cast<int*>(lds + LL.ent_w);        // float bits
   int* ent_row = reinterpret_cast<int*>(lds + LL.ent_row);
-  int* seg_beg = reinterpret_cast<int*>(lds + LL.seg_beg);
-  int* seg_item = reinterpret_cast<int*>(lds + LL.seg_item);
-  int* short_seg = reinterpret_cast<int*>(lds + LL.short_seg);
-  int* items = reinterpret_cast<int*>(lds + LL.items);
-  float4* part = reinterpret_cast<float4*>(lds + LL.part);
-  float* part_c = reinterpret_cast<float*>(lds + LL.part_c);
-  int* red = reinterpret_cast<int*>(lds + LL.red);            // [4][kKdWaves]
+  KdSeg S;
+  S.seg_beg = reinterpret_cast<int*>(lds + LL.seg_beg);
+  S.seg_item = reinterpret_cast<int*>(lds + LL.seg_item);
+  S.short_seg = reinterpret_cast<int*>(lds + LL.short_seg);
+  S.items = reinterpret_cast<int*>(lds + LL.items);
+  S.part = reinterpret_cast<float4*>(lds + LL.part);
+  S.part_c = reinterpret_cast<float*>(lds + LL.part_c);
+  S.red = reinterpret_cast<int*>(lds + LL.red);               // [4][kKdWaves]
+  int* red = S.red;
 
-  // ---- which (unit, list, slice, group)
-  const int sg_bits = a.kd_sg_bits;
-  const int combos = a.kd_sv + 2 * a.kd_sk;
-  const int item = unit_affine_item(blockIdx.x, a.U, combos << sg_bits);
-  const int u = fast_div(item, a.kd_div_pu);
-  const int rest = item - u * (combos << sg_bits);
-  const int combo = rest >> sg_bits;
-  const int grp = rest & ((1 << sg_bits) - 1);
-  int list = 0, slice = combo;
-  if (combo >= a.kd_sv) {
-    const int c2 = combo - a.kd_sv;
-    const int hk = fast_div(c2, a.kd_div_sk);
-    list = 1 + hk;
-    slice = c2 - hk * a.kd_sk;
-  }
-  const int width4 = (list == 0 ? a.dv : a.half) >> 2;   // float4 per row
-  const int col4 = slice * L4;                              // first float4 column of the slice
-  const int b = fast_div(u, a.div_H), hh = u - b * a.H;
-  const int T = a.T, P = a.P;
+  const KdWho who = kd_who(a, L4);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int c4 = lane & (L4 - 1), pg = lane / L4;
-  const bool col_ok = col4 + c4 < width4;
-  const int64_t lbase = ((int64_t)list * a.U + u) * P;
+  const int64_t lbase = ((int64_t)who.list * a.U + who.u) * a.P;
 
   // ---- this group's run of entries: regions [r0, r0 + RG) (wave 0)
-  const int RG = a.regions >> sg_bits;
-  const int r0 = grp * RG;
+  const int RG = a.regions >> a.kd_sg_bits;
+  const int r0 = who.grp * RG;
   if (wave == 0) {
     int4 kd = make_int4(0, 0, 0, 0);
-    if (lane < RG) kd = a.kinds[((int64_t)list * a.U + u) * a.regions + r0 + lane];
+    if (lane < RG) kd = a.kinds[((int64_t)who.list * a.U + who.u) * a.regions + r0 + lane];
     const int ent = wave_sum(lane < RG ? kd.w : 0);
     if (lane == 0) {
       red[3 * kKdWaves] = kd.z;          // lane 0: the first region's offset
       red[3 * kKdWaves + 1] = ent;
     }
   }
-
-  // ---- stage the slice of every token's data row (g_t for V, the query
-  // half for K); columns past the row read zero.  Indices past the data
-  // re-read an entry in range and are masked, so every load goes out at once.
   {
-    constexpr int kMax = kKdDataBytes / 16 / kKdThreads;   // float4 per thread at most
-    float4 v[kMax];
-#pragma unroll
-    for (int j = 0; j < kMax; ++j) {
-      const int idx = tid + j * kKdThreads;
-      const int t = min(idx / L4, T - 1), cc = idx & (L4 - 1);
-      const int c = min(col4 + cc, width4 - 1);
-      const float4* src = list == 0
-          ? reinterpret_cast<const float4*>(a.g + ((int64_t)u * T + t) * a.dv)
-          : reinterpret_cast<const float4*>(a.q + ((int64_t)(b * T + t) * a.H + hh) * a.dqk +
-                                            (list - 1) * a.half);
-      v[j] = src[c];
-      const unsigned int mk = opaque_mask(col4 + cc < width4);
-      v[j] = make_float4(__uint_as_float(__float_as_uint(v[j].x) & mk),
-                         __uint_as_float(__float_as_uint(v[j].y) & mk),
-                         __uint_as_float(__float_as_uint(v[j].z) & mk),
-                         __uint_as_float(__float_as_uint(v[j].w) & mk));
-    }
-#pragma unroll
-    for (int j = 0; j < kMax; ++j) {
-      const int idx = tid + j * kKdThreads;
-      if (idx / L4 < T) dat[(idx / L4) * DP + (idx & (L4 - 1))] = v[j];
-    }
+    float4 v[kKdStageMax];
+    kd_stage_load<L4>(a, who, v);
+    kd_stage_store<L4>(a.T, v, dat);
   }
   __syncthreads();
   const int e_first = red[3 * kKdWaves], e_count = red[3 * kKdWaves + 1];
-  const float lr = a.lr;
-  const bool idw_key = list != 0 && a.mode == 0;
   const int* erow = a.ent_row + lbase + e_first;
   const int2* etw = a.ent_tw + lbase + e_first;
-  float* tbase = list == 0
-      ? a.v + (int64_t)b * a.stride_v + (int64_t)hh * a.n * a.n * a.dv
-      : (list == 1 ? a.k1 : a.k2) + (int64_t)b * a.stride_k + (int64_t)hh * a.n * a.half;
-  const int rstride = list == 0 ? a.dv : a.half;
 
   for (int done = 0; done < e_count;) {             // block-uniform
     const int n = min(kKdEntCap, e_count - done);
@@ -294,9 +576,9 @@ __global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
       if (tid == 0) ent_row[n] = last ? -1 : after;
     }
     __syncthreads();
-    // ---- segments: heads of runs of one row.  Unless this is the last
-    // batch, it ends at its last head (a segment is at most one pair per
-    // token, shorter than a batch, so one exists past entry 0).
+    // ---- unless this is the last batch, it ends at its last segment head
+    // (a segment is at most one pair per token, shorter than a batch, so one
+    // exists past entry 0)
     int cut = n;
     if (!last) {
       int hmax = 0;
@@ -317,229 +599,246 @@ __global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
 #pragma unroll
       for (int w = 0; w < kKdWaves; ++w) cut = max(cut, red[kKdWaves + w]);
     }
-    // entries tid * kKdPer + j: contiguous per thread, so segment starts
-    // come out in order from one scan
-    bool hd[kKdPer];
-    int nh = 0;
-#pragma unroll
-    for (int j = 0; j < kKdPer; ++j) {
-      const int e = tid * kKdPer + j;
-      hd[j] = e < cut && (e == 0 || ent_row[e] != ent_row[e - 1]);
-      nh += hd[j];
-    }
-    int nseg;
-    int sp = kd_block_scan(nh, red, &nseg);
-#pragma unroll
-    for (int j = 0; j < kKdPer; ++j)
-      if (hd[j]) seg_beg[sp++] = tid * kKdPer + j;
-    if (tid == 0) seg_beg[nseg] = cut;
-    __syncthreads();
-    // ---- work.  A segment of at most L4 pairs is short: PG of them share
-    // one pass of a wave, one per pair group.  A longer segment is cut into
-    // kKdPiece-pair pieces, each summed by a whole wave; the pieces of a
-    // segment longer than kKdPiece meet in `part`.
-    {
-      constexpr int PG = kWave / L4;
-      int sh[kKdPer], pcs[kKdPer], slt[kKdPer], tot = 0;
-#pragma unroll
-      for (int j = 0; j < kKdPer; ++j) {
-        const int si = tid * kKdPer + j;
-        const int len = si < nseg ? seg_beg[si + 1] - seg_beg[si] : 0;
-        sh[j] = si < nseg && len <= L4 ? 1 : 0;
-        pcs[j] = len > L4 ? (len + kKdPiece - 1) / kKdPiece : 0;
-        slt[j] = len > kKdPiece ? pcs[j] : 0;
-        tot += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
-      }
-      int total;
-      int pre = kd_block_scan(tot, red + 2 * kKdWaves, &total);
-#pragma unroll
-      for (int j = 0; j < kKdPer; ++j) {
-        const int si = tid * kKdPer + j;
-        if (si < nseg) {
-          seg_item[si] = pre;          // short index | first piece << 12 | first slot << 22
-          if (sh[j]) short_seg[pre & 0xfff] = si;
-          for (int q = 0; q < pcs[j]; ++q) items[((pre >> 12) & 0x3ff) + q] = (si << 5) | q;
-        }
-        pre += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
-      }
-      __syncthreads();
-      const int nshort = total & 0xfff;
-      const int npieces = (total >> 12) & 0x3ff;
-      const int npass = (nshort + PG - 1) / PG;
-
-      // ---- short segments: pass i takes segments i*PG .. i*PG + PG - 1,
-      // pair group g the g-th; lane g*L4 + j holds pair j of its segment.
-      // Waves take passes wave, wave + W, ...; each lane fetches its own
-      // segment's old row value ahead, KS passes per round (unrolled, so no
-      // loop head between the prefetch and its use waits for the loads).
-      constexpr int KS = 4;
-      for (int j0 = 0; wave + j0 * kKdWaves < npass; j0 += KS) {
-        float4 old[KS];
-#pragma unroll
-        for (int r = 0; r < KS; ++r) {
-          const int pi = min(wave + (j0 + r) * kKdWaves, npass - 1);
-          const int s0 = seg_beg[short_seg[min(pi * PG + pg, nshort - 1)]];
-          old[r] = reinterpret_cast<const float4*>(tbase + (int64_t)ent_row[s0] * rstride)[min(col4 + c4, width4 - 1)];
-        }
-#pragma unroll
-        for (int r = 0; r < KS; ++r) {
-          const int pi = wave + (j0 + r) * kKdWaves;
-          if (pi >= npass) break;                                  // wave-uniform
-          const int sidx = pi * PG + pg;
-          const bool has = sidx < nshort;
-          const int si = short_seg[min(sidx, nshort - 1)];
-          const int s0 = seg_beg[si];
-          const int len = has ? seg_beg[si + 1] - s0 : 0;
-          const int my_t = ent_t[s0 + min(c4, max(len - 1, 0))];
-          const int my_w = c4 < len ? ent_w[s0 + c4] : 0;
-          int steps = len;
-          if constexpr (L4 <= 4) steps = max(steps, xor_lane<4>(steps));
-          if constexpr (L4 <= 8) steps = max(steps, xor_lane<8>(steps));
-          if constexpr (L4 <= 16) steps = max(steps, xor_lane<16>(steps));
-          steps = __builtin_amdgcn_readfirstlane(max(steps, xor_lane<32>(steps)));
-          float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-          float cs = 0.f;
-          sum_steps<L4, 0>(steps, my_t, my_w, dat, c4, acc, cs);
-          if (r == 0) {
-            // every prefetched value is taken in before the round's first
-            // store: a later wait for one of them would otherwise also wait
-            // for the stores issued since (one counter covers both)
-#pragma unroll
-            for (int rr = 0; rr < KS; ++rr)
-              asm volatile("" :: "v"(old[rr].x), "v"(old[rr].y), "v"(old[rr].z), "v"(old[rr].w));
-          }
-          if (has && col_ok) {
-            float4 x = old[r];
-            const float inv = __builtin_amdgcn_rcpf((float)len);
-            if (idw_key) {
-              acc.x = fmaf(-cs, x.x, acc.x); acc.y = fmaf(-cs, x.y, acc.y);
-              acc.z = fmaf(-cs, x.z, acc.z); acc.w = fmaf(-cs, x.w, acc.w);
-            }
-            x.x -= lr * (acc.x * inv); x.y -= lr * (acc.y * inv);
-            x.z -= lr * (acc.z * inv); x.w -= lr * (acc.w * inv);
-            reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride)[col4 + c4] = x;
-          }
-        }
-      }
-
-      // ---- pieces of longer segments, continuing the waves' turns: lane
-      // g*L4 + j holds pair j*PG + g of the piece, pair groups are added by a
-      // butterfly.  A one-piece segment is finished by lane group jj of its
-      // round, whose prefetch register r holds its old row value.
-      constexpr int KP = PG >= 16 ? 1 : kKdPrefetch;
-      constexpr int R = KP * PG;
-      const int w0 = (wave - npass % kKdWaves + kKdWaves) % kKdWaves;
-      for (int j0 = 0; w0 + j0 * kKdWaves < npieces; j0 += R) {
-        float4 old[KP];
-#pragma unroll
-        for (int r = 0; r < KP; ++r) {
-          const int it = min(w0 + (j0 + r * PG + pg) * kKdWaves, npieces - 1);
-          const int s0 = seg_beg[items[it] >> 5];
-          old[r] = reinterpret_cast<const float4*>(tbase + (int64_t)ent_row[s0] * rstride)[min(col4 + c4, width4 - 1)];
-        }
-#pragma unroll
-        for (int r = 0; r < KP; ++r) {
-#pragma unroll
-          for (int jj = 0; jj < PG; ++jj) {
-            const int it = w0 + (j0 + r * PG + jj) * kKdWaves;
-            if (it >= npieces) break;                              // wave-uniform
-            const int packed = items[it];
-            const int si = packed >> 5, q = packed & 31;
-            const int s0 = seg_beg[si];
-            const int len = __builtin_amdgcn_readfirstlane(seg_beg[si + 1] - s0);
-            const int e0 = s0 + q * kKdPiece;
-            const int np = min(kKdPiece, len - q * kKdPiece);
-            const int pj = c4 * PG + pg;
-            const int my_t = ent_t[e0 + min(pj, np - 1)];
-            const int my_w = pj < np ? ent_w[e0 + pj] : 0;
-            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-            float cs = 0.f;
-            sum_steps<L4, 0>((np + PG - 1) / PG, my_t, my_w, dat, c4, acc, cs);
-            pair_group_sum<L4>(acc, cs);
-            if (r == 0 && jj == 0) {
-#pragma unroll
-              for (int rr = 0; rr < KP; ++rr)
-                asm volatile("" :: "v"(old[rr].x), "v"(old[rr].y), "v"(old[rr].z), "v"(old[rr].w));
-            }
-            if (len <= kKdPiece) {
-              if (pg == jj && col_ok) {
-                float4 x = old[r];
-                const float inv = __builtin_amdgcn_rcpf((float)len);
-                if (idw_key) {
-                  acc.x = fmaf(-cs, x.x, acc.x); acc.y = fmaf(-cs, x.y, acc.y);
-                  acc.z = fmaf(-cs, x.z, acc.z); acc.w = fmaf(-cs, x.w, acc.w);
-                }
-                x.x -= lr * (acc.x * inv); x.y -= lr * (acc.y * inv);
-                x.z -= lr * (acc.z * inv); x.w -= lr * (acc.w * inv);
-                reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride)[col4 + c4] = x;
-              }
-            } else {
-              const int slot = (seg_item[si] >> 22) + q;
-              if (pg == 0) part[slot * L4 + c4] = acc;
-              if (lane == 0) part_c[slot] = cs;
-            }
-          }
-        }
-      }
-      __syncthreads();
-      // ---- long segments: add the pieces in order and finish the row
-      for (int si = wave; si < nseg; si += kKdWaves) {
-        const int s0 = seg_beg[si];
-        const int len = seg_beg[si + 1] - s0;
-        if (len <= kKdPiece) continue;
-        const int pieces = (len + kKdPiece - 1) / kKdPiece;
-        const int slot0 = seg_item[si] >> 22;
-        if (lane < L4 && col_ok) {
-          float4* trow = reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride) + col4 + c4;
-          float4 x = *trow;
-          float4 acc = part[slot0 * L4 + c4];
-          float cs = part_c[slot0];
-          for (int q = 1; q < pieces; ++q) {
-            acc = f4_add(acc, part[(slot0 + q) * L4 + c4]);
-            cs += part_c[slot0 + q];
-          }
-          const float inv = __builtin_amdgcn_rcpf((float)len);
-          if (idw_key) {
-            acc.x = fmaf(-cs, x.x, acc.x); acc.y = fmaf(-cs, x.y, acc.y);
-            acc.z = fmaf(-cs, x.z, acc.z); acc.w = fmaf(-cs, x.w, acc.w);
-          }
-          x.x -= lr * (acc.x * inv); x.y -= lr * (acc.y * inv);
-          x.z -= lr * (acc.z * inv); x.w -= lr * (acc.w * inv);
-          *trow = x;
-        }
-      }
-    }
+    kd_sum_segments<L4>(a, who, dat, ent_row, ent_t, ent_w, cut, S);
     done += cut;
     __syncthreads();                 // the staged entries are reused
   }
 }
 
+// ints of the fused kernel's digit counters, later segment starts and items
+constexpr int kKwCntInts = (kKdWaves * 256 > 2 * kKdEntCap + 1 ? kKdWaves * 256 : 2 * kKdEntCap + 1) + 64;
+
+// LDS layout (byte offsets) of the fused kernel: chunks of T tokens, slices
+// of SW floats, at most kKdEntCap pairs per unit.
+struct KwLds {
+  int dat, key0, idx0, key1, idx1, wl, cnt, items, part, part_c, red, total;
+};
+__host__ __device__ constexpr KwLds kw_lds_layout(int T, int SW) {
+  KwLds L{};
+  int o = 0;
+  L.dat = o;    o = kd_align(o + T * (SW / 4 + 1) * 16);
+  L.key0 = o;   o = kd_align(o + kKdEntCap * 4);                  // sort ping: rows, pair indices
+  L.idx0 = o;   o = kd_align(o + kKdEntCap * 4);
+  L.key1 = o;   o = kd_align(o + kKdEntCap * 4);                  // pong (later tokens, weights)
+  L.idx1 = o;   o = kd_align(o + kKdEntCap * 4);
+  L.wl = o;     o = kd_align(o + kKdEntCap * 4);                  // weight of each pair (later short segments)
+  L.cnt = o;    o = kd_align(o + kKwCntInts * 4);                 // digit counters (later segment starts, items)
+  L.items = o;  o = kd_align(o + kKdMaxPieces * 4);
+  L.part = o;   o = kd_align(o + kKdMaxLong * (SW / 4) * 16);
+  L.part_c = o; o = kd_align(o + kKdMaxLong * 4);
+  L.red = o;    o = kd_align(o + 4 * kKdWaves * 4);
+  L.total = o;
+  return L;
+}
+static_assert(2 * kKdEntCap + 1 <= kKwCntInts, "segment starts and items fit the counters' space");
+
+// Chunks of at most kKdEntCap pairs per unit: grouping fused in.
+template <int SW>
+__global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
+  constexpr int L4 = SW / 4;
+  constexpr int kTiles = kKdEntCap / kWave / kKdWaves;   // list tiles per wave at most (2)
+  extern __shared__ float4 kd_lds4[];
+  char* lds = reinterpret_cast<char*>(kd_lds4);
+  const KwLds LL = kw_lds_layout(a.T, SW);
+  float4* dat = reinterpret_cast<float4*>(lds + LL.dat);
+  int* key0 = reinterpret_cast<int*>(lds + LL.key0);
+  int* idx0 = reinterpret_cast<int*>(lds + LL.idx0);
+  int* key1 = reinterpret_cast<int*>(lds + LL.key1);
+  int* idx1 = reinterpret_cast<int*>(lds + LL.idx1);
+  int* wl = reinterpret_cast<int*>(lds + LL.wl);
+  int* cnt = reinterpret_cast<int*>(lds + LL.cnt);
+  int* red = reinterpret_cast<int*>(lds + LL.red);
+
+  const KdWho who = kd_who(a, L4);
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int P = a.P;
+  const int64_t lbase = ((int64_t)who.list * a.U + who.u) * P;
+  const int* keys = a.keys + lbase;
+  const float* wsrc = who.list == 0 ? a.sel_w + (int64_t)who.u * P
+                                    : a.coef + (int64_t)(who.list - 1) * a.U * P + (int64_t)who.u * P;
+  const int invalid = who.list == 0 ? a.n * a.n : a.n;
+
+  // ---- one round of loads: the list's rows and weights first, then the
+  // data slice, which is stored to LDS only after the sort (loads complete
+  // in order, so the grouping waits for the rows alone).  Wave w owns list
+  // tiles [w*tpw, (w+1)*tpw), so kept entries come out in pair order;
+  // indices past the list re-read entry 0 and are masked.
+  const int tiles = (P + kWave - 1) / kWave;
+  const int tpw = (tiles + kKdWaves - 1) / kKdWaves;          // <= kTiles
+  int kr[kTiles];
+  float wr[kTiles];
+#pragma unroll
+  for (int j = 0; j < kTiles; ++j) {
+    const int i = (wave * tpw + j) * kWave + lane;
+    const int ic = j < tpw && i < P ? i : 0;
+    kr[j] = keys[ic];
+    wr[j] = wsrc[ic];
+  }
+  float4 v[kKdStageMax];
+  kd_stage_load<L4>(a, who, v);
+  for (int i = lane; i < 256; i += kWave) cnt[wave * 256 + i] = 0;   // this wave's digit counters
+  // ---- keep this group's rows, in pair order
+  int kept = 0;
+#pragma unroll
+  for (int j = 0; j < kTiles; ++j) {
+    const int i = (wave * tpw + j) * kWave + lane;
+    const bool in = j < tpw && i < P;
+    if (in) wl[i] = __float_as_int(wr[j]);
+    const bool mine = in && kr[j] != invalid && hash_group(kr[j], a.kd_sg_bits) == who.grp;
+    kept += __popcll(__ballot(mine));
+  }
+  if (lane == 0) red[wave] = kept;
+  __syncthreads();
+  int base = 0, M = 0;
+#pragma unroll
+  for (int w = 0; w < kKdWaves; ++w) {
+    const int t = red[w];
+    base += w < wave ? t : 0;
+    M += t;
+  }
+#pragma unroll
+  for (int j = 0; j < kTiles; ++j) {
+    const int i = (wave * tpw + j) * kWave + lane;
+    const bool in = j < tpw && i < P;
+    const bool mine = in && kr[j] != invalid && hash_group(kr[j], a.kd_sg_bits) == who.grp;
+    const unsigned long long m = __ballot(mine);
+    if (mine) {
+      const int pos = base + __popcll(m & lanes_below());
+      key0[pos] = kr[j];
+      idx0[pos] = i;
+    }
+    base += __popcll(m);
+  }
+  if (M == 0) return;                                 // block-uniform: nothing to write
+  __syncthreads();
+
+  // ---- stable LSD radix sort of the M kept (row, pair) by row: 8-bit
+  // digits, as many passes as the largest row needs.  Wave w owns entry
+  // tiles [t_lo, t_hi) and its own digit counters; the scatter base of a
+  // (digit, wave) is an exclusive scan in digit-major order.
+  const int rmax = invalid - 1;
+  int bits = 0;
+  while (bits < 31 && (rmax >> bits) != 0) ++bits;
+  const int passes = max(1, (bits + 7) / 8);
+  const int vtiles = (M + kWave - 1) / kWave;
+  const int vtpw = (vtiles + kKdWaves - 1) / kKdWaves;
+  const int t_lo = wave * vtpw, t_hi = min(vtiles, t_lo + vtpw);
+  int* mycnt = cnt + wave * 256;
+  int *ks = key0, *is = idx0, *kd = key1, *id = idx1;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = pass * 8;
+    // counts need no order: LDS atomic adds (the stable ranks come below)
+    for (int tile = t_lo; tile < t_hi; ++tile) {
+      const int i = tile * kWave + lane;
+      if (i < M) atomicAdd(&mycnt[((unsigned)ks[i] >> shift) & 255], 1);
+    }
+    __syncthreads();
+    // scatter bases in digit-major, wave-minor order, digit-parallel: thread
+    // d < 256 (waves 0-3) runs over the waves' counters of digit d, then the
+    // digits' totals are scanned across those four waves
+    int pre[kKdWaves];
+    int dbase = 0;
+    if (tid < 256) {                                     // whole waves 0-3
+      int run = 0;
+#pragma unroll
+      for (int w = 0; w < kKdWaves; ++w) {
+        pre[w] = run;
+        run += cnt[w * 256 + tid];
+      }
+      const int incl = wave_inclusive_scan(run);
+      if (lane == kWave - 1) red[wave] = incl;
+      dbase = incl - run;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int w = 0; w < wave; ++w) dbase += red[w];
+#pragma unroll
+      for (int w = 0; w < kKdWaves; ++w) cnt[w * 256 + tid] = dbase + pre[w];
+    }
+    __syncthreads();
+    for (int tile = t_lo; tile < t_hi; ++tile) {
+      const int i = tile * kWave + lane;
+      const bool valid = i < M;
+      const int key = valid ? ks[i] : 0;
+      const int d = ((unsigned)key >> shift) & 255;
+      const unsigned long long peers = digit_peers(d, valid);
+      const unsigned long long lower = peers & lanes_below();
+      const int b0 = valid ? mycnt[d] : 0;
+      if (valid) {
+        const int dst = b0 + __popcll(lower);
+        kd[dst] = key;
+        id[dst] = is[i];
+      }
+      if (valid && lower == 0ull) mycnt[d] = b0 + __popcll(peers);
+    }
+    for (int i = lane; i < 256; i += kWave) mycnt[i] = 0;   // for the next pass
+    __syncthreads();
+    int* t;
+    t = ks; ks = kd; kd = t;
+    t = is; is = id; id = t;
+  }
+  // ---- the data slice into LDS; sorted entries: rows ks, tokens and
+  // weights into the free buffers
+  kd_stage_store<L4>(a.T, v, dat);
+  int* ent_t = kd;
+  int* ent_w = id;
+  for (int i = tid; i < M; i += kKdThreads) {
+    const int p = is[i];
+    ent_t[i] = token_of(p, a.k);
+    ent_w[i] = wl[p];
+  }
+  __syncthreads();
+  KdSeg S;
+  S.seg_beg = cnt;
+  S.seg_item = cnt + kKdEntCap + 1;
+  S.short_seg = wl;
+  S.items = reinterpret_cast<int*>(lds + LL.items);
+  S.part = reinterpret_cast<float4*>(lds + LL.part);
+  S.part_c = reinterpret_cast<float*>(lds + LL.part_c);
+  S.red = red;
+  kd_sum_segments<L4>(a, who, dat, ks, ent_t, ent_w, M, S);
+}
+
 namespace {
+
+// Column-slice width: the widest whose data for every token fits kKdDataBytes.
+int kd_slice_width(int T) {
+  return T * 64 * 4 <= kKdDataBytes ? 64 : (T * 32 * 4 <= kKdDataBytes ? 32 : 16);
+}
 
 template <int SW>
 hipError_t launch_kd_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
-  const int smem = kd_lds_layout(a.T, SW).total;
+  const int64_t per_unit = (int64_t)(a.kd_sv + 2 * a.kd_sk) << a.kd_sg_bits;
+  const dim3 grid((unsigned)(per_unit * a.U));
+  if (kd_fuses_grouping(a)) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&kd_write<SW>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        kw_lds_layout(kKdDataBytes / (SW * 4), SW).total);
+    if (attr != hipSuccess) return attr;
+    return fw_launch(kd_write<SW>, grid, dim3(kKdThreads), (uint32_t)kw_lds_layout(a.T, SW).total, s, tm, a);
+  }
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&kd_update<SW>), hipFuncAttributeMaxDynamicSharedMemorySize,
       kd_lds_layout(kKdDataBytes / (SW * 4), SW).total);
   if (attr != hipSuccess) return attr;
-  const int64_t per_unit = (int64_t)(a.kd_sv + 2 * a.kd_sk) << a.kd_sg_bits;
-  return fw_launch(kd_update<SW>, dim3((unsigned)(per_unit * a.U)), dim3(kKdThreads), (uint32_t)smem,
-                   s, tm, a);
+  return fw_launch(kd_update<SW>, grid, dim3(kKdThreads), (uint32_t)kd_lds_layout(a.T, SW).total, s, tm, a);
 }
 
 }  // namespace
 
+bool kd_fuses_grouping(const ChunkArgs& a) { return a.P <= kKdEntCap; }
+
 hipError_t launch_kd(const ChunkArgs& args, hipStream_t s, const LaunchTiming* tm) {
   ChunkArgs a = with_divisors(args);
-  // the widest column slice whose data for every token fits kKdDataBytes
-  const int sw = a.T * 64 * 4 <= kKdDataBytes ? 64 : (a.T * 32 * 4 <= kKdDataBytes ? 32 : 16);
+  const int sw = kd_slice_width(a.T);
   a.kd_sv = (a.dv + sw - 1) / sw;
   a.kd_sk = (a.half + sw - 1) / sw;
   const int combos = a.kd_sv + 2 * a.kd_sk;
-  // groups of hash regions: about one workgroup per compute unit in all
+  // hash groups of rows per (list, unit): about one workgroup per compute
+  // unit in all.  Unfused, a group is a run of the grouping kernel's regions.
+  const int most = kd_fuses_grouping(a) ? 64 : a.regions;
   int sg = 1, bits = 0;
-  while (sg * 2 <= a.regions && (int64_t)a.U * combos * sg * 2 <= 256) { sg *= 2; ++bits; }
+  while (sg * 2 <= most && (int64_t)a.U * combos * sg * 2 <= 256) { sg *= 2; ++bits; }
   a.kd_sg_bits = bits;
   a.kd_div_pu = make_fastdiv(combos << bits);
   a.kd_div_sk = make_fastdiv(a.kd_sk);

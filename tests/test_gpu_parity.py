@@ -171,6 +171,24 @@ def test_long_segments_split_into_pieces(mode):
         st, _, _ = compare_chunk(mem, st, q, y, lr, label=f"long-segments {mode} step{c}")
 
 
+@pytest.mark.parametrize("C,mode", [(300, "idw"), (700, "idw"), (700, "dot")])
+def test_update_geometry_at_wide_chunks(C, mode):
+    """Chunks of more than 256 and 512 tokens narrow the update's column
+    slices (32 and 16 floats); with 8 units and d_v 256 each workgroup then
+    owns a whole list, whose 2,400 or 5,600 entries pass in batches cut at
+    segment heads.  Half the tokens repeat 4 queries (rows touched by 38 or
+    88 tokens: multi-piece segments summed across waves), the rest are
+    distinct (one-token segments packed several to a wave pass)."""
+    need_gpu()
+    B, H, n, half, dv, k = 8, 1, 64, 64, 256, 8
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=C, num_heads=H,
+               max_batch=B, score_mode=mode)
+    st, q, y = _random_case(600 + C + (mode == "dot"), B, H, C, n, half, dv)
+    rep = np.arange(C) % 2 == 0
+    q[:, rep] = q[:, [t % 8 for t in range(C) if rep[t]]]
+    compare_chunk(mem, st, q, y, 1.0, units=[0, 3, 7], label=f"wide C{C} {mode}")
+
+
 def test_closed_form_k1_single_token_writes_target():
     need_gpu()
     n, half, dv = 16, 8, 32
