@@ -69,7 +69,7 @@ static_assert(kKdPer * kKdThreads == kKdEntCap, "whole entries per thread");
 
 // LDS layout (byte offsets) for chunks of T tokens and slices of SW floats.
 struct KdLds {
-  int dat, ent_t, ent_w, ent_row, seg_beg, seg_item, short_seg, items, part, part_c, red, total;
+  int dat, ent_t, ent_w, ent_row, seg_beg, seg_item, short_seg, items, part, part_c, long_seg, red, total;
 };
 __host__ __device__ constexpr int kd_align(int x) { return (x + 15) & ~15; }
 __host__ __device__ constexpr KdLds kd_lds_layout(int T, int SW) {
@@ -85,6 +85,7 @@ __host__ __device__ constexpr KdLds kd_lds_layout(int T, int SW) {
   L.items = o;    o = kd_align(o + kKdMaxPieces * 4);            // pieces of longer segments
   L.part = o;     o = kd_align(o + kKdMaxLong * (SW / 4) * 16);  // partial sums of long pieces
   L.part_c = o;   o = kd_align(o + kKdMaxLong * 4);
+  L.long_seg = o; o = kd_align(o + kKdMaxLong * 4);
   L.red = o;      o = kd_align(o + 4 * kKdWaves * 4);
   L.total = o;
   return L;
@@ -276,6 +277,7 @@ struct KdSeg {
   int* items;       // [kKdMaxPieces] pieces of longer segments: segment << 5 | piece
   float4* part;     // [kKdMaxLong][L4] partial sums of pieces
   float* part_c;    // [kKdMaxLong] their coefficient sums
+  int* long_seg;    // [kKdMaxLong] by slot: the segment whose first slot it is, else -1
   int* red;         // [4 * kKdWaves] block-scan scratch
 };
 
@@ -295,6 +297,7 @@ __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho&
   int* items = S.items;
   float4* part = S.part;
   float* part_c = S.part_c;
+  int* long_seg = S.long_seg;
   int* red = S.red;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int c4 = lane & (L4 - 1), pg = lane / L4;
@@ -349,12 +352,14 @@ __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho&
         seg_item[si] = pre;          // short index | first piece << 12 | first slot << 22
         if (sh[j]) short_seg[pre & 0xfff] = si;
         for (int q = 0; q < pcs[j]; ++q) items[((pre >> 12) & 0x3ff) + q] = (si << 5) | q;
+        for (int q = 0; q < slt[j]; ++q) long_seg[(pre >> 22) + q] = q == 0 ? si : -1;
       }
       pre += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
     }
     __syncthreads();
     const int nshort = total & 0xfff;
     const int npieces = (total >> 12) & 0x3ff;
+    const int nslots = total >> 22;
     const int npass = (nshort + PG - 1) / PG;
 
     // ---- short segments: pass i takes segments i*PG .. i*PG + PG - 1,
@@ -365,31 +370,29 @@ __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho&
     constexpr int KS = 4;
     for (int j0 = 0; wave + j0 * kKdWaves < npass; j0 += KS) {
       float4 old[KS];
+      int row[KS], len[KS], my_t[KS], my_w[KS];
 #pragma unroll
       for (int r = 0; r < KS; ++r) {
-        const int pi = min(wave + (j0 + r) * kKdWaves, npass - 1);
-        const int s0 = seg_beg[short_seg[min(pi * PG + pg, nshort - 1)]];
-        old[r] = reinterpret_cast<const float4*>(tbase + (int64_t)ent_row[s0] * rstride)[min(col4 + c4, width4 - 1)];
+        const int sidx = min(wave + (j0 + r) * kKdWaves, npass - 1) * PG + pg;
+        const int si = short_seg[min(sidx, nshort - 1)];
+        const int s0 = seg_beg[si];
+        len[r] = sidx < nshort ? seg_beg[si + 1] - s0 : 0;
+        row[r] = ent_row[s0];
+        my_t[r] = ent_t[s0 + min(c4, max(len[r] - 1, 0))];
+        my_w[r] = c4 < len[r] ? ent_w[s0 + c4] : 0;
+        old[r] = reinterpret_cast<const float4*>(tbase + (int64_t)row[r] * rstride)[min(col4 + c4, width4 - 1)];
       }
 #pragma unroll
       for (int r = 0; r < KS; ++r) {
-        const int pi = wave + (j0 + r) * kKdWaves;
-        if (pi >= npass) break;                                  // wave-uniform
-        const int sidx = pi * PG + pg;
-        const bool has = sidx < nshort;
-        const int si = short_seg[min(sidx, nshort - 1)];
-        const int s0 = seg_beg[si];
-        const int len = has ? seg_beg[si + 1] - s0 : 0;
-        const int my_t = ent_t[s0 + min(c4, max(len - 1, 0))];
-        const int my_w = c4 < len ? ent_w[s0 + c4] : 0;
-        int steps = len;
+        if (wave + (j0 + r) * kKdWaves >= npass) break;         // wave-uniform
+        int steps = len[r];
         if constexpr (L4 <= 4) steps = max(steps, xor_lane<4>(steps));
         if constexpr (L4 <= 8) steps = max(steps, xor_lane<8>(steps));
         if constexpr (L4 <= 16) steps = max(steps, xor_lane<16>(steps));
         steps = __builtin_amdgcn_readfirstlane(max(steps, xor_lane<32>(steps)));
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         float cs = 0.f;
-        sum_steps<L4, 0>(steps, my_t, my_w, dat, c4, acc, cs);
+        sum_steps<L4, 0>(steps, my_t[r], my_w[r], dat, c4, acc, cs);
         if (r == 0) {
           // every prefetched value is taken in before the round's first
           // store: a later wait for one of them would otherwise also wait
@@ -398,16 +401,16 @@ __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho&
           for (int rr = 0; rr < KS; ++rr)
             asm volatile("" :: "v"(old[rr].x), "v"(old[rr].y), "v"(old[rr].z), "v"(old[rr].w));
         }
-        if (has && col_ok) {
+        if (len[r] > 0 && col_ok) {
           float4 x = old[r];
-          const float inv = __builtin_amdgcn_rcpf((float)len);
+          const float inv = __builtin_amdgcn_rcpf((float)len[r]);
           if (idw_key) {
             acc.x = fmaf(-cs, x.x, acc.x); acc.y = fmaf(-cs, x.y, acc.y);
             acc.z = fmaf(-cs, x.z, acc.z); acc.w = fmaf(-cs, x.w, acc.w);
           }
           x.x -= lr * (acc.x * inv); x.y -= lr * (acc.y * inv);
           x.z -= lr * (acc.z * inv); x.w -= lr * (acc.w * inv);
-          reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride)[col4 + c4] = x;
+          reinterpret_cast<float4*>(tbase + (int64_t)row[r] * rstride)[col4 + c4] = x;
         }
       }
     }
@@ -473,12 +476,12 @@ __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho&
     }
     __syncthreads();
     // ---- long segments: add the pieces in order and finish the row
-    for (int si = wave; si < nseg; si += kKdWaves) {
+    for (int slot0 = wave; slot0 < nslots; slot0 += kKdWaves) {
+      const int si = long_seg[slot0];
+      if (si < 0) continue;                                      // not a segment's first slot
       const int s0 = seg_beg[si];
       const int len = seg_beg[si + 1] - s0;
-      if (len <= kKdPiece) continue;
       const int pieces = (len + kKdPiece - 1) / kKdPiece;
-      const int slot0 = seg_item[si] >> 22;
       if (lane < L4 && col_ok) {
         float4* trow = reinterpret_cast<float4*>(tbase + (int64_t)ent_row[s0] * rstride) + col4 + c4;
         float4 x = *trow;
@@ -521,6 +524,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
   S.items = reinterpret_cast<int*>(lds + LL.items);
   S.part = reinterpret_cast<float4*>(lds + LL.part);
   S.part_c = reinterpret_cast<float*>(lds + LL.part_c);
+  S.long_seg = reinterpret_cast<int*>(lds + LL.long_seg);
   S.red = reinterpret_cast<int*>(lds + LL.red);               // [4][kKdWaves]
   int* red = S.red;
 
@@ -611,7 +615,7 @@ constexpr int kKwCntInts = (kKdWaves * 256 > 2 * kKdEntCap + 1 ? kKdWaves * 256 
 // LDS layout (byte offsets) of the fused kernel: chunks of T tokens, slices
 // of SW floats, at most kKdEntCap pairs per unit.
 struct KwLds {
-  int dat, key0, idx0, key1, idx1, wl, cnt, items, part, part_c, red, total;
+  int dat, key0, idx0, key1, idx1, wl, cnt, items, part, part_c, long_seg, red, total;
 };
 __host__ __device__ constexpr KwLds kw_lds_layout(int T, int SW) {
   KwLds L{};
@@ -626,6 +630,7 @@ __host__ __device__ constexpr KwLds kw_lds_layout(int T, int SW) {
   L.items = o;  o = kd_align(o + kKdMaxPieces * 4);
   L.part = o;   o = kd_align(o + kKdMaxLong * (SW / 4) * 16);
   L.part_c = o; o = kd_align(o + kKdMaxLong * 4);
+  L.long_seg = o; o = kd_align(o + kKdMaxLong * 4);
   L.red = o;    o = kd_align(o + 4 * kKdWaves * 4);
   L.total = o;
   return L;
@@ -795,6 +800,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   S.items = reinterpret_cast<int*>(lds + LL.items);
   S.part = reinterpret_cast<float4*>(lds + LL.part);
   S.part_c = reinterpret_cast<float*>(lds + LL.part_c);
+  S.long_seg = reinterpret_cast<int*>(lds + LL.long_seg);
   S.red = red;
   kd_sum_segments<L4>(a, who, dat, ks, ent_t, ent_w, M, S);
 }
@@ -835,10 +841,15 @@ hipError_t launch_kd(const ChunkArgs& args, hipStream_t s, const LaunchTiming* t
   a.kd_sk = (a.half + sw - 1) / sw;
   const int combos = a.kd_sv + 2 * a.kd_sk;
   // hash groups of rows per (list, unit): about one workgroup per compute
-  // unit in all.  Unfused, a group is a run of the grouping kernel's regions.
+  // unit in all, and (unfused) about two batches of entries per group at
+  // most (P / groups <= 2 kKdEntCap on average), so
+  // that a list with many distinct rows does not leave half the chip idle
+  // behind a few long workgroups.  Unfused, a group is a run of the grouping
+  // kernel's regions.
   const int most = kd_fuses_grouping(a) ? 64 : a.regions;
   int sg = 1, bits = 0;
   while (sg * 2 <= most && (int64_t)a.U * combos * sg * 2 <= 256) { sg *= 2; ++bits; }
+  while (sg * 2 <= most && (int64_t)sg * 2 * kKdEntCap < a.P) { sg *= 2; ++bits; }
   a.kd_sg_bits = bits;
   a.kd_div_pu = make_fastdiv(combos << bits);
   a.kd_div_sk = make_fastdiv(a.kd_sk);
