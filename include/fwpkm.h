@@ -59,6 +59,9 @@ extern "C" {
 #define FWPKM_ERR_OOM         (-3) /* device workspace allocation failed */
 #define FWPKM_ERR_HIP         (-4) /* HIP runtime error; fwpkm_last_error() holds its text */
 #define FWPKM_ERR_UNSUPPORTED (-5) /* valid shape outside the kernels' limits (listed below) */
+#define FWPKM_ERR_DEVICE_CHECK (-6) /* checked builds only: a kernel found one of its invariants
+                                       broken (fwpkm_last_error() names which); the call's
+                                       outputs and state are then not meaningful */
 
 /* Scoring modes.
  * IDW: score = -log(eps + ||q - K||^2) over the full key [K1[a]; K2[b]]
@@ -307,6 +310,22 @@ int fwpkm_profile_read(fwpkm_handle* h, double* ms, int64_t* launches);
 
 /* Short name of timed kernel i ("" outside 0..FWPKM_NUM_TIMED-1). */
 const char* fwpkm_kernel_name(int32_t i);
+
+/* 1 in a checked build of this library, else 0.
+ *
+ * A checked build (compiled with FWPKM_DEVICE_CHECKS=1; the package's build
+ * script makes it with --checked, as libfwpkm_checked.so) runs the same
+ * kernels with device-side tests of the invariants the indexing rests on:
+ * every per-half candidate index below n, k Cartesian candidates per token,
+ * every selected slot in [0, N) and distinct, every selection weight finite
+ * and in [0, 1], every grouped entry's row and token in range and in row
+ * order, and every update batch within its LDS lists.  A failed test sets a
+ * bit in a word of the workspace; each chunk call then waits for its stream
+ * and returns FWPKM_ERR_DEVICE_CHECK naming the tests that failed.  The wait
+ * makes a checked build unsuitable for stream capture and for timing; the
+ * tests never trap, so a failure cannot fault the device.  For debugging
+ * and test runs, not for production. */
+int32_t fwpkm_checked_build(void);
 
 #ifdef __cplusplus
 }

@@ -10,7 +10,12 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfwpkm.so")
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# the checked build (device-side invariant tests; see fwpkm_checked_build)
+CHECKED_LIB_PATH = os.path.join(_HERE, "libfwpkm_checked.so")
+# FWPKM_LIB_PATH points the binding at another build of the same ABI, such as
+# the checked one
+LIB_PATH = os.environ.get("FWPKM_LIB_PATH") or os.path.join(_HERE, "libfwpkm.so")
 
 OK = 0
 ERR_INVALID_ARG = -1
@@ -18,6 +23,7 @@ ERR_ALIAS = -2
 ERR_OOM = -3
 ERR_HIP = -4
 ERR_UNSUPPORTED = -5
+ERR_DEVICE_CHECK = -6
 
 SCORE_IDW = 0
 SCORE_DOT = 1
@@ -43,6 +49,7 @@ EXPORTS = (
     "fwpkm_profile_enable",
     "fwpkm_profile_read",
     "fwpkm_kernel_name",
+    "fwpkm_checked_build",
 )
 
 NUM_TIMED = 10
@@ -144,6 +151,8 @@ def load() -> ctypes.CDLL:
     lib.fwpkm_profile_read.restype = ctypes.c_int
     lib.fwpkm_kernel_name.argtypes = [ctypes.c_int32]
     lib.fwpkm_kernel_name.restype = ctypes.c_char_p
+    lib.fwpkm_checked_build.argtypes = []
+    lib.fwpkm_checked_build.restype = ctypes.c_int32
     _lib = lib
     return lib
 

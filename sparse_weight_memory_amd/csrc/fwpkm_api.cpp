@@ -34,7 +34,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Byte sizes of the workspace regions for `units` units of `tokens` tokens.
 struct WsLayout {
-  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, ent_row, ent_tw, kinds;
+  size_t half_o, half_i, qnorm, sel_w, g, keys, coef, ent_row, ent_tw, kinds, check;
   size_t addr_s, addr_dk, addr_tok, addr_ell, total;
 };
 
@@ -55,6 +55,7 @@ WsLayout ws_layout(const fwpkm_config& c, int64_t units, int64_t tokens) {
   L.ent_tw = take(sizeof(int2) * 3 * units * P);
   // regions per list shrink as units grow: 3 * units * regions <= max(256, 3 * units)
   L.kinds = take(sizeof(int4) * std::max<int64_t>(256, 3 * units));
+  L.check = take(sizeof(unsigned int));     // device-check word (checked builds)
   // addressing loss (only with addr_weight != 0): every token's score over
   // every sub-key (then its dL/ds coefficient), and the key gradient
   const bool addr = c.addr_weight != 0.0f;
@@ -392,6 +393,8 @@ void fwpkm_destroy(fwpkm_handle* h) {
   delete h;
 }
 
+int32_t fwpkm_checked_build(void) { return FWPKM_DEVICE_CHECKS ? 1 : 0; }
+
 const char* fwpkm_kernel_name(int32_t i) {
   return (i >= 0 && i < FWPKM_NUM_TIMED) ? kKernelNames[i] : "";
 }
@@ -433,6 +436,36 @@ int fwpkm_profile_read(fwpkm_handle* h, double* ms, int64_t* launches) {
 // noalloc: use the fixed array `scratch` as the workspace (never the
 // handle's, which is then neither allocated nor touched) and record no
 // timing events.
+#if FWPKM_DEVICE_CHECKS
+// Checked builds: wait for the call's kernels and report the invariants they
+// found broken (the word is cleared before the first kernel of every call).
+static int read_device_checks(const unsigned int* word, hipStream_t stream) {
+  static const char* const names[fwpkm::kNumDeviceChecks] = {
+      "per-half sub-key index >= n", "fewer than k candidates", "selected slot outside [0, N)",
+      "a slot selected twice", "selection weight not finite or outside [0, 1]",
+      "grouped entry row or token out of range", "update batch over its LDS capacity",
+      "grouped entries out of row order"};
+  unsigned int bits = 0;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMemcpy(&bits, word, sizeof(bits), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(FWPKM_ERR_HIP, "reading the device-check word: %s", hipGetErrorString(e));
+  if (bits == 0) {
+    g_err[0] = '\0';
+    return FWPKM_OK;
+  }
+  char msg[512];
+  size_t at = 0;
+  msg[0] = '\0';
+  for (int i = 0; i < fwpkm::kNumDeviceChecks; ++i) {
+    if (!(bits & (1u << i))) continue;
+    const int w = snprintf(msg + at, sizeof(msg) - at, "%s%s", at ? "; " : "", names[i]);
+    if (w < 0 || (size_t)w >= sizeof(msg) - at) break;
+    at += (size_t)w;
+  }
+  return fail(FWPKM_ERR_DEVICE_CHECK, "device check failed (bits 0x%x): %s", bits, msg);
+}
+#endif
+
 static int forward_impl(fwpkm_handle* h, const float* queries, const float* targets,
                         const float* token_weights, int32_t batch, int32_t tokens, float lr,
                         const fwpkm_state* past, const fwpkm_state* next,
@@ -609,6 +642,11 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
   a.addr_dk = reinterpret_cast<float*>(ws + L.addr_dk);
   a.addr_tok = reinterpret_cast<float*>(ws + L.addr_tok);
   a.addr_ell = reinterpret_cast<float*>(ws + L.addr_ell);
+  a.check = reinterpret_cast<unsigned int*>(ws + L.check);
+#if FWPKM_DEVICE_CHECKS
+  if ((e = hipMemsetAsync(a.check, 0, sizeof(unsigned int), stream)) != hipSuccess)
+    return fail(FWPKM_ERR_HIP, "clearing the device-check word: %s", hipGetErrorString(e));
+#endif
 
   using fwpkm::LaunchTiming;
   if ((e = timed(h, prof, 0, [&](const LaunchTiming* tm) { return fwpkm::launch_ka(a, stream, tm); })) != hipSuccess)
@@ -633,8 +671,12 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
         return fail(FWPKM_ERR_HIP, "addressing step kernel: %s", hipGetErrorString(e));
     }
   }
+#if FWPKM_DEVICE_CHECKS
+  return read_device_checks(a.check, stream);
+#else
   g_err[0] = '\0';
   return FWPKM_OK;
+#endif
 }
 
 }  // extern "C"

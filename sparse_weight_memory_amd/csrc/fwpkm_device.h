@@ -19,6 +19,25 @@ constexpr int kUpdMaxLists = 3072;  // 3 * units (lists) a chunk may carry
 // Invalid entries: they order after every real candidate.
 constexpr int kNoIndex = 0x7fffffff;
 
+// Checked builds (FWPKM_DEVICE_CHECKS=1): the kernels test the invariants the
+// indexing rests on and set a bit in ChunkArgs::check for every one that
+// fails; the host reads the word after the call.  Off by default, where the
+// tests compile away.
+#ifndef FWPKM_DEVICE_CHECKS
+#define FWPKM_DEVICE_CHECKS 0
+#endif
+enum DeviceCheck : unsigned int {
+  kChkHalfIndex = 1u << 0,    // a per-half candidate's sub-key index is >= n
+  kChkCandidates = 1u << 1,   // fewer than k Cartesian candidates for a token
+  kChkSlot = 1u << 2,         // a selected slot is outside [0, N)
+  kChkDistinct = 1u << 3,     // a token selected one slot twice
+  kChkWeight = 1u << 4,       // a selection weight is not finite or outside [0, 1]
+  kChkEntry = 1u << 5,        // a grouped entry's row or token is out of range
+  kChkCapacity = 1u << 6,     // an update batch overflows its LDS lists
+  kChkOrder = 1u << 7,        // grouped entries are not sorted by row
+};
+constexpr int kNumDeviceChecks = 8;
+
 // Everything a chunk's kernels need, passed by value.
 // Division by a divisor d >= 1 fixed for a launch, for dividends 0 <= x < 2^31:
 // x / d = (umulhi(x, m) + x) >> l with l = ceil(log2 d) and
@@ -124,7 +143,17 @@ struct ChunkArgs {
   int kd_sg_bits;
   FastDiv kd_div_pu;   // x / ((kd_sv + 2 kd_sk) << kd_sg_bits): workgroups per unit
   FastDiv kd_div_sk;   // x / kd_sk
+  unsigned int* check; // one word of DeviceCheck bits (checked builds)
 };
+
+// Sets `bit` in the check word when `ok` is false (checked builds only).
+__device__ __forceinline__ void device_check(const ChunkArgs& a, bool ok, unsigned int bit) {
+#if FWPKM_DEVICE_CHECKS
+  if (!ok) atomicOr(a.check, bit);
+#else
+  (void)a; (void)ok; (void)bit;
+#endif
+}
 
 // `a` with the decomposition divisors filled in
 inline ChunkArgs with_divisors(const ChunkArgs& a) {

@@ -649,6 +649,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     }
     if (lane < k) {
       const int64_t base = ((((int64_t)u * a.T + tw) * 2 + h) * a.nblk + kb) * k;
+      device_check(a, x == kEmptyKey || key_index(x) < a.n, kChkHalfIndex);
       a.half_o[base + lane] = key_value(x);
       a.half_i[base + lane] = key_index(x);
     }
@@ -699,6 +700,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
     // a token with more than 32 survivors takes the whole-wave path instead
     if (l < k && t0 + tl < a.T && n <= 32) {
       const int64_t base = ((((int64_t)u * a.T + t0 + tl) * 2 + h) * a.nblk + kb) * k;
+      device_check(a, x == kEmptyKey || key_index(x) < a.n, kChkHalfIndex);
       a.half_o[base + l] = key_value(x);
       a.half_i[base + l] = key_index(x);
     }

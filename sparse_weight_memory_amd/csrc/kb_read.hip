@@ -277,6 +277,18 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
     if (a.out_slots) a.out_slots[ob * k + lane] = sel_s;
     if (a.out_weights) a.out_weights[ob * k + lane] = w;
   }
+#if FWPKM_DEVICE_CHECKS
+  {
+    bool twice = false;
+    for (int m = 0; m < k; ++m) twice |= m < lane && readlane_i(sel_s, m) == sel_s;
+    if (lane < k) {
+      device_check(a, sel_s != kNoIndex, kChkCandidates);
+      device_check(a, sel_s == kNoIndex || (sel_s >= 0 && sel_s < N), kChkSlot);
+      device_check(a, !twice || sel_s == kNoIndex, kChkDistinct);
+      device_check(a, w >= 0.f && w <= 1.f + 1e-6f, kChkWeight);   // false for NaN
+    }
+  }
+#endif
   if (!WRITE) return;
 
   // ---- 5. backward

@@ -281,16 +281,18 @@ struct KdSeg {
   int* red;         // [4 * kKdWaves] block-scan scratch
 };
 
-// The segments (runs of one row) of the entries [0, cut), sorted by row, in
-// LDS: rows ent_row, tokens ent_t, weights ent_w (float bits); each row's
-// mean gradient is applied to its slice of the table.  cut <= kKdEntCap.
+// The segments (runs of one row) of the entries [0, cut), in LDS: rows
+// ent_row, tokens ent_t, weights ent_w (float bits), ordered by
+// (hash_group(row, order_bits), row) -- by row alone with order_bits = 0 --
+// so every row's entries are one run; each row's mean gradient is applied to
+// its slice of the table.  cut <= kKdEntCap.
 // Ends after a barrier-free phase: the caller synchronises before reusing
 // the scratch.
 template <int L4>
 __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho& who,
                                                 const float4* dat, const int* ent_row,
                                                 const int* ent_t, const int* ent_w, int cut,
-                                                const KdSeg& S) {
+                                                const KdSeg& S, int order_bits) {
   int* seg_beg = S.seg_beg;
   int* seg_item = S.seg_item;
   int* short_seg = S.short_seg;
@@ -320,6 +322,24 @@ __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho&
     hd[j] = e < cut && (e == 0 || ent_row[e] != ent_row[e - 1]);
     nh += hd[j];
   }
+#if FWPKM_DEVICE_CHECKS
+  {
+    const int rows = who.list == 0 ? a.n * a.n : a.n;
+#pragma unroll
+    for (int j = 0; j < kKdPer; ++j) {
+      const int e = tid * kKdPer + j;
+      if (e < cut) {
+        device_check(a, ent_row[e] >= 0 && ent_row[e] < rows && ent_t[e] >= 0 && ent_t[e] < a.T, kChkEntry);
+        if (e > 0) {
+          const int r0 = ent_row[e - 1], r1 = ent_row[e];
+          const int g0 = hash_group(r0, order_bits), g1 = hash_group(r1, order_bits);
+          device_check(a, g0 < g1 || (g0 == g1 && r0 <= r1), kChkOrder);
+        }
+      }
+    }
+    if (tid == 0) device_check(a, cut <= kKdEntCap, kChkCapacity);
+  }
+#endif
   int nseg;
   int sp = kd_block_scan(nh, red, &nseg);
 #pragma unroll
@@ -360,6 +380,7 @@ __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho&
     const int nshort = total & 0xfff;
     const int npieces = (total >> 12) & 0x3ff;
     const int nslots = total >> 22;
+    if (tid == 0) device_check(a, nshort <= kKdEntCap && npieces <= kKdMaxPieces && nslots <= kKdMaxLong, kChkCapacity);
     const int npass = (nshort + PG - 1) / PG;
 
     // ---- short segments: pass i takes segments i*PG .. i*PG + PG - 1,
@@ -551,6 +572,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
   }
   __syncthreads();
   const int e_first = red[3 * kKdWaves], e_count = red[3 * kKdWaves + 1];
+  if (tid == 0) device_check(a, e_first >= 0 && e_count >= 0 && e_first + e_count <= a.P, kChkCapacity);
   const int* erow = a.ent_row + lbase + e_first;
   const int2* etw = a.ent_tw + lbase + e_first;
 
@@ -603,7 +625,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
 #pragma unroll
       for (int w = 0; w < kKdWaves; ++w) cut = max(cut, red[kKdWaves + w]);
     }
-    kd_sum_segments<L4>(a, who, dat, ent_row, ent_t, ent_w, cut, S);
+    kd_sum_segments<L4>(a, who, dat, ent_row, ent_t, ent_w, cut, S, a.region_bits);
     done += cut;
     __syncthreads();                 // the staged entries are reused
   }
@@ -802,7 +824,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   S.part_c = reinterpret_cast<float*>(lds + LL.part_c);
   S.long_seg = reinterpret_cast<int*>(lds + LL.long_seg);
   S.red = red;
-  kd_sum_segments<L4>(a, who, dat, ks, ent_t, ent_w, M, S);
+  kd_sum_segments<L4>(a, who, dat, ks, ent_t, ent_w, M, S, 0);
 }
 
 namespace {

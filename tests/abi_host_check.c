@@ -124,6 +124,7 @@ int main(void) {
   CHECK(strcmp(fwpkm_kernel_name(0), "score") == 0);
   CHECK(strcmp(fwpkm_kernel_name(-1), "") == 0);
   CHECK(strcmp(fwpkm_kernel_name(FWPKM_NUM_TIMED), "") == 0);
+  CHECK(fwpkm_checked_build() == 0);
 
   fwpkm_destroy(h);
   fwpkm_destroy(NULL);

@@ -276,3 +276,21 @@ def test_library_leaves_no_kernel_symbol_undefined():
     out = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     assert "fwpkm" not in out, out
+
+
+def test_checked_build_exports_the_same_abi():
+    """libfwpkm_checked.so (device checks compiled in) declares itself and
+    exports every symbol of the header; the product library reports 0."""
+    from sparse_weight_memory_amd import build as B
+    if not os.path.exists(_lib.CHECKED_LIB_PATH):
+        B.build(checked=True)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.CHECKED_LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fwpkm_\w+)", out))
+    assert set(declared_functions()) <= exported
+    code = ("import ctypes, sys; lib = ctypes.CDLL(sys.argv[1]); "
+            "lib.fwpkm_checked_build.restype = ctypes.c_int32; print(lib.fwpkm_checked_build())")
+    for path, want in ((_lib.CHECKED_LIB_PATH, "1"), (_lib.LIB_PATH, "0")):
+        r = subprocess.run(["python3", "-c", code, path], capture_output=True, text=True, timeout=120)
+        assert r.returncode == 0, r.stderr
+        assert r.stdout.strip().splitlines()[-1] == want
