@@ -754,10 +754,21 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   int *ks = key0, *is = idx0, *kd = key1, *id = idx1;
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * 8;
-    // counts need no order: LDS atomic adds (the stable ranks come below)
-    for (int tile = t_lo; tile < t_hi; ++tile) {
-      const int i = tile * kWave + lane;
-      if (i < M) atomicAdd(&mycnt[((unsigned)ks[i] >> shift) & 255], 1);
+    // each tile's lanes with equal digits (ballots), counted once by the
+    // lowest of them into this wave's own counters (no other wave writes
+    // them, and a wave's LDS operations complete in order, so no atomics);
+    // keys, digits and peer masks stay in registers for the scatter
+    int tk[kTiles], td[kTiles];
+    unsigned long long tp[kTiles];
+#pragma unroll
+    for (int j = 0; j < kTiles; ++j) {
+      if (t_lo + j >= t_hi) break;                     // wave-uniform: ballots run on the shared scalar unit
+      const int i = (t_lo + j) * kWave + lane;
+      const bool valid = i < M;
+      tk[j] = valid ? ks[i] : 0;
+      td[j] = ((unsigned)tk[j] >> shift) & 255;
+      tp[j] = digit_peers(td[j], valid);
+      if (valid && (tp[j] & lanes_below()) == 0ull) mycnt[td[j]] += __popcll(tp[j]);
     }
     __syncthreads();
     // scatter bases in digit-major, wave-minor order, digit-parallel: thread
@@ -783,20 +794,19 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
       for (int w = 0; w < kKdWaves; ++w) cnt[w * 256 + tid] = dbase + pre[w];
     }
     __syncthreads();
-    for (int tile = t_lo; tile < t_hi; ++tile) {
-      const int i = tile * kWave + lane;
+#pragma unroll
+    for (int j = 0; j < kTiles; ++j) {
+      if (t_lo + j >= t_hi) break;                     // wave-uniform
+      const int i = (t_lo + j) * kWave + lane;
       const bool valid = i < M;
-      const int key = valid ? ks[i] : 0;
-      const int d = ((unsigned)key >> shift) & 255;
-      const unsigned long long peers = digit_peers(d, valid);
-      const unsigned long long lower = peers & lanes_below();
-      const int b0 = valid ? mycnt[d] : 0;
+      const unsigned long long lower = tp[j] & lanes_below();
+      const int b0 = valid ? mycnt[td[j]] : 0;
       if (valid) {
         const int dst = b0 + __popcll(lower);
-        kd[dst] = key;
+        kd[dst] = tk[j];
         id[dst] = is[i];
       }
-      if (valid && lower == 0ull) mycnt[d] = b0 + __popcll(peers);
+      if (valid && lower == 0ull) mycnt[td[j]] = b0 + __popcll(tp[j]);
     }
     for (int i = lane; i < 256; i += kWave) mycnt[i] = 0;   // for the next pass
     __syncthreads();
