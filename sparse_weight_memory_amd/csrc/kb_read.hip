@@ -33,10 +33,30 @@
 // The k value rows are fetched as float4 per lane (coalesced 1 KiB per
 // wave-load) and kept in registers for the backward when they fit.
 
+#include "fwpkm.h"
 #include "fwpkm_device.h"
 #include "fwpkm_launch.h"
 
 namespace fwpkm {
+
+// Candidate c of the pruned Cartesian list for top-k, as (i << 8) | j: rows
+// i = 0, 1, ... of floor(k / (i + 1)) candidates each, in order.  A table
+// per k (it depends on k alone), so each lane's pair is one load issued with
+// the kernel's first loads instead of a loop of divisions.
+constexpr int kCartMax = 3 * kWave;     // sum_i floor(32 / i) = 130 candidates at most
+struct CartTable {
+  unsigned short ij[FWPKM_MAX_TOPK + 1][kCartMax];
+};
+constexpr CartTable make_cart_table() {
+  CartTable t{};
+  for (int k = 1; k <= FWPKM_MAX_TOPK; ++k) {
+    int c = 0;
+    for (int i = 0; i < k; ++i)
+      for (int j = 0; j < k / (i + 1); ++j) t.ij[k][c++] = (unsigned short)((i << 8) | j);
+  }
+  return t;
+}
+__constant__ CartTable kCart = make_cart_table();
 
 template <int KMAX, int VR, bool WRITE>
 __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
@@ -78,6 +98,12 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
       ov[h] = a.half_o[base + li];
     }
   }
+  // this lane's Cartesian candidates (lane + 64 r); the table's rows are
+  // zero past npr, and lanes past npr are masked below
+  constexpr int J = 3;                        // sum_i floor(32/i) = 130 <= 3 * 64
+  int cij[J];
+#pragma unroll
+  for (int r = 0; r < J; ++r) cij[r] = kCart.ij[k][lane + kWave * r];
   const float qn = (a.qnorm[ut * 2] + a.qnorm[ut * 2 + 1]) * (a.mode == 0 ? 1.f : 0.f);
   // token-importance weight of this token's loss; 0 = read only, no write.
   // Without weights the load reads this token's query norm instead (any
@@ -145,26 +171,16 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
 
   // ---- 2. pruned Cartesian candidates, then the k best
   const int npr = a.npr;
-  // floor(k / (i + 1)) without an integer divide: (k + 1/2) / (i + 1) lies at
-  // least 1/66 away from an integer, far more than the reciprocal's error
-  const float kh = (float)k + 0.5f;
-  auto row_len = [&](int i) { return (int)(kh * __builtin_amdgcn_rcpf((float)(i + 1))); };
   skey sel;
   {
-    constexpr int J = 3;   // sum_i floor(32/i) = 130 <= 3 * 64
     const int jr = (npr + kWave - 1) / kWave;   // rounds that hold candidates (1 for k <= 20)
     skey cx[J];
 #pragma unroll
     for (int r = 0; r < J; ++r) {
       cx[r] = kEmptyKey;
       if (r >= jr) continue;                     // wave-uniform
-      int c = lane + 64 * r;
-      const bool in = c < npr;
-      int i = 0;
-      if (in) {
-        for (int len = row_len(0); c >= len; len = row_len(i)) { c -= len; ++i; }
-      }
-      const int j = in ? c : 0;
+      const bool in = lane + 64 * r < npr;
+      const int i = cij[r] >> 8, j = cij[r] & 255;
       const skey ka = __shfl(hk[0], i, kWave);
       const skey kb = __shfl(hk[1], j, kWave);
       const int ia = key_index(ka), ib = key_index(kb);
