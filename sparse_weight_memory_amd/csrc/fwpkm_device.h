@@ -136,13 +136,17 @@ struct ChunkArgs {
   FastDiv div_upx;     // x / (U / 8): units per XCD
   FastDiv div_nbx;     // x / ceil(T / 4): read workgroups per unit
   // update-kernel geometry, derived on the host by its launcher: column
-  // slices of kd_sw floats, kd_sv of them per V row and kd_sk per K row,
-  // 2^kd_sg_bits groups of hash regions per (list, unit)
+  // slices, kd_sv of them per V row and kd_sk per K row; kd_gv hash groups
+  // of rows per value list and kd_gk per sub-key list
   int kd_sv;
   int kd_sk;
-  int kd_sg_bits;
-  FastDiv kd_div_pu;   // x / ((kd_sv + 2 kd_sk) << kd_sg_bits): workgroups per unit
-  FastDiv kd_div_sk;   // x / kd_sk
+  int kd_gv;
+  int kd_gk;
+  int kd_pu;           // workgroups per unit: kd_sv kd_gv + 2 kd_sk kd_gk
+  FastDiv kd_div_pu;   // x / kd_pu
+  FastDiv kd_div_gv;   // x / kd_gv
+  FastDiv kd_div_gk;   // x / kd_gk
+  FastDiv kd_div_kl;   // x / (kd_sk kd_gk): workgroups per sub-key list
   unsigned int* check; // one word of DeviceCheck bits (checked builds)
 };
 

@@ -48,6 +48,8 @@
 // one fixed order, results do not depend on scheduling, and no atomics are
 // used.
 
+#include <algorithm>
+
 #include "fwpkm_device.h"
 #include "fwpkm_launch.h"
 
@@ -199,31 +201,37 @@ __device__ __forceinline__ unsigned long long lanes_below() {
 
 // Hash group of a row among 2^bits: multiplicative (Fibonacci) hashing, so
 // rows that many tokens share spread over the groups.
-__device__ __forceinline__ int hash_group(int row, int bits) {
-  return bits == 0 ? 0 : (int)(((unsigned)row * 0x9E3779B1u) >> (32 - bits));
+__device__ __forceinline__ int hash_group(int row, int groups) {
+  // multiply-range reduction of the 32-bit hash: for 2^b groups, its top b bits
+  return (int)(((unsigned long long)((unsigned)row * 0x9E3779B1u) * (unsigned)groups) >> 32);
 }
 
 // Which (unit, list, column slice, hash group) an update workgroup owns.
+// Per unit: value-row slices times kd_gv groups, then K1's and K2's slices
+// times kd_gk groups each; the groups of a slice are adjacent.
 struct KdWho {
-  int u, list, slice, grp, b, hh, width4, col4;
+  int u, list, slice, grp, ngrp, b, hh, width4, col4;
 };
 
 __device__ __forceinline__ KdWho kd_who(const ChunkArgs& a, int L4) {
   KdWho w;
-  const int sg_bits = a.kd_sg_bits;
-  const int combos = a.kd_sv + 2 * a.kd_sk;
-  const int item = unit_affine_item(blockIdx.x, a.U, combos << sg_bits);
+  const int item = unit_affine_item(blockIdx.x, a.U, a.kd_pu);
   w.u = fast_div(item, a.kd_div_pu);
-  const int rest = item - w.u * (combos << sg_bits);
-  const int combo = rest >> sg_bits;
-  w.grp = rest & ((1 << sg_bits) - 1);
-  w.list = 0;
-  w.slice = combo;
-  if (combo >= a.kd_sv) {
-    const int c2 = combo - a.kd_sv;
-    const int hk = fast_div(c2, a.kd_div_sk);
+  const int rest = item - w.u * a.kd_pu;
+  const int nv = a.kd_sv * a.kd_gv;
+  if (rest < nv) {
+    w.list = 0;
+    w.slice = fast_div(rest, a.kd_div_gv);
+    w.grp = rest - w.slice * a.kd_gv;
+    w.ngrp = a.kd_gv;
+  } else {
+    const int r2 = rest - nv;
+    const int hk = fast_div(r2, a.kd_div_kl);          // / (kd_sk * kd_gk)
+    const int r3 = r2 - hk * a.kd_sk * a.kd_gk;
     w.list = 1 + hk;
-    w.slice = c2 - hk * a.kd_sk;
+    w.slice = fast_div(r3, a.kd_div_gk);
+    w.grp = r3 - w.slice * a.kd_gk;
+    w.ngrp = a.kd_gk;
   }
   w.width4 = (w.list == 0 ? a.dv : a.half) >> 2;   // float4 per row
   w.col4 = w.slice * L4;                             // first float4 column of the slice
@@ -283,7 +291,7 @@ struct KdSeg {
 
 // The segments (runs of one row) of the entries [0, cut), in LDS: rows
 // ent_row, tokens ent_t, weights ent_w (float bits), ordered by
-// (hash_group(row, order_bits), row) -- by row alone with order_bits = 0 --
+// (hash_group(row, order_groups), row) -- by row alone with one group --
 // so every row's entries are one run; each row's mean gradient is applied to
 // its slice of the table.  cut <= kKdEntCap.
 // Ends after a barrier-free phase: the caller synchronises before reusing
@@ -292,7 +300,7 @@ template <int L4>
 __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho& who,
                                                 const float4* dat, const int* ent_row,
                                                 const int* ent_t, const int* ent_w, int cut,
-                                                const KdSeg& S, int order_bits) {
+                                                const KdSeg& S, int order_groups) {
   int* seg_beg = S.seg_beg;
   int* seg_item = S.seg_item;
   int* short_seg = S.short_seg;
@@ -332,7 +340,7 @@ __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho&
         device_check(a, ent_row[e] >= 0 && ent_row[e] < rows && ent_t[e] >= 0 && ent_t[e] < a.T, kChkEntry);
         if (e > 0) {
           const int r0 = ent_row[e - 1], r1 = ent_row[e];
-          const int g0 = hash_group(r0, order_bits), g1 = hash_group(r1, order_bits);
+          const int g0 = hash_group(r0, order_groups), g1 = hash_group(r1, order_groups);
           device_check(a, g0 < g1 || (g0 == g1 && r0 <= r1), kChkOrder);
         }
       }
@@ -554,7 +562,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
   const int64_t lbase = ((int64_t)who.list * a.U + who.u) * a.P;
 
   // ---- this group's run of entries: regions [r0, r0 + RG) (wave 0)
-  const int RG = a.regions >> a.kd_sg_bits;
+  const int RG = a.regions / who.ngrp;                    // groups are runs of regions
   const int r0 = who.grp * RG;
   if (wave == 0) {
     int4 kd = make_int4(0, 0, 0, 0);
@@ -625,7 +633,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
 #pragma unroll
       for (int w = 0; w < kKdWaves; ++w) cut = max(cut, red[kKdWaves + w]);
     }
-    kd_sum_segments<L4>(a, who, dat, ent_row, ent_t, ent_w, cut, S, a.region_bits);
+    kd_sum_segments<L4>(a, who, dat, ent_row, ent_t, ent_w, cut, S, a.regions);
     done += cut;
     __syncthreads();                 // the staged entries are reused
   }
@@ -711,7 +719,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
     const int i = (wave * tpw + j) * kWave + lane;
     const bool in = j < tpw && i < P;
     if (in) wl[i] = __float_as_int(wr[j]);
-    const bool mine = in && kr[j] != invalid && hash_group(kr[j], a.kd_sg_bits) == who.grp;
+    const bool mine = in && kr[j] != invalid && hash_group(kr[j], who.ngrp) == who.grp;
     kept += __popcll(__ballot(mine));
   }
   if (lane == 0) red[wave] = kept;
@@ -727,7 +735,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   for (int j = 0; j < kTiles; ++j) {
     const int i = (wave * tpw + j) * kWave + lane;
     const bool in = j < tpw && i < P;
-    const bool mine = in && kr[j] != invalid && hash_group(kr[j], a.kd_sg_bits) == who.grp;
+    const bool mine = in && kr[j] != invalid && hash_group(kr[j], who.ngrp) == who.grp;
     const unsigned long long m = __ballot(mine);
     if (mine) {
       const int pos = base + __popcll(m & lanes_below());
@@ -834,7 +842,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   S.part_c = reinterpret_cast<float*>(lds + LL.part_c);
   S.long_seg = reinterpret_cast<int*>(lds + LL.long_seg);
   S.red = red;
-  kd_sum_segments<L4>(a, who, dat, ks, ent_t, ent_w, M, S, 0);
+  kd_sum_segments<L4>(a, who, dat, ks, ent_t, ent_w, M, S, 1);
 }
 
 namespace {
@@ -846,7 +854,7 @@ int kd_slice_width(int T) {
 
 template <int SW>
 hipError_t launch_kd_as(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {
-  const int64_t per_unit = (int64_t)(a.kd_sv + 2 * a.kd_sk) << a.kd_sg_bits;
+  const int64_t per_unit = a.kd_pu;
   const dim3 grid((unsigned)(per_unit * a.U));
   if (kd_fuses_grouping(a)) {
     static const hipError_t attr = hipFuncSetAttribute(
@@ -871,20 +879,44 @@ hipError_t launch_kd(const ChunkArgs& args, hipStream_t s, const LaunchTiming* t
   const int sw = kd_slice_width(a.T);
   a.kd_sv = (a.dv + sw - 1) / sw;
   a.kd_sk = (a.half + sw - 1) / sw;
-  const int combos = a.kd_sv + 2 * a.kd_sk;
-  // hash groups of rows per (list, unit): about one workgroup per compute
-  // unit in all, and (unfused) about two batches of entries per group at
-  // most (P / groups <= 2 kKdEntCap on average), so
-  // that a list with many distinct rows does not leave half the chip idle
-  // behind a few long workgroups.  Unfused, a group is a run of the grouping
-  // kernel's regions.
-  const int most = kd_fuses_grouping(a) ? 64 : a.regions;
-  int sg = 1, bits = 0;
-  while (sg * 2 <= most && (int64_t)a.U * combos * sg * 2 <= 256) { sg *= 2; ++bits; }
-  while (sg * 2 <= most && (int64_t)sg * 2 * kKdEntCap < a.P) { sg *= 2; ++bits; }
-  a.kd_sg_bits = bits;
-  a.kd_div_pu = make_fastdiv(combos << bits);
-  a.kd_div_sk = make_fastdiv(a.kd_sk);
+  int gv = 1, gk = 1;
+  if (kd_fuses_grouping(a)) {
+    // hash groups per (list, unit): each workgroup sorts its group's entries
+    // and sums them, so its work goes as entries x (radix passes + 1).  A
+    // value list holds P entries over n^2 rows; a sub-key list about P/2 (a
+    // token's candidates sharing a sub-key row are merged) over n rows.  The
+    // counts (gv, gk) even out the two kinds of workgroup within one
+    // workgroup per compute unit in all.
+    auto passes = [](int64_t rows) { int b = 0; while (b < 40 && ((rows - 1) >> b) != 0) ++b; return (b + 7) / 8; };
+    const double cost_v = (double)a.P * (passes((int64_t)a.n * a.n) + 1);
+    const double cost_k = 0.5 * a.P * (passes(a.n) + 1);
+    const int64_t most = std::max<int64_t>(256, (int64_t)a.U * (a.kd_sv + 2 * a.kd_sk));
+    double best = 1e300;
+    for (int v = 1; v <= 64; ++v)
+      for (int q = 1; q <= 64; ++q) {
+        if ((int64_t)a.U * (a.kd_sv * v + 2 * a.kd_sk * q) > most) break;
+        const double c = std::max(cost_v / v, cost_k / q);
+        if (c < best * (1.0 - 1e-9)) { best = c; gv = v; gk = q; }
+      }
+  } else {
+    // unfused, a group is a run of the grouping kernel's regions (a power of
+    // two of them): about one workgroup per compute unit in all, and about
+    // two batches of entries per group at most (P / groups <= 2 kKdEntCap on
+    // average), so that a list with many distinct rows does not leave half
+    // the chip idle behind a few long workgroups
+    const int combos = a.kd_sv + 2 * a.kd_sk;
+    int sg = 1;
+    while (sg * 2 <= a.regions && (int64_t)a.U * combos * sg * 2 <= 256) sg *= 2;
+    while (sg * 2 <= a.regions && (int64_t)sg * 2 * kKdEntCap < a.P) sg *= 2;
+    gv = gk = sg;
+  }
+  a.kd_gv = gv;
+  a.kd_gk = gk;
+  a.kd_pu = a.kd_sv * gv + 2 * a.kd_sk * gk;
+  a.kd_div_pu = make_fastdiv(a.kd_pu);
+  a.kd_div_gv = make_fastdiv(gv);
+  a.kd_div_gk = make_fastdiv(gk);
+  a.kd_div_kl = make_fastdiv(a.kd_sk * gk);
   if (sw == 64) return launch_kd_as<64>(a, s, tm);
   if (sw == 32) return launch_kd_as<32>(a, s, tm);
   return launch_kd_as<16>(a, s, tm);
