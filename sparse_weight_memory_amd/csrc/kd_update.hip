@@ -289,47 +289,13 @@ struct KdSeg {
   int* red;         // [4 * kKdWaves] block-scan scratch
 };
 
-// The segments (runs of one row) of the entries [0, cut), in LDS: rows
-// ent_row, tokens ent_t, weights ent_w (float bits), ordered by
-// (hash_group(row, order_groups), row) -- by row alone with one group --
-// so every row's entries are one run; each row's mean gradient is applied to
-// its slice of the table.  cut <= kKdEntCap.
-// Ends after a barrier-free phase: the caller synchronises before reusing
-// the scratch.
+// Checked builds: every entry [0, cut) in range, ordered by
+// (hash_group(row, order_groups), row), and cut within the LDS lists.
 template <int L4>
-__device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho& who,
-                                                const float4* dat, const int* ent_row,
-                                                const int* ent_t, const int* ent_w, int cut,
-                                                const KdSeg& S, int order_groups) {
-  int* seg_beg = S.seg_beg;
-  int* seg_item = S.seg_item;
-  int* short_seg = S.short_seg;
-  int* items = S.items;
-  float4* part = S.part;
-  float* part_c = S.part_c;
-  int* long_seg = S.long_seg;
-  int* red = S.red;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int c4 = lane & (L4 - 1), pg = lane / L4;
-  const int width4 = who.width4, col4 = who.col4;
-  const bool col_ok = col4 + c4 < width4;
-  const float lr = a.lr;
-  const bool idw_key = who.list != 0 && a.mode == 0;
-  float* tbase = who.list == 0
-      ? a.v + (int64_t)who.b * a.stride_v + (int64_t)who.hh * a.n * a.n * a.dv
-      : (who.list == 1 ? a.k1 : a.k2) + (int64_t)who.b * a.stride_k + (int64_t)who.hh * a.n * a.half;
-  const int rstride = who.list == 0 ? a.dv : a.half;
-
-  // entries tid * kKdPer + j: contiguous per thread, so segment starts
-  // come out in order from one scan
-  bool hd[kKdPer];
-  int nh = 0;
-#pragma unroll
-  for (int j = 0; j < kKdPer; ++j) {
-    const int e = tid * kKdPer + j;
-    hd[j] = e < cut && (e == 0 || ent_row[e] != ent_row[e - 1]);
-    nh += hd[j];
-  }
+__device__ __forceinline__ void kd_check_entries(const ChunkArgs& a, const KdWho& who, const int* ent_row,
+                                                 const int* ent_t, int cut, int order_groups) {
+  const int tid = threadIdx.x;
+  (void)a; (void)who; (void)ent_row; (void)ent_t; (void)cut; (void)order_groups; (void)tid;
 #if FWPKM_DEVICE_CHECKS
   {
     const int rows = who.list == 0 ? a.n * a.n : a.n;
@@ -348,46 +314,40 @@ __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho&
     if (tid == 0) device_check(a, cut <= kKdEntCap, kChkCapacity);
   }
 #endif
-  int nseg;
-  int sp = kd_block_scan(nh, red, &nseg);
-#pragma unroll
-  for (int j = 0; j < kKdPer; ++j)
-    if (hd[j]) seg_beg[sp++] = tid * kKdPer + j;
-  if (tid == 0) seg_beg[nseg] = cut;
-  __syncthreads();
-  // ---- work.  A segment of at most L4 pairs is short: PG of them share
-  // one pass of a wave, one per pair group.  A longer segment is cut into
-  // kKdPiece-pair pieces, each summed by a whole wave; the pieces of a
-  // segment longer than kKdPiece meet in `part`.
+}
+
+// The sums of segments whose tables are built: segment s is entries
+// [seg_beg[s], seg_beg[s + 1]), its fields in seg_item[s] (short index |
+// first piece << 12 | first slot << 22); short segments listed in
+// short_seg, pieces of longer ones in items (segment << 5 | piece), the
+// first slot of each segment of more than kKdPiece pairs in long_seg (-1 on
+// the rest).  Each row's mean gradient is applied to its slice of the table.
+// Ends after a barrier-free phase: the caller synchronises before reusing
+// the scratch.
+template <int L4>
+__device__ __forceinline__ void kd_segment_sums(const ChunkArgs& a, const KdWho& who, const float4* dat,
+                                                const int* ent_row, const int* ent_t, const int* ent_w,
+                                                const KdSeg& S, int nshort, int npieces, int nslots) {
+  int* seg_beg = S.seg_beg;
+  int* seg_item = S.seg_item;
+  int* short_seg = S.short_seg;
+  int* items = S.items;
+  float4* part = S.part;
+  float* part_c = S.part_c;
+  int* long_seg = S.long_seg;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int c4 = lane & (L4 - 1), pg = lane / L4;
+  const int width4 = who.width4, col4 = who.col4;
+  const bool col_ok = col4 + c4 < width4;
+  const float lr = a.lr;
+  const bool idw_key = who.list != 0 && a.mode == 0;
+  float* tbase = who.list == 0
+      ? a.v + (int64_t)who.b * a.stride_v + (int64_t)who.hh * a.n * a.n * a.dv
+      : (who.list == 1 ? a.k1 : a.k2) + (int64_t)who.b * a.stride_k + (int64_t)who.hh * a.n * a.half;
+  const int rstride = who.list == 0 ? a.dv : a.half;
+
   {
     constexpr int PG = kWave / L4;
-    int sh[kKdPer], pcs[kKdPer], slt[kKdPer], tot = 0;
-#pragma unroll
-    for (int j = 0; j < kKdPer; ++j) {
-      const int si = tid * kKdPer + j;
-      const int len = si < nseg ? seg_beg[si + 1] - seg_beg[si] : 0;
-      sh[j] = si < nseg && len <= L4 ? 1 : 0;
-      pcs[j] = len > L4 ? (len + kKdPiece - 1) / kKdPiece : 0;
-      slt[j] = len > kKdPiece ? pcs[j] : 0;
-      tot += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
-    }
-    int total;
-    int pre = kd_block_scan(tot, red + 2 * kKdWaves, &total);
-#pragma unroll
-    for (int j = 0; j < kKdPer; ++j) {
-      const int si = tid * kKdPer + j;
-      if (si < nseg) {
-        seg_item[si] = pre;          // short index | first piece << 12 | first slot << 22
-        if (sh[j]) short_seg[pre & 0xfff] = si;
-        for (int q = 0; q < pcs[j]; ++q) items[((pre >> 12) & 0x3ff) + q] = (si << 5) | q;
-        for (int q = 0; q < slt[j]; ++q) long_seg[(pre >> 22) + q] = q == 0 ? si : -1;
-      }
-      pre += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
-    }
-    __syncthreads();
-    const int nshort = total & 0xfff;
-    const int npieces = (total >> 12) & 0x3ff;
-    const int nslots = total >> 22;
     if (tid == 0) device_check(a, nshort <= kKdEntCap && npieces <= kKdMaxPieces && nslots <= kKdMaxLong, kChkCapacity);
     const int npass = (nshort + PG - 1) / PG;
 
@@ -533,6 +493,78 @@ __device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho&
   }
 }
 
+
+// The segments (runs of one row) of the entries [0, cut), in LDS: rows
+// ent_row, tokens ent_t, weights ent_w (float bits), ordered by
+// (hash_group(row, order_groups), row) -- by row alone with one group --
+// so every row's entries are one run: their tables, then their sums.
+// cut <= kKdEntCap.  Ends like kd_segment_sums.
+template <int L4>
+__device__ __forceinline__ void kd_sum_segments(const ChunkArgs& a, const KdWho& who,
+                                                const float4* dat, const int* ent_row,
+                                                const int* ent_t, const int* ent_w, int cut,
+                                                const KdSeg& S, int order_groups) {
+  int* seg_beg = S.seg_beg;
+  int* seg_item = S.seg_item;
+  int* short_seg = S.short_seg;
+  int* items = S.items;
+  int* long_seg = S.long_seg;
+  int* red = S.red;
+  const int tid = threadIdx.x;
+  kd_check_entries<L4>(a, who, ent_row, ent_t, cut, order_groups);
+  // entries tid * kKdPer + j: contiguous per thread, so segment starts
+  // come out in order from one scan
+  bool hd[kKdPer];
+  int nh = 0;
+#pragma unroll
+  for (int j = 0; j < kKdPer; ++j) {
+    const int e = tid * kKdPer + j;
+    hd[j] = e < cut && (e == 0 || ent_row[e] != ent_row[e - 1]);
+    nh += hd[j];
+  }
+  int nseg;
+  int sp = kd_block_scan(nh, red, &nseg);
+#pragma unroll
+  for (int j = 0; j < kKdPer; ++j)
+    if (hd[j]) seg_beg[sp++] = tid * kKdPer + j;
+  if (tid == 0) seg_beg[nseg] = cut;
+  __syncthreads();
+  // ---- work.  A segment of at most L4 pairs is short: kWave / L4 of them
+  // share one pass of a wave, one per pair group.  A longer segment is cut
+  // into kKdPiece-pair pieces, each summed by a whole wave; the pieces of a
+  // segment longer than kKdPiece meet in `part`.
+  {
+    int sh[kKdPer], pcs[kKdPer], slt[kKdPer], tot = 0;
+#pragma unroll
+    for (int j = 0; j < kKdPer; ++j) {
+      const int si = tid * kKdPer + j;
+      const int len = si < nseg ? seg_beg[si + 1] - seg_beg[si] : 0;
+      sh[j] = si < nseg && len <= L4 ? 1 : 0;
+      pcs[j] = len > L4 ? (len + kKdPiece - 1) / kKdPiece : 0;
+      slt[j] = len > kKdPiece ? pcs[j] : 0;
+      tot += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
+    }
+    int total;
+    int pre = kd_block_scan(tot, red + 2 * kKdWaves, &total);
+#pragma unroll
+    for (int j = 0; j < kKdPer; ++j) {
+      const int si = tid * kKdPer + j;
+      if (si < nseg) {
+        seg_item[si] = pre;          // short index | first piece << 12 | first slot << 22
+        if (sh[j]) short_seg[pre & 0xfff] = si;
+        for (int q = 0; q < pcs[j]; ++q) items[((pre >> 12) & 0x3ff) + q] = (si << 5) | q;
+        for (int q = 0; q < slt[j]; ++q) long_seg[(pre >> 22) + q] = q == 0 ? si : -1;
+      }
+      pre += sh[j] | (pcs[j] << 12) | (slt[j] << 22);
+    }
+    __syncthreads();
+    const int nshort = total & 0xfff;
+    const int npieces = (total >> 12) & 0x3ff;
+    const int nslots = total >> 22;
+    kd_segment_sums<L4>(a, who, dat, ent_row, ent_t, ent_w, S, nshort, npieces, nslots);
+  }
+}
+
 }  // namespace
 
 // Large chunks: entries grouped by the grouping kernel (kc_sort).
@@ -645,7 +677,8 @@ constexpr int kKwCntInts = (kKdWaves * 256 > 2 * kKdEntCap + 1 ? kKdWaves * 256 
 // LDS layout (byte offsets) of the fused kernel: chunks of T tokens, slices
 // of SW floats, at most kKdEntCap pairs per unit.
 struct KwLds {
-  int dat, key0, idx0, key1, idx1, wl, cnt, items, part, part_c, long_seg, red, total;
+  int dat, key0, idx0, key1, idx1, wl, cnt, items, part, part_c, long_seg, red, dbeg, ditem, dshort, rowof,
+      total;
 };
 __host__ __device__ constexpr KwLds kw_lds_layout(int T, int SW) {
   KwLds L{};
@@ -662,6 +695,10 @@ __host__ __device__ constexpr KwLds kw_lds_layout(int T, int SW) {
   L.part_c = o; o = kd_align(o + kKdMaxLong * 4);
   L.long_seg = o; o = kd_align(o + kKdMaxLong * 4);
   L.red = o;    o = kd_align(o + 4 * kKdWaves * 4);
+  L.dbeg = o;   o = kd_align(o + (256 + 1) * 4);                  // segment tables when one digit is one row
+  L.ditem = o;  o = kd_align(o + 256 * 4);
+  L.dshort = o; o = kd_align(o + 256 * 4);
+  L.rowof = o;  o = kd_align(o + 256 * 4);                        // row of each rank (renamed rows)
   L.total = o;
   return L;
 }
@@ -754,12 +791,62 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   const int rmax = invalid - 1;
   int bits = 0;
   while (bits < 31 && (rmax >> bits) != 0) ++bits;
-  const int passes = max(1, (bits + 7) / 8);
+  int passes = max(1, (bits + 7) / 8);
   const int vtiles = (M + kWave - 1) / kWave;
   const int vtpw = (vtiles + kKdWaves - 1) / kKdWaves;
   const int t_lo = wave * vtpw, t_hi = min(vtiles, t_lo + vtpw);
   int* mycnt = cnt + wave * 256;
   int *ks = key0, *is = idx0, *kd = key1, *id = idx1;
+  int* items = reinterpret_cast<int*>(lds + LL.items);
+  int* long_seg = reinterpret_cast<int*>(lds + LL.long_seg);
+  int* dbeg = reinterpret_cast<int*>(lds + LL.dbeg);
+  int* ditem = reinterpret_cast<int*>(lds + LL.ditem);
+  int* dshort = reinterpret_cast<int*>(lds + LL.dshort);
+  int* row_of = reinterpret_cast<int*>(lds + LL.rowof);
+
+  // ---- rows of up to 16 bits (two passes): each renamed to its rank among
+  // the group's distinct rows, from a bitmap of the rows present and a scan
+  // of its words' popcounts (ranks keep the rows' order).  With at most 256
+  // distinct rows one 8-bit pass then sorts them, and its digit is the row.
+  // The bitmap and its scan use the segment sums' scratch, free until then.
+  bool renamed = false;
+  static_assert(kKdMaxLong * 16 * 16 >= 2 * 2048 * 4, "bitmap and scan fit the sums' scratch at SW = 64");
+  if (SW == 64 && passes == 2) {                               // block-uniform
+    unsigned int* bm = reinterpret_cast<unsigned int*>(lds + LL.part);   // [2048] words
+    int* wpre = reinterpret_cast<int*>(lds + LL.part) + 2048;            // [2048]
+    static_assert(kKdThreads * 2 == 2048, "two bitmap words per thread");
+    bm[2 * tid] = 0u;
+    bm[2 * tid + 1] = 0u;
+    __syncthreads();
+    for (int tile = t_lo; tile < t_hi; ++tile) {
+      const int i = tile * kWave + lane;
+      if (i < M) atomicOr(&bm[(unsigned)ks[i] >> 5], 1u << (ks[i] & 31));
+    }
+    __syncthreads();
+    const unsigned int w0 = bm[2 * tid], w1 = bm[2 * tid + 1];
+    int D;
+    const int pre = kd_block_scan(__popc(w0) + __popc(w1), red, &D);
+    wpre[2 * tid] = pre;
+    wpre[2 * tid + 1] = pre + __popc(w0);
+    __syncthreads();
+    if (D <= 256) {                                            // block-uniform
+      for (int tile = t_lo; tile < t_hi; ++tile) {
+        const int i = tile * kWave + lane;
+        if (i < M) {
+          const int r = ks[i];
+          const int d = wpre[r >> 5] + __popc(bm[r >> 5] & ((1u << (r & 31)) - 1u));
+          ks[i] = d;
+          row_of[d] = r;                       // every entry of the row writes the same value
+        }
+      }
+      passes = 1;
+      renamed = true;
+      __syncthreads();
+    }
+  }
+  // one pass whose digit is the row: the segments are the digits present,
+  // and the last pass's scan builds their tables
+  const bool direct = passes == 1;
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * 8;
     // each tile's lanes with equal digits (ballots), counted once by the
@@ -781,11 +868,15 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
     __syncthreads();
     // scatter bases in digit-major, wave-minor order, digit-parallel: thread
     // d < 256 (waves 0-3) runs over the waves' counters of digit d, then the
-    // digits' totals are scanned across those four waves
+    // digits' totals are scanned across those four waves.  When the digit is
+    // the row (last pass of the direct path), the same scan numbers the
+    // digits present (the segments) and sums their fields: short (at most
+    // L4 pairs), pieces of kKdPiece pairs, slots of segments longer than one
+    // piece.
+    const bool tables = direct && pass == passes - 1;   // block-uniform
     int pre[kKdWaves];
-    int dbase = 0;
+    int dbase = 0, run = 0, nz = 0, pk = 0, inz = 0, ipk = 0, pcs = 0, slt = 0;
     if (tid < 256) {                                     // whole waves 0-3
-      int run = 0;
 #pragma unroll
       for (int w = 0; w < kKdWaves; ++w) {
         pre[w] = run;
@@ -794,12 +885,46 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
       const int incl = wave_inclusive_scan(run);
       if (lane == kWave - 1) red[wave] = incl;
       dbase = incl - run;
+      if (tables) {
+        nz = run > 0 ? 1 : 0;
+        pcs = run > L4 ? (run + kKdPiece - 1) / kKdPiece : 0;
+        slt = run > kKdPiece ? pcs : 0;
+        pk = nz ? ((run <= L4 ? 1 : 0) | (pcs << 12) | (slt << 22)) : 0;
+        inz = wave_inclusive_scan(nz);
+        ipk = wave_inclusive_scan(pk);
+        if (lane == kWave - 1) {
+          red[kKdWaves + wave] = inz;
+          red[2 * kKdWaves + wave] = ipk;
+        }
+      }
     }
     __syncthreads();
     if (tid < 256) {
-      for (int w = 0; w < wave; ++w) dbase += red[w];
+      int bz = 0, bp = 0;
+      for (int w = 0; w < wave; ++w) {
+        dbase += red[w];
+        if (tables) {
+          bz += red[kKdWaves + w];
+          bp += red[2 * kKdWaves + w];
+        }
+      }
 #pragma unroll
       for (int w = 0; w < kKdWaves; ++w) cnt[w * 256 + tid] = dbase + pre[w];
+      if (tables) {
+        const int sgi = bz + inz - nz;                 // segment number of this digit
+        const int pp = bp + ipk - pk;                  // fields of the segments before it
+        if (nz) {
+          dbeg[sgi] = dbase;
+          ditem[sgi] = pp;
+          if (run <= L4) dshort[pp & 0xfff] = sgi;
+          for (int q = 0; q < pcs; ++q) items[((pp >> 12) & 0x3ff) + q] = (sgi << 5) | q;
+          for (int q = 0; q < slt; ++q) long_seg[(pp >> 22) + q] = q == 0 ? sgi : -1;
+        }
+        if (tid == 255) {
+          dbeg[bz + inz] = M;
+          red[3 * kKdWaves] = bp + ipk;                // totals of the fields
+        }
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -831,18 +956,28 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
     const int p = is[i];
     ent_t[i] = token_of(p, a.k);
     ent_w[i] = wl[p];
+    if (renamed) ks[i] = row_of[ks[i]];
   }
   __syncthreads();
   KdSeg S;
-  S.seg_beg = cnt;
-  S.seg_item = cnt + kKdEntCap + 1;
-  S.short_seg = wl;
-  S.items = reinterpret_cast<int*>(lds + LL.items);
+  S.items = items;
   S.part = reinterpret_cast<float4*>(lds + LL.part);
   S.part_c = reinterpret_cast<float*>(lds + LL.part_c);
-  S.long_seg = reinterpret_cast<int*>(lds + LL.long_seg);
+  S.long_seg = long_seg;
   S.red = red;
-  kd_sum_segments<L4>(a, who, dat, ks, ent_t, ent_w, M, S, 1);
+  if (direct) {
+    S.seg_beg = dbeg;
+    S.seg_item = ditem;
+    S.short_seg = dshort;
+    const int tot = red[3 * kKdWaves];
+    kd_check_entries<L4>(a, who, ks, ent_t, M, 1);
+    kd_segment_sums<L4>(a, who, dat, ks, ent_t, ent_w, S, tot & 0xfff, (tot >> 12) & 0x3ff, tot >> 22);
+  } else {
+    S.seg_beg = cnt;
+    S.seg_item = cnt + kKdEntCap + 1;
+    S.short_seg = wl;
+    kd_sum_segments<L4>(a, who, dat, ks, ent_t, ent_w, M, S, 1);
+  }
 }
 
 namespace {

@@ -189,6 +189,24 @@ def test_update_geometry_at_wide_chunks(C, mode):
     compare_chunk(mem, st, q, y, 1.0, units=[0, 3, 7], label=f"wide C{C} {mode}")
 
 
+@pytest.mark.parametrize("C,k", [(300, 4), (700, 2)])
+def test_fused_update_at_narrow_slices(C, k):
+    """At most 2,048 pairs per unit keep the grouping inside the update
+    kernel while chunks of more than 256 and 512 tokens narrow its column
+    slices to 32 and 16 floats: the sub-key lists (n = 64, one radix pass)
+    take their segment tables straight from the digit counts there, and the
+    value rows (12 bits) go through two passes.  Half the tokens repeat 4
+    queries, as above."""
+    need_gpu()
+    B, H, n, half, dv = 8, 1, 64, 64, 256
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=C, num_heads=H,
+               max_batch=B)
+    st, q, y = _random_case(800 + C + k, B, H, C, n, half, dv)
+    rep = np.arange(C) % 2 == 0
+    q[:, rep] = q[:, [t % 8 for t in range(C) if rep[t]]]
+    compare_chunk(mem, st, q, y, 1.0, units=[0, 3, 7], label=f"narrow C{C} k{k}")
+
+
 def test_closed_form_k1_single_token_writes_target():
     need_gpu()
     n, half, dv = 16, 8, 32
