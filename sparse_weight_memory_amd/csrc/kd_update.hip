@@ -749,6 +749,24 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   float4 v[kKdStageMax];
   kd_stage_load<L4>(a, who, v);
   for (int i = lane; i < 256; i += kWave) cnt[wave * 256 + i] = 0;   // this wave's digit counters
+  // radix passes the rows need (8-bit digits)
+  const int rmax = invalid - 1;
+  int bits = 0;
+  while (bits < 31 && (rmax >> bits) != 0) ++bits;
+  int passes = max(1, (bits + 7) / 8);
+  // rows of up to 16 bits (two passes) may be renamed to their rank among
+  // the group's distinct rows (below): a bitmap of the rows present, in the
+  // segment sums' scratch (free until then), cleared here and filled by the
+  // compaction
+  static_assert(kKdMaxLong * 16 * 16 >= 2 * 2048 * 4, "bitmap and scan fit the sums' scratch at SW = 64");
+  static_assert(kKdThreads * 2 == 2048, "two bitmap words per thread");
+  const bool try_rename = SW == 64 && passes == 2;             // block-uniform
+  unsigned int* bm = reinterpret_cast<unsigned int*>(lds + LL.part);   // [2048] words
+  int* wpre = reinterpret_cast<int*>(lds + LL.part) + 2048;            // [2048]
+  if (try_rename) {
+    bm[2 * tid] = 0u;
+    bm[2 * tid + 1] = 0u;
+  }
   // ---- keep this group's rows, in pair order
   int kept = 0;
 #pragma unroll
@@ -778,6 +796,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
       const int pos = base + __popcll(m & lanes_below());
       key0[pos] = kr[j];
       idx0[pos] = i;
+      if (try_rename) atomicOr(&bm[(unsigned)kr[j] >> 5], 1u << (kr[j] & 31));
     }
     base += __popcll(m);
   }
@@ -788,10 +807,6 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   // digits, as many passes as the largest row needs.  Wave w owns entry
   // tiles [t_lo, t_hi) and its own digit counters; the scatter base of a
   // (digit, wave) is an exclusive scan in digit-major order.
-  const int rmax = invalid - 1;
-  int bits = 0;
-  while (bits < 31 && (rmax >> bits) != 0) ++bits;
-  int passes = max(1, (bits + 7) / 8);
   const int vtiles = (M + kWave - 1) / kWave;
   const int vtpw = (vtiles + kKdWaves - 1) / kKdWaves;
   const int t_lo = wave * vtpw, t_hi = min(vtiles, t_lo + vtpw);
@@ -804,45 +819,23 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   int* dshort = reinterpret_cast<int*>(lds + LL.dshort);
   int* row_of = reinterpret_cast<int*>(lds + LL.rowof);
 
-  // ---- rows of up to 16 bits (two passes): each renamed to its rank among
-  // the group's distinct rows, from a bitmap of the rows present and a scan
-  // of its words' popcounts (ranks keep the rows' order).  With at most 256
-  // distinct rows one 8-bit pass then sorts them, and its digit is the row.
-  // The bitmap and its scan use the segment sums' scratch, free until then.
+  // ---- rows of up to 16 bits: the rank of a row among the group's
+  // distinct rows is the popcount of the bitmap below it (a scan of the
+  // words' popcounts, then one word); ranks keep the rows' order.  With at
+  // most 256 distinct rows one 8-bit pass then sorts the ranks, its digit
+  // the row; the counting pass renames the entries as it reads them.
   bool renamed = false;
-  static_assert(kKdMaxLong * 16 * 16 >= 2 * 2048 * 4, "bitmap and scan fit the sums' scratch at SW = 64");
-  if (SW == 64 && passes == 2) {                               // block-uniform
-    unsigned int* bm = reinterpret_cast<unsigned int*>(lds + LL.part);   // [2048] words
-    int* wpre = reinterpret_cast<int*>(lds + LL.part) + 2048;            // [2048]
-    static_assert(kKdThreads * 2 == 2048, "two bitmap words per thread");
-    bm[2 * tid] = 0u;
-    bm[2 * tid + 1] = 0u;
-    __syncthreads();
-    for (int tile = t_lo; tile < t_hi; ++tile) {
-      const int i = tile * kWave + lane;
-      if (i < M) atomicOr(&bm[(unsigned)ks[i] >> 5], 1u << (ks[i] & 31));
-    }
-    __syncthreads();
+  if (try_rename) {
     const unsigned int w0 = bm[2 * tid], w1 = bm[2 * tid + 1];
     int D;
     const int pre = kd_block_scan(__popc(w0) + __popc(w1), red, &D);
     wpre[2 * tid] = pre;
     wpre[2 * tid + 1] = pre + __popc(w0);
-    __syncthreads();
     if (D <= 256) {                                            // block-uniform
-      for (int tile = t_lo; tile < t_hi; ++tile) {
-        const int i = tile * kWave + lane;
-        if (i < M) {
-          const int r = ks[i];
-          const int d = wpre[r >> 5] + __popc(bm[r >> 5] & ((1u << (r & 31)) - 1u));
-          ks[i] = d;
-          row_of[d] = r;                       // every entry of the row writes the same value
-        }
-      }
       passes = 1;
       renamed = true;
-      __syncthreads();
     }
+    __syncthreads();
   }
   // one pass whose digit is the row: the segments are the digits present,
   // and the last pass's scan builds their tables
@@ -861,6 +854,11 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
       const int i = (t_lo + j) * kWave + lane;
       const bool valid = i < M;
       tk[j] = valid ? ks[i] : 0;
+      if (renamed && valid) {
+        const int r = tk[j];
+        tk[j] = wpre[r >> 5] + __popc(bm[r >> 5] & ((1u << (r & 31)) - 1u));
+        row_of[tk[j]] = r;                     // every entry of the row writes the same value
+      }
       td[j] = ((unsigned)tk[j] >> shift) & 255;
       tp[j] = digit_peers(td[j], valid);
       if (valid && (tp[j] & lanes_below()) == 0ull) mycnt[td[j]] += __popcll(tp[j]);
