@@ -21,7 +21,7 @@
 // wave-wide load of matrix operands straight from memory would touch 16 key
 // rows at once, which the load path serves at a fraction of its rate).
 // When every chunk of the wave's dims is full, whole-line direct loads
-// (global_load_lds_dwordx4) fill a ring of four 32-dim slots; otherwise
+// (global_load_lds_dwordx4) fill a ring of two 32-dim slots; otherwise
 // chunks of 64 (or, for d_h > 256, 32) dims travel through registers into
 // two LDS buffers.  With no barrier inside the contraction, the waves of a
 // SIMD drift apart and one's LDS traffic overlaps another's matrix work.
@@ -777,13 +777,14 @@ hipError_t launch_ka(const ChunkArgs& args, hipStream_t s, const LaunchTiming* t
   a.ka_div_nblk = make_fastdiv(std::max(1, a.nblk));
   {
     // full shapes (every 32-dim chunk of a share inside d_h, whole ring
-    // turns of four slots, else of two) stage keys straight into LDS when the
-    // rings fit
+    // turns of two slots) stage keys straight into LDS when the rings fit.
+    // Two slots rather than four: at d_h <= 128 two workgroups then fit a
+    // compute unit, so that one's selection and prologue overlap the other's
+    // contraction when the grid runs in several rounds, and with one
+    // workgroup per unit the deeper ring gains nothing measurable.
     const int ndq = kScoreWaves / (a.key_block / 16);
     const int share = ((a.half + 16 * ndq - 1) / (16 * ndq)) * 16;
     const bool full32 = share % 32 == 0 && ndq * share <= a.half;
-    if (full32 && (share / 32) % 4 == 0 && ka_smem_bytes<32, 4, true>(a.half, a.key_block) <= kLdsBytes)
-      return launch_ka_full<32, 4, true, true>(a, s, tm);
     if (full32 && (share / 32) % 2 == 0 && ka_smem_bytes<32, 2, true>(a.half, a.key_block) <= kLdsBytes)
       return launch_ka_full<32, 2, true, true>(a, s, tm);
   }
