@@ -30,9 +30,14 @@
 // loads the list's row keys and weights (coefficients), keeps the rows of
 // its hash group in pair order, and sorts them stably by row with an LSD
 // radix sort in LDS (8-bit digits, ballot ranking), so a row's pairs stay in
-// ascending token order.  The sort is repeated by the column slices of one
-// group, which is cheaper than a separate grouping launch and its dependent
-// global rounds.  Larger chunks (kd_update) read the grouping kernel's
+// ascending token order.  Rows of up to 16 bits are first renamed to their
+// rank among the group's distinct rows (a bitmap of the rows present), so
+// at most 256 of them sort in one pass; when that pass's digit is the row,
+// the segments are the digits present and the pass's scan writes their
+// tables.  The sort is repeated by the column slices of one group, which is
+// cheaper than a separate grouping launch and its dependent global rounds;
+// value and sub-key lists take separate numbers of hash groups, chosen to
+// even out the workgroups' work.  Larger chunks (kd_update) read the grouping kernel's
 // output instead: per (list, unit), the kept entries sorted by row, each
 // with its token and weight, regions one after another, so a group of
 // consecutive regions is one contiguous run of entries, taken in batches
@@ -45,8 +50,8 @@
 // holds the token and weight of one pair, pair group g sums pairs g,
 // g + groups, ... as DPP broadcasts hand them over (only as many steps as the
 // item needs), and a fixed butterfly adds the groups.  Every sum runs in
-// one fixed order, results do not depend on scheduling, and no atomics are
-// used.
+// one fixed order, results do not depend on scheduling, and no atomic
+// operation touches a sum (the only atomics set bits of the row bitmap).
 
 #include <algorithm>
 
