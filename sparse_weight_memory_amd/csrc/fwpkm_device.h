@@ -274,6 +274,15 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
+// Workgroup barrier that orders LDS traffic only: each wave waits for its own
+// LDS operations, then for the other waves.  __syncthreads() first waits for
+// every global load the wave has in flight as well, so a phase that works
+// in LDS while a later phase's global loads travel uses this one.  It makes
+// no global memory written before it visible to other waves.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // All ones if ok, else zero, through an empty asm: AND-ing a loaded value
 // with it masks the value without letting the compiler turn the mask into a
 // select, and the select into a branch around the load (every such branch

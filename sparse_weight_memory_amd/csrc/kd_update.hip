@@ -101,11 +101,12 @@ __host__ __device__ constexpr KdLds kd_lds_layout(int T, int SW) {
 // Exclusive scan of one int per thread over the block; *total = the sum.
 // `red` (kKdWaves ints) must not be written again before the caller's next
 // barrier.
+template <bool kLdsOnly = false>
 __device__ __forceinline__ int kd_block_scan(int x, int* red, int* total) {
   const int wave = threadIdx.x / kWave;
   const int incl = wave_inclusive_scan(x);
   if (lane_id() == kWave - 1) red[wave] = incl;
-  __syncthreads();
+  if constexpr (kLdsOnly) lds_barrier(); else __syncthreads();
   int base = 0, sum = 0;
 #pragma unroll
   for (int w = 0; w < kKdWaves; ++w) {
@@ -594,57 +595,74 @@ __global__ __launch_bounds__(kKdThreads) void kd_update(ChunkArgs a) {
   S.red = reinterpret_cast<int*>(lds + LL.red);               // [4][kKdWaves]
   int* red = S.red;
 
+  // every launch argument the prologue needs, fetched in one batch with one
+  // wait (see kd_write)
+  asm volatile("" :: "s"(a.T), "s"(a.U), "s"(a.kd_pu), "s"(a.kd_div_pu.m), "s"(a.kd_div_pu.l), "s"(a.kd_sv),
+               "s"(a.kd_gv), "s"(a.kd_div_gv.m), "s"(a.kd_div_gv.l), "s"(a.kd_sk), "s"(a.kd_gk),
+               "s"(a.kd_div_kl.m), "s"(a.kd_div_kl.l), "s"(a.kd_div_gk.m), "s"(a.kd_div_gk.l), "s"(a.dv),
+               "s"(a.half), "s"(a.div_H.m), "s"(a.div_H.l), "s"(a.H), "s"(a.P), "s"(a.regions), "s"(a.kinds),
+               "s"(a.ent_row), "s"(a.ent_tw));
   const KdWho who = kd_who(a, L4);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int64_t lbase = ((int64_t)who.list * a.U + who.u) * a.P;
 
-  // ---- this group's run of entries: regions [r0, r0 + RG) (wave 0)
+  // ---- this group's run of entries: regions [r0, r0 + RG).  Every wave
+  // reads the (at most 64) region records itself, so the entry loads need
+  // no barrier.
   const int RG = a.regions / who.ngrp;                    // groups are runs of regions
   const int r0 = who.grp * RG;
-  if (wave == 0) {
-    int4 kd = make_int4(0, 0, 0, 0);
-    if (lane < RG) kd = a.kinds[((int64_t)who.list * a.U + who.u) * a.regions + r0 + lane];
-    const int ent = wave_sum(lane < RG ? kd.w : 0);
-    if (lane == 0) {
-      red[3 * kKdWaves] = kd.z;          // lane 0: the first region's offset
-      red[3 * kKdWaves + 1] = ent;
-    }
-  }
-  {
-    float4 v[kKdStageMax];
-    kd_stage_load<L4>(a, who, v);
-    kd_stage_store<L4>(a.T, v, dat);
-  }
-  __syncthreads();
-  const int e_first = red[3 * kKdWaves], e_count = red[3 * kKdWaves + 1];
+  int4 kd = make_int4(0, 0, 0, 0);
+  if (lane < RG) kd = a.kinds[((int64_t)who.list * a.U + who.u) * a.regions + r0 + lane];
+  const int e_count = wave_sum(lane < RG ? kd.w : 0);
+  const int e_first = readlane_i(kd.z, 0);               // the first region's offset
   if (tid == 0) device_check(a, e_first >= 0 && e_count >= 0 && e_first + e_count <= a.P, kChkCapacity);
+  if (e_count == 0) return;                               // block-uniform: nothing to write
   const int* erow = a.ent_row + lbase + e_first;
   const int2* etw = a.ent_tw + lbase + e_first;
+
+  // ---- a batch's entries and the row after it (if any) into LDS
+  int rv[kKdPer];
+  int2 tw[kKdPer];
+  int after = 0;
+  auto load_batch = [&](int done, int n, bool last) {
+#pragma unroll
+    for (int j = 0; j < kKdPer; ++j) {
+      const int e = min(tid + j * kKdThreads, n - 1);
+      rv[j] = erow[done + e];
+      tw[j] = etw[done + e];
+    }
+    after = erow[done + (last ? n - 1 : n)];
+  };
+  auto store_batch = [&](int n, bool last) {
+#pragma unroll
+    for (int j = 0; j < kKdPer; ++j) {
+      const int e = tid + j * kKdThreads;
+      if (e < n) {
+        ent_row[e] = rv[j];
+        ent_t[e] = tw[j].x;
+        ent_w[e] = tw[j].y;
+      }
+    }
+    if (tid == 0) ent_row[n] = last ? -1 : after;
+  };
+  {
+    // the first batch's entries go out first and the data slice right
+    // behind them: loads complete in order, so the entries are stored while
+    // the slice is still on its way
+    const int n = min(kKdEntCap, e_count);
+    load_batch(0, n, n == e_count);
+    float4 v[kKdStageMax];
+    kd_stage_load<L4>(a, who, v);
+    store_batch(n, n == e_count);
+    kd_stage_store<L4>(a.T, v, dat);
+  }
 
   for (int done = 0; done < e_count;) {             // block-uniform
     const int n = min(kKdEntCap, e_count - done);
     const bool last = done + n == e_count;
-    // ---- the batch's entries, and the row after it (if any)
-    {
-      int rv[kKdPer];
-      int2 tw[kKdPer];
-#pragma unroll
-      for (int j = 0; j < kKdPer; ++j) {
-        const int e = min(tid + j * kKdThreads, n - 1);
-        rv[j] = erow[done + e];
-        tw[j] = etw[done + e];
-      }
-      const int after = erow[done + (last ? n - 1 : n)];   // the row after the batch
-#pragma unroll
-      for (int j = 0; j < kKdPer; ++j) {
-        const int e = tid + j * kKdThreads;
-        if (e < n) {
-          ent_row[e] = rv[j];
-          ent_t[e] = tw[j].x;
-          ent_w[e] = tw[j].y;
-        }
-      }
-      if (tid == 0) ent_row[n] = last ? -1 : after;
+    if (done > 0) {
+      load_batch(done, n, last);
+      store_batch(n, last);
     }
     __syncthreads();
     // ---- unless this is the last batch, it ends at its last segment head
@@ -726,6 +744,16 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   int* cnt = reinterpret_cast<int*>(lds + LL.cnt);
   int* red = reinterpret_cast<int*>(lds + LL.red);
 
+  // every launch argument the prologue needs, as scalar operands of an empty
+  // statement: they are fetched in one batch with one wait.  Left to itself
+  // the compiler fetches them in dependent rounds, and with 16 waves taking
+  // turns on the compute unit's scalar unit the last wave then issued its
+  // first loads ~0.5 us after the first.
+  asm volatile("" :: "s"(a.T), "s"(a.U), "s"(a.kd_pu), "s"(a.kd_div_pu.m), "s"(a.kd_div_pu.l), "s"(a.kd_sv),
+               "s"(a.kd_gv), "s"(a.kd_div_gv.m), "s"(a.kd_div_gv.l), "s"(a.kd_sk), "s"(a.kd_gk),
+               "s"(a.kd_div_kl.m), "s"(a.kd_div_kl.l), "s"(a.kd_div_gk.m), "s"(a.kd_div_gk.l), "s"(a.dv),
+               "s"(a.half), "s"(a.div_H.m), "s"(a.div_H.l), "s"(a.H), "s"(a.P), "s"(a.keys), "s"(a.sel_w),
+               "s"(a.coef), "s"(a.n));
   const KdWho who = kd_who(a, L4);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int P = a.P;
@@ -735,11 +763,9 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
                                     : a.coef + (int64_t)(who.list - 1) * a.U * P + (int64_t)who.u * P;
   const int invalid = who.list == 0 ? a.n * a.n : a.n;
 
-  // ---- one round of loads: the list's rows and weights first, then the
-  // data slice, which is stored to LDS only after the sort (loads complete
-  // in order, so the grouping waits for the rows alone).  Wave w owns list
-  // tiles [w*tpw, (w+1)*tpw), so kept entries come out in pair order;
-  // indices past the list re-read entry 0 and are masked.
+  // ---- the list's rows and weights.  Wave w owns list tiles
+  // [w*tpw, (w+1)*tpw), so kept entries come out in pair order; indices past
+  // the list re-read entry 0 and are masked.
   const int tiles = (P + kWave - 1) / kWave;
   const int tpw = (tiles + kKdWaves - 1) / kKdWaves;          // <= kTiles
   int kr[kTiles];
@@ -751,8 +777,6 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
     kr[j] = keys[ic];
     wr[j] = wsrc[ic];
   }
-  float4 v[kKdStageMax];
-  kd_stage_load<L4>(a, who, v);
   for (int i = lane; i < 256; i += kWave) cnt[wave * 256 + i] = 0;   // this wave's digit counters
   // radix passes the rows need (8-bit digits)
   const int rmax = invalid - 1;
@@ -783,7 +807,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
     kept += __popcll(__ballot(mine));
   }
   if (lane == 0) red[wave] = kept;
-  __syncthreads();
+  lds_barrier();
   int base = 0, M = 0;
 #pragma unroll
   for (int w = 0; w < kKdWaves; ++w) {
@@ -791,6 +815,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
     base += w < wave ? t : 0;
     M += t;
   }
+  if (M == 0) return;                                 // block-uniform: nothing to write
 #pragma unroll
   for (int j = 0; j < kTiles; ++j) {
     const int i = (wave * tpw + j) * kWave + lane;
@@ -805,8 +830,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
     }
     base += __popcll(m);
   }
-  if (M == 0) return;                                 // block-uniform: nothing to write
-  __syncthreads();
+  lds_barrier();
 
   // ---- stable LSD radix sort of the M kept (row, pair) by row: 8-bit
   // digits, as many passes as the largest row needs.  Wave w owns entry
@@ -833,18 +857,25 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   if (try_rename) {
     const unsigned int w0 = bm[2 * tid], w1 = bm[2 * tid + 1];
     int D;
-    const int pre = kd_block_scan(__popc(w0) + __popc(w1), red, &D);
+    const int pre = kd_block_scan<true>(__popc(w0) + __popc(w1), red, &D);
     wpre[2 * tid] = pre;
     wpre[2 * tid + 1] = pre + __popc(w0);
     if (D <= 256) {                                            // block-uniform
       passes = 1;
       renamed = true;
     }
-    __syncthreads();
+    lds_barrier();
   }
   // one pass whose digit is the row: the segments are the digits present,
   // and the last pass's scan builds their tables
   const bool direct = passes == 1;
+  // the data slice, stored to LDS only after the sort: its loads travel
+  // while the radix passes run (the grouping's barriers order LDS alone).
+  // Issued beside the rows, they queued ahead of the later waves' row loads
+  // in the compute unit's load path and held the compaction back ~1 us;
+  // issued before the compaction, the waves stalled issuing them.
+  float4 v[kKdStageMax];
+  kd_stage_load<L4>(a, who, v);
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * 8;
     // each tile's lanes with equal digits (ballots), counted once by the
@@ -868,7 +899,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
       tp[j] = digit_peers(td[j], valid);
       if (valid && (tp[j] & lanes_below()) == 0ull) mycnt[td[j]] += __popcll(tp[j]);
     }
-    __syncthreads();
+    lds_barrier();
     // scatter bases in digit-major, wave-minor order, digit-parallel: thread
     // d < 256 (waves 0-3) runs over the waves' counters of digit d, then the
     // digits' totals are scanned across those four waves.  When the digit is
@@ -901,7 +932,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < 256) {
       int bz = 0, bp = 0;
       for (int w = 0; w < wave; ++w) {
@@ -929,7 +960,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < kTiles; ++j) {
       if (t_lo + j >= t_hi) break;                     // wave-uniform
@@ -945,7 +976,7 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
       if (valid && lower == 0ull) mycnt[td[j]] = b0 + __popcll(tp[j]);
     }
     for (int i = lane; i < 256; i += kWave) mycnt[i] = 0;   // for the next pass
-    __syncthreads();
+    lds_barrier();
     int* t;
     t = ks; ks = kd; kd = t;
     t = is; is = id; id = t;
