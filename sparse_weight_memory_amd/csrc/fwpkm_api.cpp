@@ -443,7 +443,7 @@ static int read_device_checks(const unsigned int* word, hipStream_t stream) {
   static const char* const names[fwpkm::kNumDeviceChecks] = {
       "per-half sub-key index >= n", "fewer than k candidates", "selected slot outside [0, N)",
       "a slot selected twice", "selection weight not finite or outside [0, 1]",
-      "grouped entry row or token out of range", "update batch over its LDS capacity",
+      "grouped entry row or token out of range, or not its pair's row", "update batch over its LDS capacity",
       "grouped entries out of row order"};
   unsigned int bits = 0;
   hipError_t e = hipStreamSynchronize(stream);

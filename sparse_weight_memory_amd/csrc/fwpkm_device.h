@@ -32,7 +32,7 @@ enum DeviceCheck : unsigned int {
   kChkSlot = 1u << 2,         // a selected slot is outside [0, N)
   kChkDistinct = 1u << 3,     // a token selected one slot twice
   kChkWeight = 1u << 4,       // a selection weight is not finite or outside [0, 1]
-  kChkEntry = 1u << 5,        // a grouped entry's row or token is out of range
+  kChkEntry = 1u << 5,        // a grouped entry's row or token is out of range, or not its pair's row
   kChkCapacity = 1u << 6,     // an update batch overflows its LDS lists
   kChkOrder = 1u << 7,        // grouped entries are not sorted by row
 };

@@ -11,9 +11,13 @@
 // position in list order) into one 32-bit word and places every entry at the
 // count of words below its own (one pass, every entry against every other);
 // other regions use an LSD radix sort (8-bit digits; as many passes as the
-// largest row needs).  Stability keeps every row's
-// pairs in ascending (token, rank) order, so each row's gradient is summed in
-// one fixed order and no float atomics are used.
+// largest row needs).  A region of at least 512 entries whose rows need two
+// or more passes first tries to rename its rows to their rank among its
+// distinct rows (a hash set in LDS, then every distinct row against every
+// other): with at most 256 of them -- hot rows, as in a long stream of
+// clustered tokens -- one pass over the ranks gives the same order.
+// Stability keeps every row's pairs in ascending (token, rank) order, so each
+// row's gradient is summed in one fixed order and no float atomics are used.
 // [gist.science "Fast-weight Product Key Memory", section 2, Key Technical
 // Choices: gradients of slots accessed several times in a chunk are
 // aggregated (averaged)]
@@ -62,6 +66,18 @@ static_assert(kRankMax <= kGroupThreads, "one ranked entry per thread");
 static_assert(kRankMax + kRankBatch - 1 <= kRankPartOffset, "packed words before the partial counts");
 static_assert(kRankPartOffset + (kGroupWaves - 1) * kWave <= kGroupWaves * kDigits,
               "partial counts fit the counters' space");
+// Renaming: a region of at least kRenameMin entries whose rows need two or
+// more radix passes first maps its rows to their rank among its distinct
+// rows, through a hash set of kRenameSlots rows in the counters' space;
+// with at most kRenameMax distinct rows one pass then sorts the ranks.
+constexpr int kRenameBits = 10;
+constexpr int kRenameSlots = 1 << kRenameBits;
+constexpr int kRenameMax = 256;          // = kDigits: one pass
+constexpr int kRenameMin = 2 * kRenameMax;
+constexpr int kRenameProbes = 32;        // longest probe run tried before giving up
+constexpr int kRenameInts = kRenameMax + 8;   // row of each rank, then two control words
+static_assert(2 * kRenameSlots <= kGroupWaves * kDigits, "hash set and slot ranks fit the counters' space");
+static_assert(kRenameMax == kDigits, "renamed rows take one pass");
 
 // r + (w < me): the compare's carry feeds the add (two instructions).
 __device__ __forceinline__ unsigned int add_if_below(unsigned int r, unsigned int w, unsigned int me) {
@@ -125,6 +141,7 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   int* idx1 = key1 + P;                   // [P] (pong)
   int* cnt = idx1 + P;                    // [kGroupWaves][kDigits]
   int* red = cnt + kGroupWaves * kDigits; // [3][kGroupWaves]
+  int* rowof = red + 3 * kGroupWaves;     // [kRenameMax] row of each rank, [+0, +1] control words
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -204,8 +221,29 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
     base += __popcll(m);
   }
   int* mycnt = cnt + wave * kDigits;   // only this wave counts into / scatters from it
+  // radix passes the rows need, and whether to rename them first (below)
+  int bits = 0;
+  while (bits < 31 && (kmax >> bits) != 0) ++bits;
+  int passes = (bits + kBits - 1) / kBits;
+  const bool try_rename = !by_rank && passes >= 2 && M >= kRenameMin;   // block-uniform
+  // renaming: a hash set of rows in the counters' space, the row of each
+  // rank, two control words, and the distinct rows (padded to whole int4
+  // reads, 16-byte aligned) and their slots in the pong buffer
+  // (P >= M >= kRenameMin ints)
+  int* tab = cnt;                                            // [kRenameSlots] row, -1 = empty
+  int* rank_of = cnt + kRenameSlots;                         // [kRenameSlots] rank of the slot's row
+  int* ctl = rowof + kRenameMax;                             // distinct rows found, overflow
+  int* drow = key1 + ((4 - (int)((reinterpret_cast<uintptr_t>(key1) >> 2) & 3)) & 3);   // [kRenameMax + 4]
+  int* dslot = drow + kRenameMax + 4;                        // [kRenameMax]
   if (by_rank) {
     if (tid < kRankBatch - 1) packed[M + tid] = 0xFFFFFFFFu;   // pad to whole batches; never below a real word
+  } else if (try_rename) {
+    for (int q = tid; q < kRenameSlots; q += kGroupThreads) tab[q] = -1;
+    for (int q = tid; q < kRenameMax + 4; q += kGroupThreads) drow[q] = 0x7FFFFFFF;
+    if (tid == 0) {
+      ctl[0] = 0;
+      ctl[1] = 0;
+    }
   } else {
     for (int i = lane; i < kDigits; i += kWave) mycnt[i] = 0;
   }
@@ -217,6 +255,7 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   const int t_lo = wave * vtpw;
   const int t_hi = min(vtiles, t_lo + vtpw);
   int *ks = key0, *is = idx0, *kd = key1, *id = idx1;
+  bool renamed = false;
   if (by_rank) {
     // ---- rank sort: the words are distinct and ordered as (row, position),
     // so an entry's place in the stable order is the number of words below
@@ -262,9 +301,75 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
     __syncthreads();
     ks = key1; is = idx1; kd = key0; id = idx0;
   } else {
-  int bits = 0;
-  while (bits < 31 && (kmax >> bits) != 0) ++bits;
-  const int passes = (bits + kBits - 1) / kBits;
+  // ---- rename the rows to their rank among the region's distinct rows
+  // (hot rows: few distinct rows, many entries).  Each entry's row goes
+  // into a hash set (linear probing, compare-and-swap; the set of distinct
+  // rows found does not depend on the order of insertion); the distinct
+  // rows are ranked by value, each against all, so ranks keep the rows'
+  // order and one stable pass over the ranks gives exactly the order the
+  // passes over the rows would.  More than kRenameMax distinct rows, or a
+  // probe run longer than kRenameProbes, leaves the rows as they are (once
+  // the count has passed the limit every lane stops at its next probe and
+  // every wave at its next tile, so regions of many distinct rows give up
+  // early).
+  if (try_rename) {
+    int* eslot = id;                                         // [M] slot of each entry
+    for (int tile = t_lo; tile < t_hi; ++tile) {
+      // too many distinct rows already: renaming is off, this wave stops
+      if (__builtin_amdgcn_readfirstlane(*(volatile int*)&ctl[0]) > kRenameMax) break;
+      const int i = tile * kWave + lane;
+      if (i < M) {
+        const int r = ks[i];
+        int h = (int)(((unsigned)r * 0x85EBCA6Bu) >> (32 - kRenameBits));
+        int slot = -1;
+        for (int probe = 0; probe < kRenameProbes; ++probe) {
+          if (*(volatile int*)&ctl[0] > kRenameMax) break;   // renaming is off: stop at once
+          const int old = atomicCAS(&tab[h], -1, r);
+          if (old == -1) {
+            const int d = atomicAdd(&ctl[0], 1);
+            if (d < kRenameMax) {
+              drow[d] = r;
+              dslot[d] = h;
+            }
+            slot = h;
+            break;
+          }
+          if (old == r) {
+            slot = h;
+            break;
+          }
+          h = (h + 1) & (kRenameSlots - 1);
+        }
+        if (slot < 0) ctl[1] = 1;
+        eslot[i] = slot;
+      }
+    }
+    __syncthreads();
+    const int D = ctl[0];
+    if (D <= kRenameMax && ctl[1] == 0) {                    // block-uniform
+      if (tid < D) {
+        const int me = drow[tid];
+        const int4* d4 = reinterpret_cast<const int4*>(drow);
+        int rk = 0;
+        for (int j = 0; j < (D + 3) / 4; ++j) {              // pads sort last
+          const int4 w = d4[j];
+          rk += (w.x < me) + (w.y < me) + (w.z < me) + (w.w < me);
+        }
+        rank_of[dslot[tid]] = rk;
+        rowof[rk] = me;
+      }
+      __syncthreads();
+      for (int tile = t_lo; tile < t_hi; ++tile) {
+        const int i = tile * kWave + lane;
+        if (i < M) ks[i] = rank_of[eslot[i]];
+      }
+      passes = 1;
+      renamed = true;
+      __syncthreads();         // every wave has read the slot ranks before the counters are cleared
+    }
+    for (int i = lane; i < kDigits; i += kWave) mycnt[i] = 0;   // the set used the counters
+    __syncthreads();
+  }
 
   // ---- LSD radix passes over the M kept entries
   for (int pass = 0; pass < passes; ++pass) {
@@ -342,7 +447,9 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   for (int j = 0; j < kOutTiles; ++j) {
     const int i = (t_lo + j) * kWave + lane;
     if (t_lo + j < t_hi && i < M) {
-      erow[i] = ks[i];
+      const int row = renamed ? rowof[ks[i]] : ks[i];
+      erow[i] = row;
+      device_check(a, row == keys[pv[j]], kChkEntry);        // the pair's own row
       etw[i] = make_int2(token_of(pv[j], a.k), __float_as_int(wv[j]));
     }
   }
@@ -355,7 +462,7 @@ int group_regions(int units) {
 }
 
 size_t kc_smem_bytes(int P) {
-  return sizeof(int) * ((size_t)4 * P + (size_t)kGroupWaves * kDigits + 3 * kGroupWaves);
+  return sizeof(int) * ((size_t)4 * P + (size_t)kGroupWaves * kDigits + 3 * kGroupWaves + kRenameInts);
 }
 
 hipError_t launch_kc(const ChunkArgs& a, hipStream_t s, const LaunchTiming* tm) {

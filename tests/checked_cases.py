@@ -9,8 +9,9 @@ same cases run on the product library in its own process.
 The cases cover the paths whose indexing the device checks watch: two key
 blocks with a ragged second one and a ragged token tile, both score modes,
 a chunk of more than 2048 pairs per unit (separate grouping kernel and
-batched update), sub-keys that all tie (whole-wave selection fallback), and
-the addressing loss.  The last case feeds NaN queries in dot mode, whose
+batched update), sub-keys that all tie (whole-wave selection fallback), the
+addressing loss, and one query asked by 1,024 tokens (hot rows renamed in
+the grouping kernel).  The last case feeds NaN queries in dot mode, whose
 softmax weights are then NaN: a checked build must report it.
 """
 
@@ -28,6 +29,7 @@ CASES = {
     "mass_ties": (2, 1, 48, 64, 32, 64, 8, "idw", 0.0, 1, "tied_keys"),
     "addressing": (2, 2, 64, 48, 32, 96, 4, "idw", 0.1, 2, None),
     "nan_dot": (1, 1, 32, 32, 32, 64, 4, "dot", 0.0, 1, "nan_queries"),
+    "hot_rows": (1, 1, 1024, 512, 8, 16, 8, "idw", 0.0, 1, "one_query"),
 }
 
 
@@ -53,6 +55,8 @@ def run(name):
         q = rng.standard_normal((B, C, H, 2 * half)).astype(np.float32)
         if special == "nan_queries":
             q[:] = np.nan
+        if special == "one_query":
+            q[:] = q[:, :1]
         y = rng.standard_normal((B, C, H, dv)).astype(np.float32)
         print(f"[checked-cases] {name} call {c}", flush=True)
         try:

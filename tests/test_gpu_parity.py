@@ -189,6 +189,23 @@ def test_update_geometry_at_wide_chunks(C, mode):
     compare_chunk(mem, st, q, y, 1.0, units=[0, 3, 7], label=f"wide C{C} {mode}")
 
 
+@pytest.mark.parametrize("fresh", [0, 8])
+def test_grouping_renames_hot_rows(fresh):
+    """One sequence of 1,024 tokens, n = 512, k = 8: 8,192 pairs per unit take
+    the separate grouping kernel, and with every token asking the same query
+    (or all but every fresh-th token) each selected value slot (18 bits) and
+    sub-key row (9 bits) is hit by hundreds of tokens.  Their regions hold
+    hundreds of entries over a few distinct rows, which are renamed to their
+    ranks and sorted in one radix pass; the fresh tokens' rows mix cold rows
+    into the same regions."""
+    need_gpu()
+    B, H, C, n, half, dv, k = 1, 1, 1024, 512, 8, 16, 8
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=C, num_heads=H, max_batch=B)
+    st, q, y = _random_case(1100 + fresh, B, H, C, n, half, dv)
+    q[:] = q[:, [t if fresh and t % fresh == 0 else 0 for t in range(C)]]
+    compare_chunk(mem, st, q, y, 1.0, label=f"hot rows, fresh every {fresh}")
+
+
 @pytest.mark.parametrize("C,k", [(300, 4), (700, 2)])
 def test_fused_update_at_narrow_slices(C, k):
     """At most 2,048 pairs per unit keep the grouping inside the update
