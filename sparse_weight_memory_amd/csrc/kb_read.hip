@@ -137,35 +137,43 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   for (int h = 0; h < 2; ++h) {
     const int64_t base = (ut * 2 + h) * a.nblk * k;
     if (a.nblk != 1) {
-      // merge the per-block lists: the best k so far stay in lanes 0..k-1,
-      // the next 64-k candidates fill lanes k..63, and a bitonic sort brings
-      // the best k of both back to lanes 0..k-1
-      const int nc = a.nblk * k;
-      const int fresh = kWave - k;
-      // candidate pos + lane - k of a round; indices outside [0, nc) re-read
-      // an entry in range and are masked.  The next round's pair of loads is
-      // issued before this round's sort.
-      auto fetch = [&](int pos, int& ix, float& ov) {
-        const int c = min(max(pos + lane - k, 0), nc - 1);
-        ix = a.half_i[base + c];
-        ov = a.half_o[base + c];
+      // merge the per-block lists, each sorted best-first: the best k so far
+      // sit in lanes 0..k-1 (lanes k..KMAX-1 empty) and the next block's list
+      // goes into lanes KMAX..2 KMAX-1 in reverse order, so that lanes
+      // 0..2 KMAX-1 hold one bitonic sequence; a bitonic merge over 2 KMAX
+      // lanes sorts it and the best k are back in lanes 0..k-1 (log2(2 KMAX)
+      // exchange steps a block, where sorting a wave of candidates took 21).
+      // The next block's loads are issued before this block's merge.
+      static_assert(2 * KMAX <= kWave, "two lists fit the wave");
+      const int nb = a.nblk;
+      auto entry_of = [&](int blk) { return blk == 0 ? lane : 2 * KMAX - 1 - lane; };
+      auto fetch = [&](int blk, int& ix, float& ov) {
+        const int c = min(max(entry_of(blk), 0), k - 1);   // lanes without an entry re-read one, masked
+        ix = a.half_i[base + (int64_t)blk * k + c];
+        ov = a.half_o[base + (int64_t)blk * k + c];
       };
       int ixn;
       float ovn;
       fetch(0, ixn, ovn);
       skey x = kEmptyKey;
-      for (int pos = 0; pos < nc; pos += fresh) {
+      for (int blk = 0; blk < nb; ++blk) {                  // block-uniform
         const int ix = ixn;
         const float ov = ovn;
-        fetch(pos + fresh < nc ? pos + fresh : pos, ixn, ovn);
-        const int c = pos + lane - k;
-        const unsigned int m32 = opaque_mask(lane >= k && c < nc && ix != kNoIndex);
+        fetch(min(blk + 1, nb - 1), ixn, ovn);
+        const int e = entry_of(blk);
+        const bool slot_ok = blk == 0 ? lane < k : (lane >= KMAX && lane < 2 * KMAX && e < k);
+        const unsigned int m32 = opaque_mask(slot_ok && ix != kNoIndex);
         const skey m = (skey)m32 << 32 | m32;
         const skey cand = (pack_key(order_key(ov), ix) & m) | (kEmptyKey & ~m);
-        x = lane >= k ? cand : x;
-        sort_keys<64>(x);
+        if (blk == 0) {
+          x = cand;
+        } else {
+          x = lane < KMAX ? x : cand;
+          key_merge_steps<2 * KMAX, 2 * KMAX, KMAX>(x);
+          x = lane < k ? x : kEmptyKey;
+        }
       }
-      hk[h] = lane < k ? x : kEmptyKey;
+      hk[h] = x;
     }
   }
 
