@@ -109,11 +109,14 @@ __device__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
   return base + incl - x;
 }
 
-// Lanes of this wave holding the same digit (among `valid` lanes).
-__device__ __forceinline__ unsigned long long digit_peers(int d, bool valid) {
+// Lanes of this wave holding the same digit (among `valid` lanes).  Digit
+// bits from `nbits` up are zero in every lane (the keys' range), so their
+// ballots would change nothing and are skipped (nbits is wave-uniform).
+__device__ __forceinline__ unsigned long long digit_peers(int d, bool valid, int nbits) {
   unsigned long long peers = __ballot(valid);
 #pragma unroll
   for (int bit = 0; bit < kBits; ++bit) {
+    if (bit >= nbits) break;
     const unsigned long long on = __ballot((d >> bit) & 1);
     peers &= ((d >> bit) & 1) ? on : ~on;
   }
@@ -363,7 +366,10 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
         const int i = tile * kWave + lane;
         if (i < M) ks[i] = rank_of[eslot[i]];
       }
-      passes = 1;
+      // ranks take bitlen(D - 1) bits; one distinct row is sorted already
+      bits = 0;
+      while (bits < kBits && ((D - 1) >> bits) != 0) ++bits;
+      passes = D > 1 ? 1 : 0;
       renamed = true;
       __syncthreads();         // every wave has read the slot ranks before the counters are cleared
     }
@@ -374,11 +380,12 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   // ---- LSD radix passes over the M kept entries
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass * kBits;
+    const int nbits = min(kBits, bits - shift);   // digit bits any key of this pass can have
     for (int tile = t_lo; tile < t_hi; ++tile) {
       const int i = tile * kWave + lane;
       const bool valid = i < M;
       const int d = valid ? (((unsigned)ks[i] >> shift) & (kDigits - 1)) : 0;
-      const unsigned long long peers = digit_peers(d, valid);
+      const unsigned long long peers = digit_peers(d, valid, nbits);
       if (valid && (peers & lanes_below()) == 0ull) mycnt[d] += __popcll(peers);
     }
     __syncthreads();
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
       const bool valid = i < M;
       const int key = valid ? ks[i] : 0;
       const int d = ((unsigned)key >> shift) & (kDigits - 1);
-      const unsigned long long peers = digit_peers(d, valid);
+      const unsigned long long peers = digit_peers(d, valid, nbits);
       const unsigned long long lower = peers & lanes_below();
       const int b0 = valid ? mycnt[d] : 0;
       if (valid) {
