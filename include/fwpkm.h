@@ -318,8 +318,11 @@ const char* fwpkm_kernel_name(int32_t i);
  * kernels with device-side tests of the invariants the indexing rests on:
  * every per-half candidate index below n, k Cartesian candidates per token,
  * every selected slot in [0, N) and distinct, every selection weight finite
- * and in [0, 1], every grouped entry's row and token in range and in row
- * order, and every update batch within its LDS lists.  A failed test sets a
+ * and in [0, 1], every grouped entry's row and token in range, equal to its
+ * pair's row and in row order, and every update batch within its LDS lists.
+ * Every chunk call first fills its whole workspace with 0xFF bytes (NaN as a
+ * float, -1 as an index), so that a kernel reading workspace the call never
+ * wrote gets values the tests or the results expose.  A failed test sets a
  * bit in a word of the workspace; each chunk call then waits for its stream
  * and returns FWPKM_ERR_DEVICE_CHECK naming the tests that failed.  The wait
  * makes a checked build unsuitable for stream capture and for timing; the

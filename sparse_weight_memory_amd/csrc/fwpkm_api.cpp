@@ -644,6 +644,12 @@ static int forward_impl(fwpkm_handle* h, const float* queries, const float* targ
   a.addr_ell = reinterpret_cast<float*>(ws + L.addr_ell);
   a.check = reinterpret_cast<unsigned int*>(ws + L.check);
 #if FWPKM_DEVICE_CHECKS
+  // checked builds: every byte of the call's workspace starts as 0xFF (NaN as
+  // a float, -1 as an index, so a kernel that reads workspace its call never
+  // wrote gets values the device checks or the results expose), then the
+  // check word is cleared
+  if ((e = hipMemsetAsync(ws, 0xFF, L.total, stream)) != hipSuccess)
+    return fail(FWPKM_ERR_HIP, "poisoning the workspace: %s", hipGetErrorString(e));
   if ((e = hipMemsetAsync(a.check, 0, sizeof(unsigned int), stream)) != hipSuccess)
     return fail(FWPKM_ERR_HIP, "clearing the device-check word: %s", hipGetErrorString(e));
 #endif
