@@ -76,6 +76,7 @@ constexpr int kRenameMax = 256;          // = kDigits: one pass
 constexpr int kRenameMin = 2 * kRenameMax;
 constexpr int kRenameProbes = 32;        // longest probe run tried before giving up
 constexpr int kRenameInts = kRenameMax + 8;   // row of each rank, then two control words
+constexpr int kRenamePong = 3 + (kRenameMax + 4) + kRenameMax;   // alignment, distinct rows, their slots
 static_assert(2 * kRenameSlots <= kGroupWaves * kDigits, "hash set and slot ranks fit the counters' space");
 static_assert(kRenameMax == kDigits, "renamed rows take one pass");
 
@@ -228,11 +229,11 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   int bits = 0;
   while (bits < 31 && (kmax >> bits) != 0) ++bits;
   int passes = (bits + kBits - 1) / kBits;
-  const bool try_rename = !by_rank && passes >= 2 && M >= kRenameMin;   // block-uniform
+  const bool try_rename = !by_rank && passes >= 2 && M >= kRenameMin && P >= kRenamePong;   // block-uniform
   // renaming: a hash set of rows in the counters' space, the row of each
   // rank, two control words, and the distinct rows (padded to whole int4
-  // reads, 16-byte aligned) and their slots in the pong buffer
-  // (P >= M >= kRenameMin ints)
+  // reads, 16-byte aligned) and their slots in the pong buffer (P ints,
+  // at least kRenamePong)
   int* tab = cnt;                                            // [kRenameSlots] row, -1 = empty
   int* rank_of = cnt + kRenameSlots;                         // [kRenameSlots] rank of the slot's row
   int* ctl = rowof + kRenameMax;                             // distinct rows found, overflow

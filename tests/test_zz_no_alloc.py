@@ -44,6 +44,14 @@ def _run(mem, st, q, y, lr, noalloc, copy_mode):
     return r.cpu(), [t.cpu() for t in n], slots.cpu(), w.cpu()
 
 
+def _compare(i, got, ref):
+    assert torch.equal(got[2], ref[2]), f"call {i}: selected slots differ"
+    assert torch.equal(got[3], ref[3]), f"call {i}: weights differ"
+    assert torch.equal(got[0], ref[0]), f"call {i}: retrieved differs"
+    for name, a, b in zip(("k1", "k2", "v"), got[1], ref[1]):
+        assert torch.equal(a, b), f"call {i}: next {name} differs"
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("mode", ["idw", "dot"])
 def test_noalloc_equals_the_allocating_entry_point(mode):
@@ -60,11 +68,29 @@ def test_noalloc_equals_the_allocating_entry_point(mode):
         st, q, y = _case(100 * i + (mode == "dot"), B, H, T, n, half, dv)
         ref = _run(mem, st, q, y, lr, noalloc=False, copy_mode=copy_mode)
         got = _run(mem, st, q, y, lr, noalloc=True, copy_mode=copy_mode)
-        assert torch.equal(got[2], ref[2]), f"call {i}: selected slots differ"
-        assert torch.equal(got[3], ref[3]), f"call {i}: weights differ"
-        assert torch.equal(got[0], ref[0]), f"call {i}: retrieved differs"
-        for name, a, b in zip(("k1", "k2", "v"), got[1], ref[1]):
-            assert torch.equal(a, b), f"call {i}: next {name} differs"
+        _compare(i, got, ref)
+    mem.close()
+
+
+@pytest.mark.gpu
+def test_noalloc_with_the_separate_grouping_kernel():
+    """More than 2,048 pairs per unit: the grouping runs as its own kernel on
+    the fixed array too.  The first call's tokens mostly ask one query, so
+    its hot regions are renamed to ranks (one radix pass); the second, with
+    fewer and random tokens, sorts every region by its rows."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from sparse_weight_memory_amd import Config, Memory
+    n, half, dv, k, C, H = 512, 8, 16, 8, 1024, 1
+    mem = Memory(Config(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=C,
+                        num_heads=H, max_batch=1))
+    for i, (T, lr, copy_mode, hot) in enumerate([(1024, 1.0, False, True), (600, 0.5, True, False)]):
+        st, q, y = _case(500 + i, 1, H, T, n, half, dv)
+        if hot:
+            q[:] = q[:, [t if t % 8 == 0 else 0 for t in range(T)]]
+        ref = _run(mem, st, q, y, lr, noalloc=False, copy_mode=copy_mode)
+        got = _run(mem, st, q, y, lr, noalloc=True, copy_mode=copy_mode)
+        _compare(i, got, ref)
     mem.close()
 
 
