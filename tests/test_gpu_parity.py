@@ -98,6 +98,11 @@ EDGE = [
     ("k16-two-blocks", 1, 1, 64, 64, 520, 16, 64, 16, "idw"),
     ("k24-fallback", 1, 1, 32, 32, 64, 8, 32, 24, "idw"),
     ("k32-max", 1, 1, 32, 32, 40, 4, 600, 32, "idw"),
+    # per-block lists merged across the whole wave (2 KMAX = 64 lanes), four
+    # 64-key blocks with a ragged last one; and k below KMAX, whose lanes
+    # k..KMAX-1 must stay empty between merges
+    ("k32-four-blocks", 1, 1, 32, 32, 200, 4, 64, 32, "idw"),
+    ("k20-three-blocks-dot", 1, 1, 48, 48, 150, 8, 16, 20, "dot"),
     ("dot-small", 2, 1, 64, 64, 16, 8, 12, 4, "dot"),
     ("dot-k16", 1, 2, 64, 50, 64, 16, 32, 16, "dot"),
     # keys staged straight into LDS: 128-key blocks (two dim shares), and
