@@ -370,7 +370,7 @@ def main():
         copy_probe(args.copy_probe_mib)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the FwPKM step here runs on one GPU only (asked for --gpus {args.gpus}); "
               "memory units are independent, so N GPUs would each run this step on "
               "their own share of the batch.", file=sys.stderr)
         sys.exit(2)

@@ -4,7 +4,7 @@ tests/abi_host_check.c drives every validation path, the size queries, the
 timing calls and (without a GPU) a well-formed call up to its first HIP
 call.  Here the library's host source is rebuilt with both sanitizers on the
 host side only (the kernels' objects are the ordinary ones, their device
-code untouched), linked with the driver, and run: any heap, stack or
+code untouched), linked with the host test program, and run: any heap, stack or
 undefined-behaviour error in the host runtime fails the test.  CPU only.
 """
 

@@ -138,7 +138,7 @@ def test_two_token_selection_odd_tail_and_mass_ties(k):
     lane's candidates are copies of one row, the best values tie across 64
     keys, and a token's survivors (64 or 128) overflow the 32 lanes: it takes
     the whole-wave path.  Every token is then an exact float64 tie at the
-    k-th place, and the checker accepts only the lower-slot choice among
+    k-th place, and the validity check accepts only the lower-slot choice among
     exactly tied candidates, so the path's selection is checked bit for bit."""
     need_gpu()
     B, H, T, n, half, dv = 8, 1, 249, 256, 16, 16

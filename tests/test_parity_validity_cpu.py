@@ -2,7 +2,7 @@
 
 Where the oracle certifies a near-tie, the GPU path may rank the k-th and
 (k+1)-th candidates either way, and the oracle then adopts the GPU's set.
-These CPU tests feed the checker selections that are wrong in the ways a
+These CPU tests feed the validity check selections that are wrong in the ways a
 broken top-k would be (wrong slots, repeated slots, slots out of range, an
 exact tie broken toward the higher index) and require it to fail, and feed
 it legitimate near-tie swaps and require it to pass.  No GPU is involved:
@@ -32,7 +32,7 @@ def _mass_tie_unit(k, seed, T=249, n=256, half=16, dv=16):
 
 
 def _as_gpu(slots_per_token):
-    """[T, k] selections -> the [B=1, T, H=1, k] layout the checker reads."""
+    """[T, k] selections -> the [B=1, T, H=1, k] layout the validity check reads."""
     return np.asarray(slots_per_token)[None, :, None, :]
 
 
