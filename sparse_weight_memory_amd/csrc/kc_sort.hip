@@ -164,17 +164,21 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
     const int i = (wave * tpw + j) * kWave + lane;
     kreg[j] = (j < tpw && i < P) ? keys[i] : invalid_key;
   }
+  // (tiles past tpw are skipped by a wave-uniform test, not a break: a loop
+  // that can leave early is not unrolled, and kreg[j] at a run-time j is an
+  // indexed register access, ~250 cycles a tile on the shared scalar unit)
   int kept = 0, below = 0, kmax = 0;
 #pragma unroll
   for (int j = 0; j < kScanTiles; ++j) {
-    if (j >= tpw) break;
-    const int key = kreg[j];
-    const bool ok = key != invalid_key;
-    const int rg = region_of(key, a.region_bits);
-    const bool mine = ok && rg == region;
-    below += __popcll(__ballot(ok && rg < region));
-    kept += __popcll(__ballot(mine));
-    kmax = mine && key > kmax ? key : kmax;
+    if (j < tpw) {
+      const int key = kreg[j];
+      const bool ok = key != invalid_key;
+      const int rg = region_of(key, a.region_bits);
+      const bool mine = ok && rg == region;
+      below += __popcll(__ballot(ok && rg < region));
+      kept += __popcll(__ballot(mine));
+      kmax = mine && key > kmax ? key : kmax;
+    }
   }
   kmax = max(kmax, xor_lane<32>(kmax));
   kmax = max(kmax, xor_lane<16>(kmax));
@@ -212,17 +216,18 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   unsigned int* packed = reinterpret_cast<unsigned int*>(cnt);
 #pragma unroll
   for (int j = 0; j < kScanTiles; ++j) {
-    if (j >= tpw) break;
-    const int key = kreg[j];
-    const bool mine = key != invalid_key && region_of(key, a.region_bits) == region;
-    const unsigned long long m = __ballot(mine);
-    if (mine) {
-      const int pos = base + __popcll(m & lanes_below());
-      key0[pos] = key;
-      idx0[pos] = (wave * tpw + j) * kWave + lane;
-      if (by_rank) packed[pos] = ((unsigned int)key << kRankPosBits) | (unsigned int)pos;
+    if (j < tpw) {                                   // wave-uniform (see above)
+      const int key = kreg[j];
+      const bool mine = key != invalid_key && region_of(key, a.region_bits) == region;
+      const unsigned long long m = __ballot(mine);
+      if (mine) {
+        const int pos = base + __popcll(m & lanes_below());
+        key0[pos] = key;
+        idx0[pos] = (wave * tpw + j) * kWave + lane;
+        if (by_rank) packed[pos] = ((unsigned int)key << kRankPosBits) | (unsigned int)pos;
+      }
+      base += __popcll(m);
     }
-    base += __popcll(m);
   }
   int* mycnt = cnt + wave * kDigits;   // only this wave counts into / scatters from it
   // radix passes the rows need, and whether to rename them first (below)
