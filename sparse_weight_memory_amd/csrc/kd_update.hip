@@ -26,15 +26,16 @@
 // instead of a dependent global load.
 //
 // Grouping.  With at most kKdEntCap pairs per unit (kd_write), the
-// workgroup groups its rows itself: in the same round as its data slice it
-// loads the list's row keys and weights (coefficients), keeps the rows of
-// its hash group in pair order, and sorts them stably by row with an LSD
-// radix sort in LDS (8-bit digits, ballot ranking), so a row's pairs stay in
-// ascending token order.  Rows of up to 16 bits are first renamed to their
-// rank among the group's distinct rows (a bitmap of the rows present), so
-// at most 256 of them sort in one pass; when that pass's digit is the row,
-// the segments are the digits present and the pass's scan writes their
-// tables.  The sort is repeated by the column slices of one group, which is
+// workgroup groups its rows itself: it loads the list's row keys and
+// weights (coefficients) and orders the rows of its hash group by row, a
+// row's pairs in ascending token order.  Rows of up to 16 bits are first
+// renamed to their rank among the group's distinct rows (a bitmap of the
+// rows present); with at most 256 ranks and 256 tokens, every rank's tokens
+// are set as bits of a mask in LDS, and an entry's place is a popcount of
+// the masks (ranks below its own, tokens below its own in its rank), which
+// also gives the segments and their tables.  Otherwise the rows are kept in
+// pair order and sorted stably with an LSD radix sort in LDS (8-bit digits,
+// ballot ranking).  The grouping is repeated by the column slices of one group, which is
 // cheaper than a separate grouping launch and its dependent global rounds;
 // value and sub-key lists take separate numbers of hash groups, chosen to
 // even out the workgroups' work.  Larger chunks (kd_update) read the grouping kernel's
@@ -700,8 +701,7 @@ constexpr int kKwCntInts = (kKdWaves * 256 > 2 * kKdEntCap + 1 ? kKdWaves * 256 
 // LDS layout (byte offsets) of the fused kernel: chunks of T tokens, slices
 // of SW floats, at most kKdEntCap pairs per unit.
 struct KwLds {
-  int dat, key0, idx0, key1, idx1, wl, cnt, items, part, part_c, long_seg, red, dbeg, ditem, dshort, rowof,
-      total;
+  int dat, key0, idx0, key1, idx1, wl, cnt, items, part, part_c, long_seg, red, dbeg, ditem, dshort, total;
 };
 __host__ __device__ constexpr KwLds kw_lds_layout(int T, int SW) {
   KwLds L{};
@@ -721,7 +721,6 @@ __host__ __device__ constexpr KwLds kw_lds_layout(int T, int SW) {
   L.dbeg = o;   o = kd_align(o + (256 + 1) * 4);                  // segment tables when one digit is one row
   L.ditem = o;  o = kd_align(o + 256 * 4);
   L.dshort = o; o = kd_align(o + 256 * 4);
-  L.rowof = o;  o = kd_align(o + 256 * 4);                        // row of each rank (renamed rows)
   L.total = o;
   return L;
 }
@@ -784,9 +783,8 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   while (bits < 31 && (rmax >> bits) != 0) ++bits;
   int passes = max(1, (bits + 7) / 8);
   // rows of up to 16 bits (two passes) may be renamed to their rank among
-  // the group's distinct rows (below): a bitmap of the rows present, in the
-  // segment sums' scratch (free until then), cleared here and filled by the
-  // compaction
+  // the group's distinct rows: a bitmap of the rows present, in the segment
+  // sums' scratch (free until then)
   static_assert(kKdMaxLong * 16 * 16 >= 2 * 2048 * 4, "bitmap and scan fit the sums' scratch at SW = 64");
   static_assert(kKdThreads * 2 == 2048, "two bitmap words per thread");
   const bool try_rename = SW == 64 && passes == 2;             // block-uniform
@@ -796,7 +794,159 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
     bm[2 * tid] = 0u;
     bm[2 * tid + 1] = 0u;
   }
-  // ---- keep this group's rows, in pair order
+  int* items = reinterpret_cast<int*>(lds + LL.items);
+  int* long_seg = reinterpret_cast<int*>(lds + LL.long_seg);
+  int* dbeg = reinterpret_cast<int*>(lds + LL.dbeg);
+  int* ditem = reinterpret_cast<int*>(lds + LL.ditem);
+  int* dshort = reinterpret_cast<int*>(lds + LL.dshort);
+
+  // ---- row masks.  At most 256 tokens, and rows that are (or are renamed
+  // to) at most 256 ranks: each rank's tokens form a 256-bit mask, set by
+  // LDS atomic ORs (the result does not depend on their order).  Within a
+  // list a token touches a row at most once, so a rank's entries in token
+  // order are exactly its entries in pair order, and an entry's place in
+  // the grouped list is the entries of the ranks below plus the tokens of
+  // its own rank below it (popcounts).  This gives the stable sort's output
+  // without a compaction, digit ballots or a scatter pass.
+  static_assert(256 * 8 * 2 <= kKwCntInts, "row masks and their starts fit the counters' space");
+  constexpr bool kMaskT = SW == 64;                   // T <= 256: eight mask words per rank
+  int D = 0;
+  if (kMaskT && passes <= 2) {
+    lds_barrier();                                    // counters and bitmap cleared; the rows' loads stay in flight
+    if (try_rename) {
+#pragma unroll
+      for (int j = 0; j < kTiles; ++j) {
+        const int i = (wave * tpw + j) * kWave + lane;
+        const bool mine = j < tpw && i < P && kr[j] != invalid && hash_group(kr[j], who.ngrp) == who.grp;
+        if (mine) atomicOr(&bm[(unsigned)kr[j] >> 5], 1u << (kr[j] & 31));
+      }
+      lds_barrier();
+      const unsigned int w0 = bm[2 * tid], w1 = bm[2 * tid + 1];
+      const int pre = kd_block_scan<true>(__popc(w0) + __popc(w1), red, &D);
+      if (D == 0) return;                             // block-uniform: nothing to write
+      wpre[2 * tid] = pre;
+      wpre[2 * tid + 1] = pre + __popc(w0);
+      lds_barrier();
+    }
+  }
+  if (kMaskT && (passes == 1 || (try_rename && D <= 256))) {   // block-uniform
+    unsigned int* rmask = reinterpret_cast<unsigned int*>(cnt);   // [256][8] tokens of each rank
+    int* rstart = cnt + 256 * 8;                                  // [256][8] first place of each mask word
+    float4 v[kKdStageMax];
+    kd_stage_load<L4>(a, who, v);                     // the data slice travels while the rows are grouped
+    int rk[kTiles], tk[kTiles];
+#pragma unroll
+    for (int j = 0; j < kTiles; ++j) {
+      const int i = (wave * tpw + j) * kWave + lane;
+      const bool mine = j < tpw && i < P && kr[j] != invalid && hash_group(kr[j], who.ngrp) == who.grp;
+      rk[j] = -1;
+      tk[j] = 0;
+      if (mine) {
+        const int r = kr[j];
+        rk[j] = try_rename ? wpre[r >> 5] + __popc(bm[r >> 5] & ((1u << (r & 31)) - 1u)) : r;
+        tk[j] = token_of(i, a.k);
+        atomicOr(&rmask[rk[j] * 8 + (tk[j] >> 5)], 1u << (tk[j] & 31));
+      }
+    }
+    lds_barrier();
+    // entries per rank, their starts (a scan over ranks by waves 0-3) and
+    // the segment tables: every rank with entries is one segment, its
+    // fields short (at most L4 pairs), pieces of kKdPiece pairs, slots of
+    // segments longer than one piece
+    uint4 m0 = make_uint4(0u, 0u, 0u, 0u), m1 = m0;
+    int run = 0, dbase = 0, nz = 0, pk = 0, inz = 0, ipk = 0, pcs = 0, slt = 0;
+    if (tid < 256) {                                  // whole waves 0-3
+      m0 = reinterpret_cast<const uint4*>(rmask)[2 * tid];
+      m1 = reinterpret_cast<const uint4*>(rmask)[2 * tid + 1];
+      run = __popc(m0.x) + __popc(m0.y) + __popc(m0.z) + __popc(m0.w) +
+            __popc(m1.x) + __popc(m1.y) + __popc(m1.z) + __popc(m1.w);
+      const int incl = wave_inclusive_scan(run);
+      dbase = incl - run;
+      nz = run > 0 ? 1 : 0;
+      pcs = run > L4 ? (run + kKdPiece - 1) / kKdPiece : 0;
+      slt = run > kKdPiece ? pcs : 0;
+      pk = nz ? ((run <= L4 ? 1 : 0) | (pcs << 12) | (slt << 22)) : 0;
+      inz = wave_inclusive_scan(nz);
+      ipk = wave_inclusive_scan(pk);
+      if (lane == kWave - 1) {
+        red[wave] = incl;
+        red[kKdWaves + wave] = inz;
+        red[2 * kKdWaves + wave] = ipk;
+      }
+    }
+    lds_barrier();
+    if (tid < 256) {
+      int bz = 0, bp = 0;
+      for (int w = 0; w < wave; ++w) {
+        dbase += red[w];
+        bz += red[kKdWaves + w];
+        bp += red[2 * kKdWaves + w];
+      }
+      int4 s0, s1;
+      int s = dbase;
+      s0.x = s; s += __popc(m0.x);
+      s0.y = s; s += __popc(m0.y);
+      s0.z = s; s += __popc(m0.z);
+      s0.w = s; s += __popc(m0.w);
+      s1.x = s; s += __popc(m1.x);
+      s1.y = s; s += __popc(m1.y);
+      s1.z = s; s += __popc(m1.z);
+      s1.w = s;
+      reinterpret_cast<int4*>(rstart)[2 * tid] = s0;
+      reinterpret_cast<int4*>(rstart)[2 * tid + 1] = s1;
+      const int sgi = bz + inz - nz;                  // segment number of this rank
+      const int pp = bp + ipk - pk;                   // fields of the segments before it
+      if (nz) {
+        dbeg[sgi] = dbase;
+        ditem[sgi] = pp;
+        if (run <= L4) dshort[pp & 0xfff] = sgi;
+        for (int q = 0; q < pcs; ++q) items[((pp >> 12) & 0x3ff) + q] = (sgi << 5) | q;
+        for (int q = 0; q < slt; ++q) long_seg[(pp >> 22) + q] = q == 0 ? sgi : -1;
+      }
+      if (tid == 255) {
+        dbeg[bz + inz] = dbase + run;
+        red[3 * kKdWaves] = bp + ipk;                 // totals of the fields
+        red[3 * kKdWaves + 1] = dbase + run;          // entries
+      }
+    }
+    lds_barrier();
+    const int M = red[3 * kKdWaves + 1];
+    const int tot = red[3 * kKdWaves];
+    if (M == 0) {                                     // block-uniform: nothing to write
+      kd_stage_store<L4>(a.T, v, dat);                // (the slice's loads land before the exit)
+      return;
+    }
+    // each entry to its place: rows, tokens and weights grouped by rank
+    int* ks = key0;
+    int* ent_t = key1;
+    int* ent_w = idx1;
+#pragma unroll
+    for (int j = 0; j < kTiles; ++j) {
+      if (rk[j] >= 0) {
+        const int wi = rk[j] * 8 + (tk[j] >> 5);
+        const int pos = rstart[wi] + __popc(rmask[wi] & ((1u << (tk[j] & 31)) - 1u));
+        ks[pos] = kr[j];
+        ent_t[pos] = tk[j];
+        ent_w[pos] = __float_as_int(wr[j]);
+      }
+    }
+    kd_stage_store<L4>(a.T, v, dat);
+    __syncthreads();
+    KdSeg S;
+    S.items = items;
+    S.part = reinterpret_cast<float4*>(lds + LL.part);
+    S.part_c = reinterpret_cast<float*>(lds + LL.part_c);
+    S.long_seg = long_seg;
+    S.red = red;
+    S.seg_beg = dbeg;
+    S.seg_item = ditem;
+    S.short_seg = dshort;
+    kd_check_entries<L4>(a, who, ks, ent_t, M, 1);
+    kd_segment_sums<L4>(a, who, dat, ks, ent_t, ent_w, S, tot & 0xfff, (tot >> 12) & 0x3ff, tot >> 22);
+    return;
+  }
+  // ---- otherwise a stable LSD radix sort.  Keep this group's rows, in
+  // pair order
   int kept = 0;
 #pragma unroll
   for (int j = 0; j < kTiles; ++j) {
@@ -826,7 +976,6 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
       const int pos = base + __popcll(m & lanes_below());
       key0[pos] = kr[j];
       idx0[pos] = i;
-      if (try_rename) atomicOr(&bm[(unsigned)kr[j] >> 5], 1u << (kr[j] & 31));
     }
     base += __popcll(m);
   }
@@ -841,31 +990,6 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   const int t_lo = wave * vtpw, t_hi = min(vtiles, t_lo + vtpw);
   int* mycnt = cnt + wave * 256;
   int *ks = key0, *is = idx0, *kd = key1, *id = idx1;
-  int* items = reinterpret_cast<int*>(lds + LL.items);
-  int* long_seg = reinterpret_cast<int*>(lds + LL.long_seg);
-  int* dbeg = reinterpret_cast<int*>(lds + LL.dbeg);
-  int* ditem = reinterpret_cast<int*>(lds + LL.ditem);
-  int* dshort = reinterpret_cast<int*>(lds + LL.dshort);
-  int* row_of = reinterpret_cast<int*>(lds + LL.rowof);
-
-  // ---- rows of up to 16 bits: the rank of a row among the group's
-  // distinct rows is the popcount of the bitmap below it (a scan of the
-  // words' popcounts, then one word); ranks keep the rows' order.  With at
-  // most 256 distinct rows one 8-bit pass then sorts the ranks, its digit
-  // the row; the counting pass renames the entries as it reads them.
-  bool renamed = false;
-  if (try_rename) {
-    const unsigned int w0 = bm[2 * tid], w1 = bm[2 * tid + 1];
-    int D;
-    const int pre = kd_block_scan<true>(__popc(w0) + __popc(w1), red, &D);
-    wpre[2 * tid] = pre;
-    wpre[2 * tid + 1] = pre + __popc(w0);
-    if (D <= 256) {                                            // block-uniform
-      passes = 1;
-      renamed = true;
-    }
-    lds_barrier();
-  }
   // one pass whose digit is the row: the segments are the digits present,
   // and the last pass's scan builds their tables
   const bool direct = passes == 1;
@@ -890,11 +1014,6 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
       const int i = (t_lo + j) * kWave + lane;
       const bool valid = i < M;
       tk[j] = valid ? ks[i] : 0;
-      if (renamed && valid) {
-        const int r = tk[j];
-        tk[j] = wpre[r >> 5] + __popc(bm[r >> 5] & ((1u << (r & 31)) - 1u));
-        row_of[tk[j]] = r;                     // every entry of the row writes the same value
-      }
       td[j] = ((unsigned)tk[j] >> shift) & 255;
       tp[j] = digit_peers(td[j], valid);
       if (valid && (tp[j] & lanes_below()) == 0ull) mycnt[td[j]] += __popcll(tp[j]);
@@ -990,7 +1109,6 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
     const int p = is[i];
     ent_t[i] = token_of(p, a.k);
     ent_w[i] = wl[p];
-    if (renamed) ks[i] = row_of[ks[i]];
   }
   __syncthreads();
   KdSeg S;
