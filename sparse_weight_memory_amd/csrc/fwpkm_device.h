@@ -195,6 +195,11 @@ __device__ __forceinline__ int64_t seq_chunk_row(const SeqArgs& s, int b, int t)
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Bits needed to write x >= 0 (0 for x = 0): one count-leading-zeros.  A
+// loop over the bits would run on the compute unit's one scalar unit once
+// per wave.
+__device__ __forceinline__ int bit_length(int x) { return 32 - __clz(x); }
+
 // Token of pair p = t*k + m without an integer divide: (p + 1/2) / k lies at
 // least 1/(2k) >= 1/64 away from an integer, relative 2e-6 at p < 8192, far
 // above the reciprocal's error.

@@ -231,8 +231,7 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
   }
   int* mycnt = cnt + wave * kDigits;   // only this wave counts into / scatters from it
   // radix passes the rows need, and whether to rename them first (below)
-  int bits = 0;
-  while (bits < 31 && (kmax >> bits) != 0) ++bits;
+  int bits = bit_length(kmax);
   int passes = (bits + kBits - 1) / kBits;
   const bool try_rename = !by_rank && passes >= 2 && M >= kRenameMin && P >= kRenamePong;   // block-uniform
   // renaming: a hash set of rows in the counters' space, the row of each
@@ -373,8 +372,7 @@ __global__ __launch_bounds__(kGroupThreads) void kc_sort(ChunkArgs a) {
         if (i < M) ks[i] = rank_of[eslot[i]];
       }
       // ranks take bitlen(D - 1) bits; one distinct row is sorted already
-      bits = 0;
-      while (bits < kBits && ((D - 1) >> bits) != 0) ++bits;
+      bits = min(kBits, bit_length(D - 1));
       passes = D > 1 ? 1 : 0;
       renamed = true;
       __syncthreads();         // every wave has read the slot ranks before the counters are cleared

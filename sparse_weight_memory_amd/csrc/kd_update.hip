@@ -776,12 +776,9 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
     kr[j] = keys[ic];
     wr[j] = wsrc[ic];
   }
-  for (int i = lane; i < 256; i += kWave) cnt[wave * 256 + i] = 0;   // this wave's digit counters
+  reinterpret_cast<int4*>(cnt + wave * 256)[lane] = make_int4(0, 0, 0, 0);   // this wave's digit counters
   // radix passes the rows need (8-bit digits)
-  const int rmax = invalid - 1;
-  int bits = 0;
-  while (bits < 31 && (rmax >> bits) != 0) ++bits;
-  int passes = max(1, (bits + 7) / 8);
+  const int passes = max(1, (bit_length(invalid - 1) + 7) / 8);
   // rows of up to 16 bits (two passes) may be renamed to their rank among
   // the group's distinct rows: a bitmap of the rows present, in the segment
   // sums' scratch (free until then)
