@@ -10,8 +10,10 @@ The cases cover the paths whose indexing the device checks watch: two key
 blocks with a ragged second one and a ragged token tile, both score modes,
 a chunk of more than 2048 pairs per unit (separate grouping kernel and
 batched update), sub-keys that all tie (whole-wave selection fallback), the
-addressing loss, and one query asked by 1,024 tokens (hot rows renamed in
-the grouping kernel).  The last case feeds NaN queries in dot mode, whose
+addressing loss, one query asked by 1,024 tokens (hot rows renamed in
+the grouping kernel), and 16 units whose value lists are each one hash
+group of ~2,000 distinct rows (too many for the update's per-row token
+masks: the radix sort groups them).  The last case feeds NaN queries in dot mode, whose
 softmax weights are then NaN: a checked build must report it.
 """
 
@@ -30,6 +32,7 @@ CASES = {
     "addressing": (2, 2, 64, 48, 32, 96, 4, "idw", 0.1, 2, None),
     "nan_dot": (1, 1, 32, 32, 32, 64, 4, "dot", 0.0, 1, "nan_queries"),
     "hot_rows": (1, 1, 1024, 512, 8, 16, 8, "idw", 0.0, 1, "one_query"),
+    "many_rows": (16, 1, 256, 256, 512, 64, 8, "idw", 0.0, 1, None),
 }
 
 

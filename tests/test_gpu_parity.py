@@ -229,6 +229,27 @@ def test_fused_update_at_narrow_slices(C, k):
     compare_chunk(mem, st, q, y, 1.0, units=[0, 3, 7], label=f"narrow C{C} k{k}")
 
 
+@pytest.mark.parametrize("k,distinct,seed", [(1, 256, 3010), (2, 129, 3022)])
+def test_fused_grouping_at_the_row_mask_limit(k, distinct, seed):
+    """With 16 units, d_h = 512 and d_v = 64, one hash group per list already
+    gives the update a workgroup per compute unit, so a unit's whole value
+    list is one group.  256 tokens asking 256 distinct queries with k = 1 give
+    unit 0 exactly 256 distinct value rows, the most the per-row token masks
+    take (unit 15: 255); 129 distinct queries with k = 2 give 258 (unit 0) and
+    257 (unit 15), which the radix sort groups instead, after the bitmap of
+    the rows present has counted them."""
+    need_gpu()
+    B, H, C, n, half, dv = 16, 1, 256, 256, 512, 64
+    units = [0, 15]
+    mem = _mem(sqrt_slots=n, dim_qk=2 * half, dim_v=dv, topk=k, chunk_size=C, num_heads=H, max_batch=B)
+    st, q, y = _random_case(seed, B, H, C, n, half, dv)
+    q[:] = q[:, [t if t < distinct else t % distinct for t in range(C)]]
+    rows = [len(np.unique(O.unit_chunk(st["k1"][u], st["k2"][u], st["v"][u], q[u, :, 0], y[u, :, 0],
+                                       1.0, k, mem.cfg.eps, O.IDW).slots)) for u in units]
+    assert rows == ([256, 255] if k == 1 else [258, 257]), rows
+    compare_chunk(mem, st, q, y, 1.0, units=units, label=f"row-mask limit k{k} rows {rows}")
+
+
 def test_closed_form_k1_single_token_writes_target():
     need_gpu()
     n, half, dv = 16, 8, 32
