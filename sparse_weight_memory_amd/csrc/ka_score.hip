@@ -255,7 +255,6 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void ka_score_topk(ChunkArgs a
   const int dq = wave >> a.ka_nkt_log2;
   const int row = lane & 15;          // A row (key) / B column (token)
   const int quad = lane >> 4;         // 4-dim group inside a 16-dim step
-  const int steps = (int)((unsigned int)share / 16);
   const int nchunks = (int)(((unsigned int)share + kDimChunk - 1) / kDimChunk);   // chunks holding data
   const int nchunks_p = ka_chunks_of<kDimChunk, kPrefetch>(share);            // chunks multiplied
   const float* kbase = (h == 0 ? a.k1 : a.k2) + (int64_t)b * a.stride_k + (int64_t)hh * a.n * half;

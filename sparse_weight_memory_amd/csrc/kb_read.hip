@@ -77,7 +77,6 @@ __global__ __launch_bounds__(256) void kb_read(ChunkArgs a) {
   const int n = a.n;
   const int b = fast_div(u, a.div_H), hh = u - b * a.H;
   const int64_t ut = (int64_t)u * a.T + t;
-  const float inf = __builtin_inff();
   const int64_t io = ((int64_t)(b * a.T + t) * a.H + hh);
   const int dv4 = a.dv >> 2;
 
