@@ -121,15 +121,17 @@ def test_training_length_stream_sampled_units():
 
 def test_multihead_stream_sampled_units():
     """4 heads x 262,144 slots, top-16, batch 4 x 8192 tokens; units (0,0)
-    and (2,3) chained with every chunk's retrieved checked, then one unit
-    per head (on four XCDs) teacher-forced through the first four chunks."""
+    and (2,3) chained with every chunk's retrieved checked, then every unit
+    (two per XCD, each through its own place in the separate grouping and
+    update kernels' unit-major grids) teacher-forced through the first two
+    chunks."""
     need_gpu()
     w = get_config(4)
     _chained(w, units=[0, 11], chunks=w.chunks, check_every_chunk=True)
     mem = _mem_for(w)
     Q, Y = draw_queries(w), draw_targets(w)
     dev = _device_state(initial_tables(w), w.batch)
-    _teacher_forced_pass(mem, dev, Q, Y, w, [0, 5, 10, 15], 4, f"{w.name} tf")
+    _teacher_forced_pass(mem, dev, Q, Y, w, list(range(w.units)), 2, f"{w.name} tf")
 
 
 def test_long_context_two_passes():
