@@ -10,6 +10,7 @@ namespace fwpkm {
 constexpr int kWave = 64;
 constexpr int kKeyBlock = 64;       // smallest key block of the score kernel
 constexpr int kTokTile = 16;        // tokens per score workgroup (MFMA N)
+constexpr int kReadTokensMax = 4;  // tokens (one wave each) per read workgroup, at most
 constexpr int kAddrPad = 256;   // score-row pitch multiple of the addressing loss (4 loads per lane)
 constexpr int kGroupWaves = 8;      // waves of one grouping workgroup
 constexpr int kSortMaxPairs = 8192; // C*k limit of the in-LDS sort
@@ -134,7 +135,10 @@ struct ChunkArgs {
   FastDiv div_H;       // x / H
   FastDiv div_U;       // x / U
   FastDiv div_upx;     // x / (U / 8): units per XCD
-  FastDiv div_nbx;     // x / ceil(T / 4): read workgroups per unit
+  // read-kernel geometry, derived on the host by its launcher
+  int kb_tpw;          // tokens (one wave each) per read workgroup
+  int kb_nbx;          // read workgroups per unit = ceil(T / kb_tpw)
+  FastDiv kb_div_nbx;  // x / kb_nbx
   // update-kernel geometry, derived on the host by its launcher: column
   // slices, kd_sv of them per V row and kd_sk per K row; kd_gv hash groups
   // of rows per value list and kd_gk per sub-key list
@@ -165,7 +169,6 @@ inline ChunkArgs with_divisors(const ChunkArgs& a) {
   g.div_H = make_fastdiv(a.H > 1 ? a.H : 1);
   g.div_U = make_fastdiv(a.U > 1 ? a.U : 1);
   g.div_upx = make_fastdiv(a.U / 8 > 1 ? a.U / 8 : 1);
-  g.div_nbx = make_fastdiv((a.T + 3) / 4 > 1 ? (a.T + 3) / 4 : 1);
   return g;
 }
 
