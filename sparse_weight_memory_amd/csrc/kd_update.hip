@@ -76,6 +76,9 @@ constexpr int kKdPrefetch = 2;                  // old-row float4 prefetched per
 static_assert(kKdPer * kKdThreads == kKdEntCap, "whole entries per thread");
 
 // LDS layout (byte offsets) for chunks of T tokens and slices of SW floats.
+// The data slice, the one part whose size depends on T, comes last, so every
+// other offset is a constant the compiler folds (a runtime layout cost each
+// of the 16 waves ~25 instructions on the compute unit's one scalar unit).
 struct KdLds {
   int dat, ent_t, ent_w, ent_row, seg_beg, seg_item, short_seg, items, part, part_c, long_seg, red, total;
 };
@@ -83,7 +86,6 @@ __host__ __device__ constexpr int kd_align(int x) { return (x + 15) & ~15; }
 __host__ __device__ constexpr KdLds kd_lds_layout(int T, int SW) {
   KdLds L{};
   int o = 0;
-  L.dat = o;      o = kd_align(o + T * (SW / 4 + 1) * 16);        // [T][SW/4 + 1] float4 (padded rows)
   L.ent_t = o;    o = kd_align(o + kKdEntCap * 4);
   L.ent_w = o;    o = kd_align(o + kKdEntCap * 4);
   L.ent_row = o;  o = kd_align(o + (kKdEntCap + 1) * 4);         // + the row after the batch
@@ -95,6 +97,7 @@ __host__ __device__ constexpr KdLds kd_lds_layout(int T, int SW) {
   L.part_c = o;   o = kd_align(o + kKdMaxLong * 4);
   L.long_seg = o; o = kd_align(o + kKdMaxLong * 4);
   L.red = o;      o = kd_align(o + 4 * kKdWaves * 4);
+  L.dat = o;      o = kd_align(o + T * (SW / 4 + 1) * 16);        // [T][SW/4 + 1] float4 (padded rows)
   L.total = o;
   return L;
 }
@@ -706,7 +709,6 @@ struct KwLds {
 __host__ __device__ constexpr KwLds kw_lds_layout(int T, int SW) {
   KwLds L{};
   int o = 0;
-  L.dat = o;    o = kd_align(o + T * (SW / 4 + 1) * 16);
   L.key0 = o;   o = kd_align(o + kKdEntCap * 4);                  // sort ping: rows, pair indices
   L.idx0 = o;   o = kd_align(o + kKdEntCap * 4);
   L.key1 = o;   o = kd_align(o + kKdEntCap * 4);                  // pong (later tokens, weights)
@@ -721,6 +723,7 @@ __host__ __device__ constexpr KwLds kw_lds_layout(int T, int SW) {
   L.dbeg = o;   o = kd_align(o + (256 + 1) * 4);                  // segment tables when one digit is one row
   L.ditem = o;  o = kd_align(o + 256 * 4);
   L.dshort = o; o = kd_align(o + 256 * 4);
+  L.dat = o;    o = kd_align(o + T * (SW / 4 + 1) * 16);          // last: the one T-dependent part
   L.total = o;
   return L;
 }
@@ -765,8 +768,8 @@ __global__ __launch_bounds__(kKdThreads) void kd_write(ChunkArgs a) {
   // ---- the list's rows and weights.  Wave w owns list tiles
   // [w*tpw, (w+1)*tpw), so kept entries come out in pair order; indices past
   // the list re-read entry 0 and are masked.
-  const int tiles = (P + kWave - 1) / kWave;
-  const int tpw = (tiles + kKdWaves - 1) / kKdWaves;          // <= kTiles
+  const int tiles = (int)(((unsigned)P + kWave - 1) / kWave);
+  const int tpw = (int)(((unsigned)tiles + kKdWaves - 1) / kKdWaves);   // <= kTiles
   int kr[kTiles];
   float wr[kTiles];
 #pragma unroll
