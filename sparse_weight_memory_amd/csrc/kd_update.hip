@@ -52,7 +52,8 @@
 // g + groups, ... as DPP broadcasts hand them over (only as many steps as the
 // item needs), and a fixed butterfly adds the groups.  Every sum runs in
 // one fixed order, results do not depend on scheduling, and no atomic
-// operation touches a sum (the only atomics set bits of the row bitmap).
+// operation touches a sum (the only atomics set bits of the row bitmap and
+// of the per-rank token masks, whose values do not depend on their order).
 
 #include <algorithm>
 
