@@ -122,16 +122,27 @@ def parse():
 
 
 def copy_probe(mib):
+    """A plain device-to-device copy of `mib` MiB, 5 times: the calibration
+    for the HBM byte counters, and (timed with events on the copy's stream)
+    the bandwidth such a copy achieves, as context for the 8 TB/s peak."""
     import torch
     n = mib * (1 << 20) // 4
     src = torch.ones(n, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
+    ms = []
     for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
     torch.cuda.synchronize()
+    med = statistics.median(ms)
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
-                      "copies": 5}))
+                      "copies": 5, "ms_per_copy": ms,
+                      "read_plus_write_gbps_median": 2 * n * 4 / (med * 1e6)}))
 
 
 def algorithmic_cost(cfg, kernel, tokens, uniq_v, uniq_k, addr=False):
